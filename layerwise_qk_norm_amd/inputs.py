@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for layerwise QK-Norm workloads.
+
+This module only draws numbers: it holds none of the normalisation
+arithmetic, imports neither the HIP binding nor the oracle, and serves both.
+
+Recipe (stated once, used everywhere):
+
+* Per-tensor streams come from ``numpy.random.SeedSequence(seed).spawn(6)`` in
+  the order [q, k, gamma_q, gamma_k, outlier_q, outlier_k].
+* Activations: ``N(0, sigma^2)`` (``standard_normal * sigma``) or Student-t
+  with 3 degrees of freedom; drawn in float64 row-major, in row chunks (the
+  stream is consumed in C order, so the first T' rows of a T-row draw equal a
+  T'-row draw).
+* Outlier channels: a fixed set of ``max(1, round(p * H))`` columns per tensor,
+  the first entries of a seeded permutation, shared by every token; those
+  columns are multiplied by the outlier scale before rounding.
+* gamma: ``U(0.5, 1.5)`` or ``N(1, 0.1^2)``, drawn in float64.
+* Storage: float64 -> float32 (round to nearest even), then for bf16
+  float32 -> bf16 round to nearest even on the bit pattern. bf16 tensors are
+  numpy ``uint16`` bit patterns.
+
+The shapes and distributions are the stand-in for the Q/K activations of the
+models the letter evaluates ("SwiftQK ...", Section IV-A and the Q/K sizes of
+Fig. 2(a)); no dataset values are used.
+"""
+from __future__ import annotations
+
+import dataclasses
+import itertools
+from typing import Iterator
+
+import numpy as np
+
+EPS = 1e-6
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    Hq: int
+    Hk: int
+    n_shards: int
+    dtype: str  # "bf16" or "f32" (inputs, gamma and outputs share it)
+    dist: str = "normal"  # "normal" or "t3"
+    sigma: float = 1.0
+    outlier_frac: float = 0.0
+    outlier_scale: float = 1.0
+    gamma_dist: str = "uniform"  # "uniform" (0.5, 1.5) or "normal" (1, 0.1)
+    eps: float = EPS
+    seed: int = 0
+
+    def with_T(self, T: int) -> "Workload":
+        return dataclasses.replace(self, T=T)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def algorithmic_bytes(self) -> int:
+        """One read and one write of Q and K, plus gamma_q and gamma_k once."""
+        s = self.elem_bytes
+        return 2 * self.T * (self.Hq + self.Hk) * s + (self.Hq + self.Hk) * s
+
+    def outlier_count(self, H: int) -> int:
+        if self.outlier_frac <= 0:
+            return 0
+        return max(1, int(round(self.outlier_frac * H)))
+
+
+TINY = Workload("tiny", 8, 256, 256, 2, "f32", gamma_dist="normal")
+DECODE = Workload("decode", 64, 4096, 4096, 4, "bf16", outlier_frac=0.01, outlier_scale=20.0)
+PREFILL = Workload("prefill", 16384, 5120, 5120, 2, "bf16", sigma=2.0)
+GQA = Workload("gqa", 8192, 5120, 1024, 4, "bf16", outlier_frac=0.005, outlier_scale=50.0)
+CONFIGS = {w.name: w for w in (TINY, DECODE, PREFILL, GQA)}
+
+SWEEP_T = (4096, 4097, 16384, 65536)
+SWEEP_H = (1024, 3072, 5120, 8192, 16384)
+SWEEP_N = (1, 2, 4, 8)
+SWEEP_DTYPE = ("bf16", "f32")
+SWEEP_DIST = ("normal", "t3")
+
+
+def sweep() -> Iterator[Workload]:
+    for T, H, N, dt, dist in itertools.product(SWEEP_T, SWEEP_H, SWEEP_N, SWEEP_DTYPE,
+                                               SWEEP_DIST):
+        yield Workload(f"sweep_T{T}_H{H}_N{N}_{dt}_{dist}", T, H, H, N, dt, dist=dist)
+
+
+# ---------------------------------------------------------------- rounding
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest, ties to even; NaN -> 0x7FC0."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
+    out = ((u + bias) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0) | (((u[nan] >> 16) & np.uint32(0x8000)).astype(np.uint16))
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def store(a64: np.ndarray, dtype: str) -> np.ndarray:
+    f32 = a64.astype(np.float32)
+    return f32_to_bf16_bits(f32) if dtype == "bf16" else f32
+
+
+# ---------------------------------------------------------------- host draws
+
+def _streams(seed: int):
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(6)]
+
+
+def _activations(rng, T, H, w: Workload, outlier_cols, chunk_rows: int) -> np.ndarray:
+    out = np.empty((T, H), np.uint16 if w.dtype == "bf16" else np.float32)
+    for lo in range(0, T, chunk_rows):
+        hi = min(T, lo + chunk_rows)
+        if w.dist == "normal":
+            a = rng.standard_normal((hi - lo, H)) * w.sigma
+        elif w.dist == "t3":
+            a = rng.standard_t(3, (hi - lo, H)) * w.sigma
+        else:
+            raise ValueError(w.dist)
+        if outlier_cols is not None:
+            a[:, outlier_cols] *= w.outlier_scale
+        out[lo:hi] = store(a, w.dtype)
+    return out
+
+
+def _gamma(rng, H, w: Workload) -> np.ndarray:
+    if w.gamma_dist == "uniform":
+        g = rng.uniform(0.5, 1.5, H)
+    elif w.gamma_dist == "normal":
+        g = rng.normal(1.0, 0.1, H)
+    else:
+        raise ValueError(w.gamma_dist)
+    return store(g, w.dtype)
+
+
+def outlier_columns(w: Workload, which: str):
+    """The outlier column indices of tensor ``which`` ("q" or "k"), or None."""
+    H = w.Hq if which == "q" else w.Hk
+    n = w.outlier_count(H)
+    if n == 0:
+        return None
+    rng = _streams(w.seed)[4 if which == "q" else 5]
+    return np.sort(rng.permutation(H)[:n])
+
+
+def make_host(w: Workload, chunk_rows: int = 2048) -> dict:
+    """Host arrays ``q, k, gamma_q, gamma_k`` for workload ``w``."""
+    rq, rk, rgq, rgk, _, _ = _streams(w.seed)
+    return {
+        "q": _activations(rq, w.T, w.Hq, w, outlier_columns(w, "q"), chunk_rows),
+        "k": _activations(rk, w.T, w.Hk, w, outlier_columns(w, "k"), chunk_rows),
+        "gamma_q": _gamma(rgq, w.Hq, w),
+        "gamma_k": _gamma(rgk, w.Hk, w),
+    }
+
+
+# ---------------------------------------------------------------- device draws
+
+def make_device_activations(w: Workload, which: str, device, torch):
+    """Device-side draw of one activation tensor with torch's seeded generator.
+
+    Used only where a host draw would dominate a test's run time (the
+    largest sweep points). Same distribution as the host draw, different
+    values; the oracle then reads back exactly the rows it checks.
+    Returns a torch tensor of dtype bfloat16 or float32 on ``device``.
+    """
+    H = w.Hq if which == "q" else w.Hk
+    seed = int(np.random.SeedSequence(w.seed).spawn(6)[0 if which == "q" else 1]
+               .generate_state(1)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = torch.empty((w.T, H), dtype=out_dtype, device=device)
+    rows = max(1, (1 << 26) // H)
+    for lo in range(0, w.T, rows):
+        hi = min(w.T, lo + rows)
+        a = torch.randn((hi - lo, H), generator=g, device=device, dtype=torch.float32)
+        if w.dist == "t3":
+            chi = sum(torch.randn((hi - lo, H), generator=g, device=device,
+                                  dtype=torch.float32) ** 2 for _ in range(3))
+            a = a / torch.sqrt(chi / 3.0)
+        a = a * w.sigma
+        cols = outlier_columns(w, which)
+        if cols is not None:
+            a[:, torch.as_tensor(cols, device=device)] *= w.outlier_scale
+        out[lo:hi] = a.to(out_dtype)
+    return out

@@ -1,0 +1,124 @@
+/*
+ * Layerwise QK-Norm oracle: plain, slow, fp64 CPU reference.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library. The product
+ * (the HIP library and its Python binding) never calls it, and the two share
+ * no code: this file includes nothing from the product tree.
+ *
+ * What it computes (one RMSNorm per token and per tensor, applied to the FULL
+ * projected vector of width H):
+ *
+ *   RMSNorm(x) = x / sqrt( (1/H) * sum_{j=1..H} x_j^2 + eps ) (.) gamma
+ *
+ * Source: "SwiftQK: Fast and Communication-Efficient Tensor Parallelism for
+ * Query-Key Normalization", Section II-A, Eq. (1) (the letter's rendering is
+ * garbled); the same Eq. (1) in the reading notes "SwiftQK：当归一化层成为张量
+ * 并行的瓶颈", Section 2, which prints it cleanly. The letter states that the
+ * sharded computation preserves the global normalization semantics
+ * (Section III-A, Section V) and measures precision against an FP64 RMSNorm
+ * of the gathered vector (Section IV-C); this file is that FP64 RMSNorm.
+ *
+ * The per-shard partial sums of squares (Algorithm 1, Phase A; the notes'
+ * worked example, Eqs. (3)-(4)) are provided for the split API:
+ *
+ *   p[k][t] = sum_{j in shard k} x[t][j]^2,   shard k = columns [k*H/N, (k+1)*H/N)
+ *
+ * The contiguous equal split is the column-parallel split of the projection
+ * (letter, Section II-B) and is the split of the notes' worked example
+ * (Section 4b: the first GPU holds the first four elements).
+ *
+ * Decoding of stored inputs is exact: a bf16 value is the upper 16 bits of
+ * an IEEE binary32 value; binary32 -> binary64 is exact. eps is received as
+ * binary32 (the value the GPU library receives) and promoted exactly.
+ *
+ * No blocking, fusion or reordering: each sum is a plain left-to-right loop
+ * in binary64 (relative error <= H * 2^-53).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+static double decode_bf16(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double decode_f32(float v)
+{
+    return (double)v;
+}
+
+/* dtype codes: 0 = bf16 (uint16_t bit patterns), 1 = fp32 */
+static double load(const void* base, int dtype, int64_t i)
+{
+    if (dtype == 0)
+        return decode_bf16(((const uint16_t*)base)[i]);
+    return decode_f32(((const float*)base)[i]);
+}
+
+/*
+ * RMSNorm of T rows of width H (row-major, row stride H).
+ *   x      [T][H]  input values (bf16 bits or fp32)
+ *   gamma  [H]     scale (same dtype as x)
+ *   eps            binary32 epsilon, promoted exactly
+ * Outputs (any may be NULL):
+ *   y      [T][H]  x / sqrt(S/H + eps) * gamma, unrounded binary64
+ *   sumsq  [T]     S = sum_j x_j^2
+ *   rinv   [T]     1 / sqrt(S/H + eps)
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_rmsnorm(const void* x, const void* gamma, int dtype, int64_t T, int64_t H,
+                   float eps, double* y, double* sumsq, double* rinv)
+{
+    if (!x || (y && !gamma) || T < 0 || H < 1 || (dtype != 0 && dtype != 1))
+        return -1;
+    const double e = (double)eps;
+    for (int64_t t = 0; t < T; ++t) {
+        double S = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = load(x, dtype, t * H + j);
+            S += v * v;
+        }
+        double denom = sqrt(S / (double)H + e);
+        if (sumsq)
+            sumsq[t] = S;
+        if (rinv)
+            rinv[t] = 1.0 / denom;
+        if (y) {
+            for (int64_t j = 0; j < H; ++j) {
+                double v = load(x, dtype, t * H + j);
+                double g = load(gamma, dtype, j);
+                y[t * H + j] = v / denom * g;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Per-shard partial sums of squares, shard-major: p[k*T + t] for k = 0..N-1.
+ * Requires H % N == 0 (equal contiguous shards). Returns 0, or -1.
+ */
+int oracle_shard_sumsq(const void* x, int dtype, int64_t T, int64_t H, int n_shards,
+                       double* p)
+{
+    if (!x || !p || T < 0 || H < 1 || n_shards < 1 || H % n_shards != 0 ||
+        (dtype != 0 && dtype != 1))
+        return -1;
+    const int64_t W = H / n_shards;
+    for (int k = 0; k < n_shards; ++k) {
+        for (int64_t t = 0; t < T; ++t) {
+            double s = 0.0;
+            for (int64_t j = k * W; j < (k + 1) * W; ++j) {
+                double v = load(x, dtype, t * H + j);
+                s += v * v;
+            }
+            p[(int64_t)k * T + t] = s;
+        }
+    }
+    return 0;
+}

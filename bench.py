@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Q+K layerwise RMSNorm on one MI355X.
+
+One step = one fused call (every stage of the path: shard partials, scalar
+exchange and combine, x*gamma, final scaling) over the prefill workload:
+T=16384 tokens, Q and K width 5120, bf16, 2 logical shards, inputs resident
+in HBM. Prints ONE JSON line on stdout; progress goes to stderr.
+
+Besides the headline (GB/s of algorithmic bytes), the line carries:
+  decode      -- the T=64 decode workload: device and host-visible us per call
+  copy        -- a plain copy of the same bytes (achievable-bandwidth ceiling)
+  split       -- the three-kernel split path on the same workload
+  roofline    -- the fused kernel against MI355X peak HBM bandwidth
+  cpu_baseline-- the fp64 oracle timed on this host's cores on a sample
+
+Modes: ``--pmc`` runs only the kernels whose counters are collected
+(fused prefill and the copy of known size), for rocprofv3 --pmc runs.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+METRIC = "fused Q+K layerwise RMSNorm HBM GB/s (% of peak) at T=16384; decode µs at T=64"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_prefill_T16384_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    from layerwise_qk_norm_amd.profiling import kernel_source_sha
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def timed(fn, steps, stream, torch):
+    """Average ms per call of ``fn`` over ``steps`` back-to-back calls (HIP events)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def device_workload(w, torch, sets=1):
+    from layerwise_qk_norm_amd import inputs
+    d = inputs.make_host(w)
+    dev = "cuda:0"
+    gq, gk = inputs.to_device(d["gamma_q"], dev, torch), inputs.to_device(d["gamma_k"], dev, torch)
+    bufs = []
+    for s in range(sets):
+        q = inputs.to_device(d["q"], dev, torch)
+        k = inputs.to_device(d["k"], dev, torch)
+        bufs.append((q, k, torch.empty_like(q), torch.empty_like(k)))
+    return d, gq, gk, bufs
+
+
+def cpu_baseline(w, d, budget_s=12.0):
+    """The fp64 oracle on the first rows of the workload, sized to ~budget_s."""
+    from oracle import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    probe = min(w.T, 256)
+    t0 = time.perf_counter()
+    for n in ("q", "k"):
+        oracle.rmsnorm(d[n][:probe], d["gamma_" + n], w.eps, threads=threads)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(probe, min(w.T, budget_s / max(per_row, 1e-9))))
+    t0 = time.perf_counter()
+    for n in ("q", "k"):
+        oracle.rmsnorm(d[n][:rows], d["gamma_" + n], w.eps, threads=threads)
+    sec = time.perf_counter() - t0
+    nbytes = w.with_T(rows).algorithmic_bytes()
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {rows} of {w.T} tokens of the prefill workload (Q and K, "
+                      f"fp64 C loops, rows split over {threads} threads), {sec:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc", action="store_true", help="counter-collection mode")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; --gpus N with N > 1 is not supported "
+              "(the shards are logical shards on one device)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from layerwise_qk_norm_amd import inputs, ops
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ops.lib()  # raises if the HIP library is missing
+    stream = torch.cuda.current_stream()
+
+    w = inputs.PREFILL
+    nbytes = w.algorithmic_bytes()
+    log(f"generating {w.name} inputs ...")
+    d, gq, gk, bufs = device_workload(w, torch, sets=1 if args.pmc else 2)
+    plan = ops.current_plan(w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
+    log(f"plan: {plan}")
+
+    def fused(i):
+        q, k, oq, ok = bufs[i % len(bufs)]
+        ops.layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps, out_q=oq, out_k=ok)
+
+    def copy(i):
+        q, k, oq, ok = bufs[i % len(bufs)]
+        ops.bench_copy(q, k, oq, ok)
+
+    if args.pmc:
+        for i in range(5):
+            fused(i)
+            copy(i)
+        torch.cuda.synchronize()
+        assert ops.check_fault() == ops.QKN_OK
+        log("pmc mode done: 5 fused prefill launches, 5 copy launches of "
+            f"{2 * w.T * (w.Hq + w.Hk) * w.elem_bytes // 2} bytes read")
+        return
+
+    for i in range(args.warmup):
+        fused(i)
+    torch.cuda.synchronize()
+    if ops.check_fault() != ops.QKN_OK:
+        raise RuntimeError("fused kernel reported an exchange timeout during warmup")
+    log(f"timing {args.steps} fused steps ...")
+    ms = timed(fused, args.steps, stream, torch)
+    if ops.check_fault() != ops.QKN_OK:
+        raise RuntimeError("fused kernel reported an exchange timeout")
+    gbs = nbytes / (ms * 1e-3) / 1e9
+
+    log("timing copy ceiling and split path ...")
+    for i in range(3):
+        copy(i)
+    copy_ms = timed(copy, args.steps, stream, torch)
+    copy_gbs = (nbytes - (w.Hq + w.Hk) * w.elem_bytes) / (copy_ms * 1e-3) / 1e9
+    ops.set_option("force_split", 1)
+    for i in range(3):
+        fused(i)
+    split_ms = timed(fused, args.steps, stream, torch)
+    ops.set_option("force_split", 0)
+
+    # decode: device time per call (events around each call) and host-visible time
+    log("timing decode ...")
+    wd = inputs.DECODE
+    dd, dgq, dgk, dbufs = device_workload(wd, torch, sets=1)
+    q, k, oq, ok = dbufs[0]
+
+    def dec(_):
+        ops.layerwise_fwd(q, k, dgq, dgk, wd.n_shards, wd.eps, out_q=oq, out_k=ok)
+
+    for i in range(50):
+        dec(i)
+    torch.cuda.synchronize()
+    per_call = []
+    for i in range(200):
+        per_call.append(timed(dec, 1, stream, torch))
+    n_host = 1000
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_host):
+        dec(i)
+    torch.cuda.synchronize()
+    host_us = (time.perf_counter() - t0) / n_host * 1e6
+    dev_us_b2b = timed(dec, n_host, stream, torch) * 1e3
+    if ops.check_fault() != ops.QKN_OK:
+        raise RuntimeError("decode reported an exchange timeout")
+
+    traffic = read_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 2^2) activations, U(0.5, 1.5) gamma)",
+        "config": {"workload": "prefill: T=16384, Q and K width 5120, bf16, 2 logical shards",
+                   "T": w.T, "Hq": w.Hq, "Hk": w.Hk, "n_shards": w.n_shards, "eps": w.eps,
+                   "algorithmic_bytes": nbytes, "plan": plan},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "decode": {"workload": "T=64, Q and K width 4096, bf16, 4 logical shards",
+                   "device_us_per_call_median": round(float(np.median(per_call)) * 1e3, 2),
+                   "device_us_per_call_back_to_back": round(dev_us_b2b, 2),
+                   "host_visible_us_per_call": round(host_us, 2)},
+        "copy": {"GBs": round(copy_gbs, 1), "ms": round(copy_ms, 5),
+                 "fused_frac_of_copy": round(gbs / copy_gbs, 4)},
+        "split": {"GBs": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "ms": round(split_ms, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(w, d)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

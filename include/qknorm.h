@@ -1,0 +1,193 @@
+/*
+ * qknorm.h -- C ABI of the MI355X (gfx950) layerwise QK-Norm library.
+ *
+ * Layerwise QK-Norm is RMSNorm over the FULL projected Q and K vector of
+ * each token: one factor per vector, from the sum of squares over all H
+ * columns, then an elementwise scale by gamma:
+ *
+ *   y[t][j] = x[t][j] / sqrt( (1/H) * sum_j x[t][j]^2 + eps ) * gamma[j]
+ *
+ * ("SwiftQK: Fast and Communication-Efficient Tensor Parallelism for
+ * Query-Key Normalization", Section II-A, Eq. (1).) Q and K are two
+ * independent normalisations (Fig. 1(a): one Norm per tensor) executed in one
+ * fused pass.
+ *
+ * The library computes it with the letter's decomposition (Section III,
+ * Algorithm 1): the hidden dimension is split into n_shards contiguous
+ * column blocks ("logical shards"); each shard reduces only a scalar fp32
+ * partial sum of squares (Phase A); the partials are exchanged and combined
+ * in ascending shard order while the independent x*gamma product proceeds
+ * (Phase B); the combined factor scales the product (Phase C). All shards run
+ * on one GPU: the shards of a token tile are workgroups of one persistent,
+ * co-resident grid that exchange their scalars through device memory.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are device pointers, row-major [T][H] with row stride H
+ *    elements, contiguous; gamma is [H]. bf16 means IEEE binary32 truncated
+ *    to its upper 16 bits (stored as 16-bit words); f32 is IEEE binary32.
+ *    The caller owns every tensor it passes.
+ *  - Calls are asynchronous and stream-ordered on `stream` (0 = the null
+ *    stream of the current device); pointers must belong to the current
+ *    device. Nothing is synchronised except where stated.
+ *  - Argument errors are detected synchronously and launch nothing.
+ *    Return value: QKN_OK (0) or a negative qknorm_status.
+ *  - T == 0 is a no-op returning QKN_OK.
+ *  - An output may alias its own input exactly (in place); any other
+ *    overlap between an output and an input or another output is
+ *    QKN_EOVERLAP.
+ *  - 16-byte aligned pointers with (H / n_shards) * elem_size a multiple of
+ *    16 bytes take 128-bit memory paths; other layouts are still correct.
+ */
+#ifndef QKNORM_H
+#define QKNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qknorm_status {
+    QKN_OK = 0,
+    QKN_EINVAL = -1,     /* bad argument: null pointer, T < 0, H < 1,
+                            n_shards outside [1, QKN_MAX_SHARDS],
+                            H % n_shards != 0, eps negative or not finite */
+    QKN_EOVERLAP = -2,   /* an output partially overlaps an input/output */
+    QKN_ENOMEM = -3,     /* the library could not allocate its workspace */
+    QKN_EHIP = -4,       /* a HIP runtime call or launch failed */
+    QKN_ERESIDENCY = -5, /* not even n_shards workgroups can be co-resident */
+    QKN_ETIMEOUT = -6,   /* (qknorm_check_fault) a shard exchange timed out */
+    QKN_ECAPTURE = -7    /* fused call issued on a stream under graph capture */
+} qknorm_status;
+
+typedef enum qknorm_dtype { QKN_BF16 = 0, QKN_F32 = 1 } qknorm_dtype;
+
+#define QKN_MAX_SHARDS 32
+
+/* ------------------------------------------------------------------ fused
+ * Fused Q+K layerwise RMSNorm (Algorithm 1, Phases A-C, persistent grid of
+ * Section III-D). q [T][Hq], k [T][Hk], gamma_q [Hq], gamma_k [Hk] in, out_q
+ * [T][Hq], out_k [T][Hk] out, all of the suffix dtype; fp32 accumulation.
+ * n_shards must divide both Hq and Hk; shard s of Q and shard s of K belong
+ * to the same logical rank. eps is added to the mean square inside the
+ * square root.
+ *
+ * The library owns a small per-(device, stream) workspace (exchange slots,
+ * fault word), allocated on first use and reused by later calls; calls on
+ * different streams use different workspaces. A shard exchange that does not
+ * complete within the spin limit (default 1 s) abandons the wait, leaves the
+ * outputs unspecified and records a fault that qknorm_check_fault reports.
+ * The fused path refuses streams under graph capture (QKN_ECAPTURE); the
+ * split path below is capturable.
+ */
+int qknorm_layerwise_fwd_bf16(const void* q, const void* k, const void* gamma_q,
+                              const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
+                              int n_shards, float eps, void* out_q, void* out_k,
+                              hipStream_t stream);
+int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q,
+                             const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
+                             int n_shards, float eps, void* out_q, void* out_k,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------ split
+ * The same computation for one tensor as three stream-ordered launches, with
+ * the intermediate statistics in caller-owned device buffers (the unfused
+ * "scalar aggregation, then normalise" order the letter compares against,
+ * Section IV-A).
+ *
+ * qknorm_shard_sumsq_*: Phase A. partials [n_shards][T] fp32, shard-major
+ *   (partials[s * T + t] = sum of x[t][j]^2 over shard s's columns).
+ * qknorm_combine_scale: Phase B combine. rms_inv[t] =
+ *   1 / sqrt( (sum_{s=0}^{n_shards-1} partials[s*T+t]) / H + eps ), the sum in
+ *   fp32 in ascending s. rms_inv is [T] fp32.
+ * qknorm_apply_scale_*: Phases B (x*gamma) and C. out[t][j] =
+ *   round(x[t][j] * gamma[j] * rms_inv[t]) in the suffix dtype.
+ */
+int qknorm_shard_sumsq_bf16(const void* x, int64_t T, int64_t H, int n_shards,
+                            float* partials, hipStream_t stream);
+int qknorm_shard_sumsq_f32(const void* x, int64_t T, int64_t H, int n_shards,
+                           float* partials, hipStream_t stream);
+int qknorm_combine_scale(const float* partials, int64_t T, int64_t H, int n_shards,
+                         float eps, float* rms_inv, hipStream_t stream);
+int qknorm_apply_scale_bf16(const void* x, const void* gamma, const float* rms_inv,
+                            int64_t T, int64_t H, void* out, hipStream_t stream);
+int qknorm_apply_scale_f32(const void* x, const void* gamma, const float* rms_inv,
+                           int64_t T, int64_t H, void* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ service */
+
+/* Synchronises `stream`, then reports and clears the fault word of that
+ * stream's workspace: QKN_OK, QKN_ETIMEOUT, or QKN_EHIP. */
+int qknorm_check_fault(hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* qknorm_strerror(int status);
+
+/* Text of the last HIP error the calling thread saw inside the library, or
+ * "" (thread-local, valid until the thread's next library call). */
+const char* qknorm_last_hip_error(void);
+
+/* Workgroups of the fused kernel that the current device can hold at once
+ * for this dtype and shape (occupancy x compute units); *out receives it. */
+int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_shards,
+                                     int* out);
+
+/* Occupancy of the current device: blocks_per_cu[v] = workgroups of fused
+ * variant v one compute unit can hold (0 = variant unusable for dtype), for
+ * QKN_NUM_VARIANTS variants; *cu_count = compute units. Feeds
+ * qknorm_plan_fused with the numbers the library itself plans with. */
+int qknorm_device_occupancy(int dtype, int* blocks_per_cu, int* cu_count);
+
+/* Frees every workspace the library allocated (all devices and streams).
+ * The caller must ensure no library work is still in flight. */
+int qknorm_release_workspace(void);
+
+/* Host-only launch planning, exposed for tests and tools. Fills *plan for a
+ * device with `cu_count` compute units, of which each holds
+ * `blocks_per_cu[v]` workgroups of kernel variant v (an array of
+ * QKN_NUM_VARIANTS entries; the real path queries the occupancy API). */
+#define QKN_NUM_VARIANTS 5
+typedef struct qknorm_plan {
+    int variant;        /* fused kernel variant, or -1: shape uses the split kernels */
+    int threads;        /* workgroup size */
+    int slots;          /* 16-byte vectors per thread */
+    int rows;           /* tokens per tile */
+    int64_t n_tiles;    /* ceil(T / rows) */
+    int n_groups;       /* workgroup groups; each group = n_shards workgroups */
+    int grid;           /* n_groups * n_shards */
+    int xcd_map;        /* 1: members of a group share blockIdx % 8 */
+    int iters;          /* tiles per group (ceil(n_tiles / n_groups)) */
+} qknorm_plan;
+int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
+                      int cu_count, const int* blocks_per_cu, int aligned,
+                      qknorm_plan* plan);
+
+/* Tuning and test options (process-wide, not thread-safe against running
+ * calls). Keys: */
+enum {
+    QKN_OPT_SPIN_LIMIT_NS = 1,  /* exchange spin budget in ns (default 1e9) */
+    QKN_OPT_FORCE_VARIANT = 2,  /* -1 = planner's choice, else a variant id */
+    QKN_OPT_ROWS = 3,           /* 0 = planner's choice, else rows per tile */
+    QKN_OPT_XCD_MAP = 4,        /* -1 = auto, 0 = off, 1 = on when possible */
+    QKN_OPT_COOPERATIVE = 5,    /* 1 = hipLaunchCooperativeKernel, 0 = plain */
+    QKN_OPT_MAX_GROUPS = 6,     /* 0 = no cap, else cap on workgroup groups */
+    QKN_OPT_FORCE_SPLIT = 7,    /* 1 = fused entry points run the split kernels */
+    QKN_OPT_TEST_SKIP_PUBLISH = 8 /* test hook: 1 = fused workgroups never publish
+                                     their partial, so every exchange with n_shards
+                                     > 1 ends at the spin limit (kernel still exits) */
+};
+int qknorm_set_option(int key, int64_t value);
+int64_t qknorm_get_option(int key);
+
+/* Bandwidth ceiling for measurements: copies q -> out_q and k -> out_k
+ * (bytes_q, bytes_k bytes) with the fused kernel's access widths. */
+int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
+                      int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNORM_H */

@@ -1,0 +1,687 @@
+// Host runtime and C ABI of the layerwise QK-Norm library (see include/qknorm.h).
+//
+// Responsibilities: synchronous argument validation; launch planning (kernel
+// variant, tile rows, a persistent grid bounded by co-residency -- "SwiftQK",
+// Section III-D: at most B_res x N_CU workgroups so that every member of an
+// exchange is resident); one workspace per (device, stream) holding the
+// exchange slots and the fault word; kernel launches on the caller's stream.
+#include "qknorm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "qknorm_kernels.hpp"
+
+namespace {
+
+using qkn::Bf16;
+using qkn::F32;
+using qkn::FusedParams;
+
+// ---------------------------------------------------------------- variants
+
+struct Variant {
+    int nwd;        // data waves (plus one comm wave)
+    int vpt;        // 16-byte slots per data thread
+    int rmax;       // max tokens per tile
+    bool prefetch;  // next tile loaded during the exchange
+    bool f32_only;  // register budget only fits fp32 (u can overwrite x in place)
+};
+constexpr Variant kVariants[QKN_NUM_VARIANTS] = {
+    {4, 2, 4, true, false},    //  512 slots
+    {4, 4, 2, true, false},    // 1024 slots
+    {8, 4, 1, true, false},    // 2048 slots
+    {11, 6, 1, true, false},   // 4224 slots
+    {15, 9, 1, false, true},   // 8640 slots
+};
+
+using FusedFn = void (*)(FusedParams);
+
+template <class DT>
+FusedFn fused_fn(int v)
+{
+    switch (v) {
+    case 0: return qkn::fused_qknorm_kernel<DT, 4, 2, 4, true>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 4, 4, 2, true>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 8, 4, 1, true>;
+    case 3: return qkn::fused_qknorm_kernel<DT, 11, 6, 1, true>;
+    default: return nullptr;
+    }
+}
+template <>
+FusedFn fused_fn<F32>(int v)
+{
+    switch (v) {
+    case 0: return qkn::fused_qknorm_kernel<F32, 4, 2, 4, true>;
+    case 1: return qkn::fused_qknorm_kernel<F32, 4, 4, 2, true>;
+    case 2: return qkn::fused_qknorm_kernel<F32, 8, 4, 1, true>;
+    case 3: return qkn::fused_qknorm_kernel<F32, 11, 6, 1, true>;
+    case 4: return qkn::fused_qknorm_kernel<F32, 15, 9, 1, false>;
+    default: return nullptr;
+    }
+}
+FusedFn fused_fn_for(int dtype, int v) { return dtype == QKN_BF16 ? fused_fn<Bf16>(v) : fused_fn<F32>(v); }
+
+int threads_of(int v) { return 64 * (kVariants[v].nwd + 1); }
+
+// ---------------------------------------------------------------- options
+
+struct Options {
+    int64_t spin_ns = 1000000000;
+    int64_t force_variant = -1;
+    int64_t rows = 0;
+    int64_t xcd_map = -1;
+    int64_t cooperative = 0;
+    int64_t max_groups = 0;
+    int64_t force_split = 0;
+    int64_t test_skip_publish = 0;
+};
+Options g_opt;
+
+thread_local std::string t_hip_error;
+
+int hip_fail(hipError_t e, const char* what)
+{
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    t_hip_error = buf;
+    return QKN_EHIP;
+}
+#define QKN_HIP(call)                                         \
+    do {                                                      \
+        hipError_t e_ = (call);                               \
+        if (e_ != hipSuccess) return hip_fail(e_, #call);     \
+    } while (0)
+
+// ---------------------------------------------------------------- device info
+
+struct DevInfo {
+    int cu = 0;
+    int wall_khz = 0;
+    bool occ_done[2] = {false, false};
+    int occ[2][QKN_NUM_VARIANTS] = {};
+};
+
+std::mutex g_mu;
+std::map<int, DevInfo> g_dev;
+
+int device_info(int dev, int dtype, DevInfo** out)
+{
+    DevInfo& d = g_dev[dev];
+    if (d.cu == 0) {
+        QKN_HIP(hipDeviceGetAttribute(&d.cu, hipDeviceAttributeMultiprocessorCount, dev));
+        QKN_HIP(hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev));
+        if (d.wall_khz <= 0) d.wall_khz = 100000;
+    }
+    if (!d.occ_done[dtype]) {
+        for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
+            FusedFn fn = fused_fn_for(dtype, v);
+            int n = 0;
+            if (fn && !(kVariants[v].f32_only && dtype != QKN_F32)) {
+                QKN_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, reinterpret_cast<const void*>(fn), threads_of(v), 0));
+            }
+            d.occ[dtype][v] = n;
+        }
+        d.occ_done[dtype] = true;
+    }
+    *out = &d;
+    return QKN_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+
+struct Workspace {
+    int device = -1;
+    unsigned long long* slots = nullptr;
+    size_t slot_entries = 0;
+    uint32_t* fault = nullptr;
+    uint32_t tag_base = 1;
+    float* scratch = nullptr;  // split fallback: partials and rms_inv
+    size_t scratch_floats = 0;
+};
+
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int workspace_for(int dev, hipStream_t stream, Workspace** out)
+{
+    Workspace& w = g_ws[{dev, stream}];
+    if (!w.fault) {
+        w.device = dev;
+        void* p = nullptr;
+        if (hipMalloc(&p, 256) != hipSuccess) return QKN_ENOMEM;
+        w.fault = static_cast<uint32_t*>(p);
+        QKN_HIP(hipMemsetAsync(w.fault, 0, 256, stream));
+    }
+    *out = &w;
+    return QKN_OK;
+}
+
+int ensure_slots(Workspace* w, size_t entries, hipStream_t stream)
+{
+    if (entries <= w->slot_entries) return QKN_OK;
+    if (w->slots) {
+        QKN_HIP(hipStreamSynchronize(stream));
+        QKN_HIP(hipFree(w->slots));
+        w->slots = nullptr;
+        w->slot_entries = 0;
+    }
+    size_t n = std::max<size_t>(entries, 1 << 15);
+    void* p = nullptr;
+    if (hipMalloc(&p, n * sizeof(unsigned long long)) != hipSuccess) return QKN_ENOMEM;
+    w->slots = static_cast<unsigned long long*>(p);
+    w->slot_entries = n;
+    QKN_HIP(hipMemsetAsync(w->slots, 0, n * sizeof(unsigned long long), stream));
+    w->tag_base = 1;
+    return QKN_OK;
+}
+
+int ensure_scratch(Workspace* w, size_t floats, hipStream_t stream)
+{
+    if (floats <= w->scratch_floats) return QKN_OK;
+    if (w->scratch) {
+        QKN_HIP(hipStreamSynchronize(stream));
+        QKN_HIP(hipFree(w->scratch));
+        w->scratch = nullptr;
+        w->scratch_floats = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, floats * sizeof(float)) != hipSuccess) return QKN_ENOMEM;
+    w->scratch = static_cast<float*>(p);
+    w->scratch_floats = floats;
+    return QKN_OK;
+}
+
+// ---------------------------------------------------------------- validation
+
+struct Range {
+    uintptr_t lo, hi;
+};
+Range range_of(const void* p, int64_t bytes)
+{
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + (uintptr_t)bytes};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+bool same(Range a, Range b) { return a.lo == b.lo && a.hi == b.hi; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_dims(int64_t T, int64_t H, int n_shards)
+{
+    if (T < 0 || H < 1 || H > (int64_t(1) << 28)) return QKN_EINVAL;
+    if (n_shards < 1 || n_shards > QKN_MAX_SHARDS) return QKN_EINVAL;
+    if (H % n_shards != 0) return QKN_EINVAL;
+    return QKN_OK;
+}
+bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.f; }
+
+int elem_size(int dtype) { return dtype == QKN_BF16 ? 2 : 4; }
+
+int current_device(int* dev)
+{
+    QKN_HIP(hipGetDevice(dev));
+    return QKN_OK;
+}
+
+// ---------------------------------------------------------------- planning
+
+int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int* bpc,
+         int aligned, qknorm_plan* out)
+{
+    std::memset(out, 0, sizeof *out);
+    out->variant = -1;
+    if (dtype != QKN_BF16 && dtype != QKN_F32) return QKN_EINVAL;
+    int rc = check_dims(T, Hq, N);
+    if (rc) return rc;
+    rc = check_dims(T, Hk, N);
+    if (rc) return rc;
+    if (cu < 1 || !bpc) return QKN_EINVAL;
+    const int ev = 16 / elem_size(dtype);
+    const int64_t Wq = Hq / N, Wk = Hk / N;
+    if (!aligned || Wq % ev || Wk % ev || g_opt.force_split) return QKN_OK;  // split kernels
+    const int64_t vrow = (Wq + Wk) / ev;
+    int v = -1;
+    for (int c = 0; c < QKN_NUM_VARIANTS; ++c) {
+        if (g_opt.force_variant >= 0 && c != g_opt.force_variant) continue;
+        const Variant& k = kVariants[c];
+        if (k.f32_only && dtype != QKN_F32) continue;
+        if ((int64_t)64 * k.nwd * k.vpt < vrow) continue;
+        if (N * 2 * k.rmax > 64) continue;
+        if (bpc[c] <= 0) continue;
+        v = c;
+        break;
+    }
+    if (v < 0) return QKN_OK;  // no fused variant fits: split kernels
+    const Variant& k = kVariants[v];
+    const int64_t cap = (int64_t)bpc[v] * cu;
+    if (cap < N) return QKN_ERESIDENCY;
+    const int64_t slots = (int64_t)64 * k.nwd * k.vpt;
+    int rows = (int)std::min<int64_t>(k.rmax, slots / vrow);
+    if (g_opt.rows > 0) {
+        rows = (int)std::min<int64_t>(rows, g_opt.rows);
+    } else {
+        // fewer rows per tile while that still leaves the grid short of capacity
+        while (rows > 1 && ((T + rows - 1) / rows) * N < cap) --rows;
+    }
+    const int64_t n_tiles = (T + rows - 1) / rows;
+    int64_t groups = std::min<int64_t>(n_tiles, cap / N);
+    if (g_opt.max_groups > 0) groups = std::min<int64_t>(groups, g_opt.max_groups);
+    int xcd = 0;
+    if (g_opt.xcd_map != 0 && groups >= 8) {
+        if (groups < n_tiles) groups -= groups % 8;  // capped: round to whole XCD sets
+        xcd = (groups % 8 == 0) ? 1 : 0;
+    }
+    if (groups < 1) groups = 1;
+    out->variant = v;
+    out->threads = threads_of(v);
+    out->slots = k.vpt;
+    out->rows = rows;
+    out->n_tiles = n_tiles;
+    out->n_groups = (int)groups;
+    out->grid = (int)(groups * N);
+    out->xcd_map = xcd;
+    out->iters = (int)((n_tiles + groups - 1) / groups);
+    return QKN_OK;
+}
+
+// ---------------------------------------------------------------- split launches
+
+int launch_sumsq(int dtype, const void* x, int64_t T, int64_t H, int N, float* partials,
+                 hipStream_t s)
+{
+    const int64_t items = T * N;
+    const int64_t blocks = (items + 3) / 4;
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    const int W = (int)(H / N);
+    const bool vec = aligned16(x) && (W * elem_size(dtype)) % 16 == 0;
+    dim3 g((unsigned)blocks), b(256);
+    if (dtype == QKN_BF16) {
+        if (vec) hipLaunchKernelGGL((qkn::shard_sumsq_kernel<Bf16, true>), g, b, 0, s, x, T, (int)H, N, partials);
+        else hipLaunchKernelGGL((qkn::shard_sumsq_kernel<Bf16, false>), g, b, 0, s, x, T, (int)H, N, partials);
+    } else {
+        if (vec) hipLaunchKernelGGL((qkn::shard_sumsq_kernel<F32, true>), g, b, 0, s, x, T, (int)H, N, partials);
+        else hipLaunchKernelGGL((qkn::shard_sumsq_kernel<F32, false>), g, b, 0, s, x, T, (int)H, N, partials);
+    }
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+int launch_combine(const float* partials, int64_t T, int64_t H, int N, float eps, float* rinv,
+                   hipStream_t s)
+{
+    const int64_t blocks = (T + 255) / 256;
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    hipLaunchKernelGGL(qkn::combine_scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       partials, T, (int)H, N, eps, rinv);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+int launch_apply(int dtype, const void* x, const void* g, const float* rinv, int64_t T, int64_t H,
+                 void* y, hipStream_t s)
+{
+    const int es = elem_size(dtype);
+    const bool vec = aligned16(x) && aligned16(g) && aligned16(y) && (H * es) % 16 == 0;
+    const int64_t per_row = vec ? H * es / 16 : H;
+    const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, 2048 / per_row));
+    const int64_t blocks = (T + rpb - 1) / rpb;
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    dim3 gr((unsigned)blocks), b(256);
+    if (dtype == QKN_BF16) {
+        if (vec) hipLaunchKernelGGL((qkn::apply_scale_kernel<Bf16, true>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
+        else hipLaunchKernelGGL((qkn::apply_scale_kernel<Bf16, false>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
+    } else {
+        if (vec) hipLaunchKernelGGL((qkn::apply_scale_kernel<F32, true>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
+        else hipLaunchKernelGGL((qkn::apply_scale_kernel<F32, false>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
+    }
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+// ---------------------------------------------------------------- fused entry
+
+int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const void* gk,
+                  int64_t T, int64_t Hq, int64_t Hk, int N, float eps, void* oq, void* ok,
+                  hipStream_t stream)
+{
+    t_hip_error.clear();
+    int rc = check_dims(T, Hq, N);
+    if (rc) return rc;
+    if ((rc = check_dims(T, Hk, N))) return rc;
+    if (!eps_ok(eps)) return QKN_EINVAL;
+    if (T == 0) return QKN_OK;
+    if (!q || !k || !gq || !gk || !oq || !ok) return QKN_EINVAL;
+    const int es = elem_size(dtype);
+    const Range rq = range_of(q, T * Hq * es), rk = range_of(k, T * Hk * es);
+    const Range rgq = range_of(gq, Hq * es), rgk = range_of(gk, Hk * es);
+    const Range roq = range_of(oq, T * Hq * es), rok = range_of(ok, T * Hk * es);
+    if (overlaps(roq, rok)) return QKN_EOVERLAP;
+    if (overlaps(roq, rq) && !same(roq, rq)) return QKN_EOVERLAP;
+    if (overlaps(rok, rk) && !same(rok, rk)) return QKN_EOVERLAP;
+    if (overlaps(roq, rk) || overlaps(roq, rgq) || overlaps(roq, rgk)) return QKN_EOVERLAP;
+    if (overlaps(rok, rq) || overlaps(rok, rgq) || overlaps(rok, rgk)) return QKN_EOVERLAP;
+
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    QKN_HIP(hipStreamIsCapturing(stream, &cap));
+    if (cap != hipStreamCaptureStatusNone) return QKN_ECAPTURE;
+
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if ((rc = current_device(&dev))) return rc;
+    DevInfo* di = nullptr;
+    if ((rc = device_info(dev, dtype, &di))) return rc;
+    Workspace* ws = nullptr;
+    if ((rc = workspace_for(dev, stream, &ws))) return rc;
+
+    const int aligned = aligned16(q) && aligned16(k) && aligned16(gq) && aligned16(gk) &&
+                        aligned16(oq) && aligned16(ok);
+    qknorm_plan pl;
+    if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, di->occ[dtype], aligned, &pl))) return rc;
+
+    if (pl.variant < 0) {
+        // Shapes the fused kernel cannot hold in registers (or unaligned): the
+        // same computation with the three split kernels, per tensor.
+        const size_t need = (size_t)(N + 1) * (size_t)T;
+        if ((rc = ensure_scratch(ws, need, stream))) return rc;
+        float* part = ws->scratch;
+        float* rinv = ws->scratch + (size_t)N * T;
+        const void* xs[2] = {q, k};
+        const void* gs[2] = {gq, gk};
+        void* ys[2] = {oq, ok};
+        const int64_t Hs[2] = {Hq, Hk};
+        for (int i = 0; i < 2; ++i) {
+            if ((rc = launch_sumsq(dtype, xs[i], T, Hs[i], N, part, stream))) return rc;
+            if ((rc = launch_combine(part, T, Hs[i], N, eps, rinv, stream))) return rc;
+            if ((rc = launch_apply(dtype, xs[i], gs[i], rinv, T, Hs[i], ys[i], stream))) return rc;
+        }
+        return QKN_OK;
+    }
+
+    const Variant& var = kVariants[pl.variant];
+    const size_t entries = (size_t)pl.n_groups * 2 * N * 2 * var.rmax;
+    if ((rc = ensure_slots(ws, entries, stream))) return rc;
+    if ((uint64_t)ws->tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
+        // tags would wrap: clear every slot so no stale tag can match
+        QKN_HIP(hipMemsetAsync(ws->slots, 0, ws->slot_entries * sizeof(unsigned long long), stream));
+        ws->tag_base = 1;
+    }
+
+    FusedParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x[0] = q;
+    p.x[1] = k;
+    p.gamma[0] = gq;
+    p.gamma[1] = gk;
+    p.y[0] = oq;
+    p.y[1] = ok;
+    p.T = T;
+    p.n_tiles = pl.n_tiles;
+    p.H[0] = (int32_t)Hq;
+    p.H[1] = (int32_t)Hk;
+    const int ev = 16 / es;
+    p.Wv[0] = (int32_t)(Hq / N / ev);
+    p.Wv[1] = (int32_t)(Hk / N / ev);
+    p.rows = pl.rows;
+    p.n_shards = N;
+    p.n_groups = pl.n_groups;
+    p.xcd_map = pl.xcd_map;
+    p.eps = eps;
+    p.tag_base = ws->tag_base;
+    p.slots = ws->slots;
+    p.fault = ws->fault;
+    const double ticks = (double)g_opt.spin_ns * 1e-9 * (double)di->wall_khz * 1e3;
+    p.spin_ticks = ticks < 1.0 ? 1 : (uint64_t)ticks;
+    p.test_flags = g_opt.test_skip_publish ? 1u : 0u;
+    ws->tag_base += (uint32_t)pl.iters;
+
+    FusedFn fn = fused_fn_for(dtype, pl.variant);
+    if (g_opt.cooperative) {
+        void* args[] = {&p};
+        QKN_HIP(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(pl.grid),
+                                           dim3(pl.threads), args, 0, stream));
+    } else {
+        hipLaunchKernelGGL(fn, dim3(pl.grid), dim3(pl.threads), 0, stream, p);
+        QKN_HIP(hipGetLastError());
+    }
+    return QKN_OK;
+}
+
+int shard_sumsq(int dtype, const void* x, int64_t T, int64_t H, int N, float* partials,
+                hipStream_t s)
+{
+    t_hip_error.clear();
+    int rc = check_dims(T, H, N);
+    if (rc) return rc;
+    if (T == 0) return QKN_OK;
+    if (!x || !partials) return QKN_EINVAL;
+    const int es = elem_size(dtype);
+    if (overlaps(range_of(partials, (int64_t)N * T * 4), range_of(x, T * H * es))) return QKN_EOVERLAP;
+    return launch_sumsq(dtype, x, T, H, N, partials, s);
+}
+
+int apply_scale(int dtype, const void* x, const void* g, const float* rinv, int64_t T, int64_t H,
+                void* y, hipStream_t s)
+{
+    t_hip_error.clear();
+    int rc = check_dims(T, H, 1);
+    if (rc) return rc;
+    if (T == 0) return QKN_OK;
+    if (!x || !g || !rinv || !y) return QKN_EINVAL;
+    const int es = elem_size(dtype);
+    const Range ry = range_of(y, T * H * es), rx = range_of(x, T * H * es);
+    if (overlaps(ry, rx) && !same(ry, rx)) return QKN_EOVERLAP;
+    if (overlaps(ry, range_of(g, H * es)) || overlaps(ry, range_of(rinv, T * 4))) return QKN_EOVERLAP;
+    return launch_apply(dtype, x, g, rinv, T, H, y, s);
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+
+extern "C" {
+
+int qknorm_layerwise_fwd_bf16(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
+                              int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
+                              void* out_q, void* out_k, hipStream_t stream)
+{
+    return layerwise_fwd(QKN_BF16, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps, out_q, out_k,
+                         stream);
+}
+
+int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
+                             int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
+                             void* out_q, void* out_k, hipStream_t stream)
+{
+    return layerwise_fwd(QKN_F32, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps, out_q, out_k,
+                         stream);
+}
+
+int qknorm_shard_sumsq_bf16(const void* x, int64_t T, int64_t H, int n_shards, float* partials,
+                            hipStream_t stream)
+{
+    return shard_sumsq(QKN_BF16, x, T, H, n_shards, partials, stream);
+}
+
+int qknorm_shard_sumsq_f32(const void* x, int64_t T, int64_t H, int n_shards, float* partials,
+                           hipStream_t stream)
+{
+    return shard_sumsq(QKN_F32, x, T, H, n_shards, partials, stream);
+}
+
+int qknorm_combine_scale(const float* partials, int64_t T, int64_t H, int n_shards, float eps,
+                         float* rms_inv, hipStream_t stream)
+{
+    t_hip_error.clear();
+    int rc = check_dims(T, H, n_shards);
+    if (rc) return rc;
+    if (!eps_ok(eps)) return QKN_EINVAL;
+    if (T == 0) return QKN_OK;
+    if (!partials || !rms_inv) return QKN_EINVAL;
+    if (overlaps(range_of(partials, (int64_t)n_shards * T * 4), range_of(rms_inv, T * 4)))
+        return QKN_EOVERLAP;
+    return launch_combine(partials, T, H, n_shards, eps, rms_inv, stream);
+}
+
+int qknorm_apply_scale_bf16(const void* x, const void* gamma, const float* rms_inv, int64_t T,
+                            int64_t H, void* out, hipStream_t stream)
+{
+    return apply_scale(QKN_BF16, x, gamma, rms_inv, T, H, out, stream);
+}
+
+int qknorm_apply_scale_f32(const void* x, const void* gamma, const float* rms_inv, int64_t T,
+                           int64_t H, void* out, hipStream_t stream)
+{
+    return apply_scale(QKN_F32, x, gamma, rms_inv, T, H, out, stream);
+}
+
+int qknorm_check_fault(hipStream_t stream)
+{
+    t_hip_error.clear();
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    QKN_HIP(hipStreamSynchronize(stream));
+    uint32_t* fault = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_ws.find({dev, stream});
+        if (it == g_ws.end() || !it->second.fault) return QKN_OK;
+        fault = it->second.fault;
+    }
+    uint32_t h = 0;
+    QKN_HIP(hipMemcpy(&h, fault, sizeof h, hipMemcpyDeviceToHost));
+    if (h == 0) return QKN_OK;
+    QKN_HIP(hipMemset(fault, 0, sizeof h));
+    return QKN_ETIMEOUT;
+}
+
+const char* qknorm_strerror(int status)
+{
+    switch (status) {
+    case QKN_OK: return "success";
+    case QKN_EINVAL: return "invalid argument";
+    case QKN_EOVERLAP: return "an output partially overlaps an input or another output";
+    case QKN_ENOMEM: return "workspace allocation failed";
+    case QKN_EHIP: return "HIP runtime error";
+    case QKN_ERESIDENCY: return "the device cannot hold n_shards co-resident workgroups";
+    case QKN_ETIMEOUT: return "a shard exchange timed out; outputs of that call are unspecified";
+    case QKN_ECAPTURE: return "the fused path cannot be issued under stream capture";
+    default: return "unknown status";
+    }
+}
+
+const char* qknorm_last_hip_error(void) { return t_hip_error.c_str(); }
+
+int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_shards, int* out)
+{
+    t_hip_error.clear();
+    if (!out || (dtype != QKN_BF16 && dtype != QKN_F32)) return QKN_EINVAL;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0, rc = current_device(&dev);
+    if (rc) return rc;
+    DevInfo* di = nullptr;
+    if ((rc = device_info(dev, dtype, &di))) return rc;
+    qknorm_plan pl;
+    if ((rc = plan(dtype, 1, Hq, Hk, n_shards, di->cu, di->occ[dtype], 1, &pl))) return rc;
+    *out = pl.variant < 0 ? 0 : di->occ[dtype][pl.variant] * di->cu;
+    return QKN_OK;
+}
+
+int qknorm_device_occupancy(int dtype, int* blocks_per_cu, int* cu_count)
+{
+    t_hip_error.clear();
+    if (!blocks_per_cu || !cu_count || (dtype != QKN_BF16 && dtype != QKN_F32)) return QKN_EINVAL;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0, rc = current_device(&dev);
+    if (rc) return rc;
+    DevInfo* di = nullptr;
+    if ((rc = device_info(dev, dtype, &di))) return rc;
+    for (int v = 0; v < QKN_NUM_VARIANTS; ++v) blocks_per_cu[v] = di->occ[dtype][v];
+    *cu_count = di->cu;
+    return QKN_OK;
+}
+
+int qknorm_release_workspace(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    for (auto& kv : g_ws) {
+        Workspace& w = kv.second;
+        (void)hipSetDevice(w.device);
+        if (w.slots) (void)hipFree(w.slots);
+        if (w.fault) (void)hipFree(w.fault);
+        if (w.scratch) (void)hipFree(w.scratch);
+    }
+    g_ws.clear();
+    (void)hipSetDevice(prev);
+    return QKN_OK;
+}
+
+int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards, int cu_count,
+                      const int* blocks_per_cu, int aligned, qknorm_plan* out)
+{
+    if (!out) return QKN_EINVAL;
+    return plan(dtype, T, Hq, Hk, n_shards, cu_count, blocks_per_cu, aligned, out);
+}
+
+int qknorm_set_option(int key, int64_t value)
+{
+    switch (key) {
+    case QKN_OPT_SPIN_LIMIT_NS: if (value < 1) return QKN_EINVAL; g_opt.spin_ns = value; return QKN_OK;
+    case QKN_OPT_FORCE_VARIANT:
+        if (value < -1 || value >= QKN_NUM_VARIANTS) return QKN_EINVAL;
+        g_opt.force_variant = value; return QKN_OK;
+    case QKN_OPT_ROWS: if (value < 0) return QKN_EINVAL; g_opt.rows = value; return QKN_OK;
+    case QKN_OPT_XCD_MAP: if (value < -1 || value > 1) return QKN_EINVAL; g_opt.xcd_map = value; return QKN_OK;
+    case QKN_OPT_COOPERATIVE: g_opt.cooperative = value ? 1 : 0; return QKN_OK;
+    case QKN_OPT_MAX_GROUPS: if (value < 0) return QKN_EINVAL; g_opt.max_groups = value; return QKN_OK;
+    case QKN_OPT_FORCE_SPLIT: g_opt.force_split = value ? 1 : 0; return QKN_OK;
+    case QKN_OPT_TEST_SKIP_PUBLISH: g_opt.test_skip_publish = value ? 1 : 0; return QKN_OK;
+    default: return QKN_EINVAL;
+    }
+}
+
+int64_t qknorm_get_option(int key)
+{
+    switch (key) {
+    case QKN_OPT_SPIN_LIMIT_NS: return g_opt.spin_ns;
+    case QKN_OPT_FORCE_VARIANT: return g_opt.force_variant;
+    case QKN_OPT_ROWS: return g_opt.rows;
+    case QKN_OPT_XCD_MAP: return g_opt.xcd_map;
+    case QKN_OPT_COOPERATIVE: return g_opt.cooperative;
+    case QKN_OPT_MAX_GROUPS: return g_opt.max_groups;
+    case QKN_OPT_FORCE_SPLIT: return g_opt.force_split;
+    case QKN_OPT_TEST_SKIP_PUBLISH: return g_opt.test_skip_publish;
+    default: return INT64_MIN;
+    }
+}
+
+int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k, int64_t bytes_q,
+                      int64_t bytes_k, hipStream_t stream)
+{
+    t_hip_error.clear();
+    if (bytes_q < 0 || bytes_k < 0) return QKN_EINVAL;
+    if (bytes_q + bytes_k == 0) return QKN_OK;
+    if (!q || !k || !out_q || !out_k) return QKN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(out_q) || !aligned16(out_k)) return QKN_EINVAL;
+    const int64_t va = bytes_q / 16, vb = bytes_k / 16;
+    int dev = 0, cu = 0, rc = current_device(&dev);
+    if (rc) return rc;
+    QKN_HIP(hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev));
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((va + vb + 255) / 256, (int64_t)cu * 16));
+    hipLaunchKernelGGL(qkn::copy2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, k, out_q,
+                       out_k, va, vb, bytes_q - va * 16, bytes_k - vb * 16);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+}  // extern "C"

@@ -194,3 +194,24 @@ def make_device_activations(w: Workload, which: str, device, torch):
             a[:, torch.as_tensor(cols, device=device)] *= w.outlier_scale
         out[lo:hi] = a.to(out_dtype)
     return out
+
+
+# ---------------------------------------------------------------- transfers
+
+def to_device(a: np.ndarray, device, torch):
+    """numpy bf16 bit patterns (uint16) or float32 -> torch tensor on ``device``."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.float32:
+        return torch.from_numpy(a).to(device)
+    raise TypeError(a.dtype)
+
+
+def from_device(t) -> np.ndarray:
+    """torch tensor -> numpy bf16 bit patterns (uint16) or float32."""
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -1,0 +1,282 @@
+"""Python binding of ``libqknorm.so`` (argument marshalling only).
+
+Every function has the C entry point's name without the ``qknorm_`` prefix
+and the dtype suffix; the dtype comes from the tensors. PyTorch supplies
+device memory and the stream (the current stream of the tensors' device);
+all computation runs in the library's HIP kernels. If the library is not
+built, the first call raises ``RuntimeError`` -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqknorm.so")
+_lib = None
+_lock = threading.Lock()
+
+QKN_OK, QKN_EINVAL, QKN_EOVERLAP, QKN_ENOMEM, QKN_EHIP = 0, -1, -2, -3, -4
+QKN_ERESIDENCY, QKN_ETIMEOUT, QKN_ECAPTURE = -5, -6, -7
+QKN_BF16, QKN_F32 = 0, 1
+NUM_VARIANTS = 5
+MAX_SHARDS = 32
+OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
+       "max_groups": 6, "force_split": 7, "test_skip_publish": 8}
+
+
+class QKNormError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = f"{what}: {strerror(status)} ({status})"
+        hip = last_hip_error()
+        if hip:
+            msg += f" [{hip}]"
+        super().__init__(msg)
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("threads", ctypes.c_int), ("slots", ctypes.c_int),
+                ("rows", ctypes.c_int), ("n_tiles", ctypes.c_int64), ("n_groups", ctypes.c_int),
+                ("grid", ctypes.c_int), ("xcd_map", ctypes.c_int), ("iters", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+_SIGS = {
+    "qknorm_layerwise_fwd_bf16": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
+    "qknorm_layerwise_fwd_f32": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
+    "qknorm_shard_sumsq_bf16": [_P, _I64, _I64, _I, _P, _P],
+    "qknorm_shard_sumsq_f32": [_P, _I64, _I64, _I, _P, _P],
+    "qknorm_combine_scale": [_P, _I64, _I64, _I, _F, _P, _P],
+    "qknorm_apply_scale_bf16": [_P, _P, _P, _I64, _I64, _P, _P],
+    "qknorm_apply_scale_f32": [_P, _P, _P, _I64, _I64, _P, _P],
+    "qknorm_check_fault": [_P],
+    "qknorm_strerror": [_I],
+    "qknorm_last_hip_error": [],
+    "qknorm_max_coresident_workgroups": [_I, _I64, _I64, _I, ctypes.POINTER(_I)],
+    "qknorm_release_workspace": [],
+    "qknorm_device_occupancy": [_I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
+    "qknorm_plan_fused": [_I, _I64, _I64, _I64, _I, _I, ctypes.POINTER(_I), _I,
+                          ctypes.POINTER(Plan)],
+    "qknorm_set_option": [_I, _I64],
+    "qknorm_get_option": [_I],
+    "qknorm_bench_copy": [_P, _P, _P, _P, _I64, _I64, _P],
+}
+_RESTYPE = {"qknorm_strerror": ctypes.c_char_p, "qknorm_last_hip_error": ctypes.c_char_p,
+            "qknorm_get_option": ctypes.c_int64}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(_LIB_PATH):
+                    raise RuntimeError(
+                        f"{_LIB_PATH} is missing: build it with "
+                        "`python -m layerwise_qk_norm_amd.build` (there is no fallback path)")
+                L = ctypes.CDLL(_LIB_PATH)
+                for name, args in _SIGS.items():
+                    fn = getattr(L, name)
+                    fn.argtypes = args
+                    fn.restype = _RESTYPE.get(name, ctypes.c_int)
+                _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().qknorm_strerror(status).decode()
+
+
+def last_hip_error() -> str:
+    return lib().qknorm_last_hip_error().decode()
+
+
+def _check(status: int, what: str):
+    if status != QKN_OK:
+        raise QKNormError(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return QKN_BF16
+    if t.dtype == torch.float32:
+        return QKN_F32
+    raise TypeError(f"tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _suffix(code: int) -> str:
+    return "bf16" if code == QKN_BF16 else "f32"
+
+
+def _need(t: torch.Tensor, name: str, ndim: int, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_q=None,
+                  out_k=None):
+    """Fused Q+K layerwise RMSNorm; returns ``(out_q, out_k)``."""
+    _need(q, "q", 2)
+    dt = q.dtype
+    dev = q.device
+    _need(k, "k", 2, dt, dev)
+    _need(gamma_q, "gamma_q", 1, dt, dev)
+    _need(gamma_k, "gamma_k", 1, dt, dev)
+    T, Hq = q.shape
+    if k.shape[0] != T:
+        raise ValueError("q and k must have the same number of tokens")
+    Hk = k.shape[1]
+    if gamma_q.shape[0] != Hq or gamma_k.shape[0] != Hk:
+        raise ValueError("gamma_q must be [Hq] and gamma_k [Hk]")
+    out_q = torch.empty_like(q) if out_q is None else out_q
+    out_k = torch.empty_like(k) if out_k is None else out_k
+    _need(out_q, "out_q", 2, dt, dev)
+    _need(out_k, "out_k", 2, dt, dev)
+    if out_q.shape != q.shape or out_k.shape != k.shape:
+        raise ValueError("outputs must have the shapes of q and k")
+    code = _dtype_code(q)
+    fn = getattr(lib(), f"qknorm_layerwise_fwd_{_suffix(code)}")
+    with torch.cuda.device(dev):
+        _check(fn(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), T, Hq, Hk,
+                  n_shards, eps, out_q.data_ptr(), out_k.data_ptr(), _stream(dev)),
+               "qknorm_layerwise_fwd")
+    return out_q, out_k
+
+
+def shard_sumsq(x, n_shards: int, partials=None):
+    """Per-shard fp32 sums of squares, ``[n_shards, T]`` (shard-major)."""
+    _need(x, "x", 2)
+    T, H = x.shape
+    if partials is None:
+        partials = torch.empty((n_shards, T), dtype=torch.float32, device=x.device)
+    _need(partials, "partials", 2, torch.float32, x.device)
+    if tuple(partials.shape) != (n_shards, T):
+        raise ValueError("partials must be [n_shards, T]")
+    code = _dtype_code(x)
+    fn = getattr(lib(), f"qknorm_shard_sumsq_{_suffix(code)}")
+    with torch.cuda.device(x.device):
+        _check(fn(x.data_ptr(), T, H, n_shards, partials.data_ptr(), _stream(x.device)),
+               "qknorm_shard_sumsq")
+    return partials
+
+
+def combine_scale(partials, H: int, eps: float = 1e-6, rms_inv=None):
+    """Reciprocal RMS per token from shard partials; ``[T]`` fp32."""
+    _need(partials, "partials", 2, torch.float32)
+    n_shards, T = partials.shape
+    if rms_inv is None:
+        rms_inv = torch.empty((T,), dtype=torch.float32, device=partials.device)
+    _need(rms_inv, "rms_inv", 1, torch.float32, partials.device)
+    if rms_inv.shape[0] != T:
+        raise ValueError("rms_inv must be [T]")
+    with torch.cuda.device(partials.device):
+        _check(lib().qknorm_combine_scale(partials.data_ptr(), T, H, n_shards, eps,
+                                          rms_inv.data_ptr(), _stream(partials.device)),
+               "qknorm_combine_scale")
+    return rms_inv
+
+
+def apply_scale(x, gamma, rms_inv, out=None):
+    """``out = x * gamma * rms_inv[:, None]`` rounded to x's dtype."""
+    _need(x, "x", 2)
+    T, H = x.shape
+    _need(gamma, "gamma", 1, x.dtype, x.device)
+    _need(rms_inv, "rms_inv", 1, torch.float32, x.device)
+    if gamma.shape[0] != H or rms_inv.shape[0] != T:
+        raise ValueError("gamma must be [H] and rms_inv [T]")
+    out = torch.empty_like(x) if out is None else out
+    _need(out, "out", 2, x.dtype, x.device)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    code = _dtype_code(x)
+    fn = getattr(lib(), f"qknorm_apply_scale_{_suffix(code)}")
+    with torch.cuda.device(x.device):
+        _check(fn(x.data_ptr(), gamma.data_ptr(), rms_inv.data_ptr(), T, H, out.data_ptr(),
+                  _stream(x.device)), "qknorm_apply_scale")
+    return out
+
+
+def check_fault(device=None) -> int:
+    """Synchronise the current stream and return (and clear) its fault status."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    with torch.cuda.device(device):
+        return lib().qknorm_check_fault(_stream(device))
+
+
+def set_option(name: str, value: int):
+    _check(lib().qknorm_set_option(OPT[name], int(value)), f"qknorm_set_option({name})")
+
+
+def get_option(name: str) -> int:
+    return int(lib().qknorm_get_option(OPT[name]))
+
+
+def plan_fused(dtype: str, T: int, Hq: int, Hk: int, n_shards: int, cu_count: int,
+               blocks_per_cu, aligned: bool = True) -> dict:
+    """Host-only launch plan for a device with the given capacity (no GPU needed)."""
+    arr = (ctypes.c_int * NUM_VARIANTS)(*blocks_per_cu)
+    pl = Plan()
+    _check(lib().qknorm_plan_fused(QKN_BF16 if dtype == "bf16" else QKN_F32, T, Hq, Hk, n_shards,
+                                   cu_count, arr, 1 if aligned else 0, ctypes.byref(pl)),
+           "qknorm_plan_fused")
+    return pl.as_dict()
+
+
+def max_coresident_workgroups(dtype: str, Hq: int, Hk: int, n_shards: int) -> int:
+    out = ctypes.c_int(0)
+    _check(lib().qknorm_max_coresident_workgroups(QKN_BF16 if dtype == "bf16" else QKN_F32, Hq,
+                                                  Hk, n_shards, ctypes.byref(out)),
+           "qknorm_max_coresident_workgroups")
+    return out.value
+
+
+def device_occupancy(dtype: str):
+    """(blocks_per_cu per fused variant, compute units) of the current device."""
+    arr = (ctypes.c_int * NUM_VARIANTS)()
+    cu = ctypes.c_int(0)
+    _check(lib().qknorm_device_occupancy(QKN_BF16 if dtype == "bf16" else QKN_F32, arr,
+                                         ctypes.byref(cu)), "qknorm_device_occupancy")
+    return list(arr), cu.value
+
+
+def current_plan(dtype: str, T: int, Hq: int, Hk: int, n_shards: int, aligned: bool = True):
+    """The plan the library uses for this shape on the current device."""
+    bpc, cu = device_occupancy(dtype)
+    return plan_fused(dtype, T, Hq, Hk, n_shards, cu, bpc, aligned)
+
+
+def bench_copy(q, k, out_q, out_k):
+    with torch.cuda.device(q.device):
+        _check(lib().qknorm_bench_copy(q.data_ptr(), k.data_ptr(), out_q.data_ptr(),
+                                       out_k.data_ptr(), q.numel() * q.element_size(),
+                                       k.numel() * k.element_size(), _stream(q.device)),
+               "qknorm_bench_copy")
+
+
+def release_workspace():
+    _check(lib().qknorm_release_workspace(), "qknorm_release_workspace")

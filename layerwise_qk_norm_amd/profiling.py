@@ -1,0 +1,123 @@
+"""Summaries of rocprofv3 output for the committed ``profiles/`` directory.
+
+``python -m layerwise_qk_norm_amd.profiling trace STATS_CSV OUT_TXT --cmd "..."``
+  writes the per-kernel duration table of a ``--kernel-trace --stats`` run.
+``python -m layerwise_qk_norm_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_TXT --cmd-fetch
+  "..." --cmd-write "..."`` writes HBM bytes per launch of the fused prefill kernel
+  from two ``--pmc`` runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch). Each counter
+  is scaled by what it reads for the copy kernel of known size in the same run
+  (the copy reads and writes exactly the prefill workload's Q and K bytes).
+
+Summaries record the source hash of the kernels they measured; the benchmark
+uses a traffic figure only while that hash matches the current sources.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("qknorm_kernels.hpp", "qknorm.hip")]
+
+# The copy kernel of the --pmc run moves the prefill workload's Q and K:
+# 16384 x (5120 + 5120) bf16 values read and the same written.
+COPY_BYTES = 16384 * (5120 + 5120) * 2
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short(name: str) -> str:
+    return name.replace("(qkn::FusedParams)", "").replace("void ", "")[:110]
+
+
+def summarize_trace(stats_csv: str, out_txt: str, cmd: str, note: str = ""):
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}",
+             f"kernel_source_sha: {kernel_source_sha()}"]
+    if note:
+        lines.append(f"# {note}")
+    lines.append(f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
+    for r in rows:
+        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
+                     f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
+                     f"{float(r['Percentage']):6.2f}  {short(r['Name'])}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+
+
+def _per_kernel(csv_path: str):
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, out_txt: str, cmd_fetch: str,
+                      cmd_write: str, algorithmic_bytes: int):
+    fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
+    copy_name = next(n for n in fetch if "copy2_kernel" in n)
+    fused_name = next(n for n in fetch if "fused_qknorm_kernel" in n)
+    kib_copy_f = statistics.mean(fetch[copy_name])
+    kib_copy_w = statistics.mean(write[copy_name])
+    scale_f = (COPY_BYTES / 1024) / kib_copy_f
+    scale_w = (COPY_BYTES / 1024) / kib_copy_w
+    kib_f = statistics.mean(fetch[fused_name])
+    kib_w = statistics.mean(write[fused_name])
+    fetched = kib_f * scale_f * 1024
+    written = kib_w * scale_w * 1024
+    traffic = fetched + written
+    lines = [
+        "# HBM traffic of the fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)",
+        f"# command (FETCH_SIZE): {cmd_fetch}",
+        f"# command (WRITE_SIZE): {cmd_write}",
+        f"# copy kernel of known size: {COPY_BYTES} B read and {COPY_BYTES} B written",
+        f"kernel_source_sha: {kernel_source_sha()}",
+        f"kernel: {short(fused_name)}",
+        f"dispatches: {len(fetch[fused_name])} (FETCH_SIZE), {len(write[fused_name])} (WRITE_SIZE)",
+        f"fetch_kib_per_dispatch: {kib_f:.3f}",
+        f"write_kib_per_dispatch: {kib_w:.3f}",
+        f"copy_fetch_kib_per_dispatch: {kib_copy_f:.3f}",
+        f"copy_write_kib_per_dispatch: {kib_copy_w:.3f}",
+        f"copy_scale_fetch: {scale_f:.5f}",
+        f"copy_scale_write: {scale_w:.5f}",
+        f"fetched_bytes_per_launch: {fetched:.0f}",
+        f"written_bytes_per_launch: {written:.0f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"algorithmic_bytes_per_launch: {algorithmic_bytes}",
+        f"traffic_over_algorithmic: {traffic / algorithmic_bytes:.4f}",
+    ]
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("out_txt")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--note", default="")
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch_csv")
+    f.add_argument("write_csv")
+    f.add_argument("out_txt")
+    f.add_argument("--cmd-fetch", required=True)
+    f.add_argument("--cmd-write", required=True)
+    f.add_argument("--algorithmic-bytes", type=int, default=671_109_120)
+    a = ap.parse_args()
+    if a.what == "trace":
+        summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note)
+    else:
+        summarize_traffic(a.fetch_csv, a.write_csv, a.out_txt, a.cmd_fetch, a.cmd_write,
+                          a.algorithmic_bytes)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+"""Edge cases, launch options and error paths of the HIP path (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+from layerwise_qk_norm_amd import inputs, ops
+from oracle import compare, oracle
+
+from _gpu import assert_parity, needs_gpu, run_fused, run_split, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+@pytest.fixture(autouse=True)
+def _restore_options():
+    saved = {n: ops.get_option(n) for n in ops.OPT}
+    yield
+    for n, v in saved.items():
+        ops.set_option(n, v)
+
+
+def test_empty_batch_is_a_noop():
+    for dt in (torch.bfloat16, torch.float32):
+        q = torch.empty((0, 256), dtype=dt, device="cuda:0")
+        g = torch.ones(256, dtype=dt, device="cuda:0")
+        oq, ok = ops.layerwise_fwd(q, q.clone(), g, g, 2)
+        assert oq.shape == (0, 256)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 63, 65, 4097])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_token_counts(T, dtype):
+    w = inputs.Workload("r", T, 1024, 512, 2, dtype)
+    d = inputs.make_host(w)
+    oq, ok = run_fused(d, 2, w.eps)
+    assert_parity(d["q"], d["gamma_q"], oq, w.eps)
+    assert_parity(d["k"], d["gamma_k"], ok, w.eps)
+
+
+@pytest.mark.parametrize("N", [1, 3, 5, 16, 32])
+def test_shard_counts(N):
+    H = 256 * N  # 32-wide bf16 shards at N=32... every N divides H
+    w = inputs.Workload("n", 130, H, H, N, "bf16")
+    d = inputs.make_host(w)
+    oq, ok = run_fused(d, N, w.eps)
+    assert_parity(d["q"], d["gamma_q"], oq, w.eps)
+    assert_parity(d["k"], d["gamma_k"], ok, w.eps)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_unaligned_shapes_and_pointers(dtype):
+    # 25-wide shards cannot use 16-byte accesses: the library runs the split kernels
+    w = inputs.Workload("u", 70, 100, 60, 4, dtype)
+    d = inputs.make_host(w)
+    oq, ok = run_fused(d, 4, w.eps)
+    assert_parity(d["q"], d["gamma_q"], oq, w.eps)
+    assert_parity(d["k"], d["gamma_k"], ok, w.eps)
+    # 16-byte-aligned shapes at an odd element offset
+    w = inputs.Workload("o", 33, 1024, 1024, 2, dtype)
+    d = inputs.make_host(w)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    bufs = []
+    for name in ("q", "k"):
+        flat = torch.empty(d[name].size + 1, dtype=dt, device="cuda:0")
+        flat[1:] = to_dev(d[name]).reshape(-1)
+        bufs.append(flat[1:].view(33, 1024))
+    oq, ok = ops.layerwise_fwd(bufs[0], bufs[1], to_dev(d["gamma_q"]), to_dev(d["gamma_k"]), 2)
+    assert_parity(d["q"], d["gamma_q"], to_host(oq), w.eps)
+    assert_parity(d["k"], d["gamma_k"], to_host(ok), w.eps)
+
+
+def test_in_place():
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    q, k = to_dev(d["q"]), to_dev(d["k"])
+    ops.layerwise_fwd(q, k, to_dev(d["gamma_q"]), to_dev(d["gamma_k"]), 4, out_q=q, out_k=k)
+    assert_parity(d["q"], d["gamma_q"], to_host(q), w.eps)
+    assert_parity(d["k"], d["gamma_k"], to_host(k), w.eps)
+
+
+def test_overlap_is_rejected():
+    q = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.ones(256, dtype=torch.bfloat16, device="cuda:0")
+    buf = torch.empty(8 * 256 + 8, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ops.QKNormError) as e:
+        ops.layerwise_fwd(q, k, g, g, 2, out_q=k, out_k=q)
+    assert e.value.status == ops.QKN_EOVERLAP
+    with pytest.raises(ops.QKNormError) as e:
+        ops.layerwise_fwd(q, k, g, g, 2, out_q=buf[:2048].view(8, 256), out_k=buf[8:].view(8, 256))
+    assert e.value.status == ops.QKN_EOVERLAP
+
+
+def test_degenerate_rows():
+    H = 512
+    x = np.zeros((4, H), np.float32)
+    x[1, 3] = np.inf
+    x[2, 7] = np.nan
+    x[3, :] = 1e-3
+    g = np.linspace(0.5, 1.5, H).astype(np.float32)
+    for dtype in ("bf16", "f32"):
+        xd = inputs.store(x.astype(np.float64), dtype)
+        gd = inputs.store(g.astype(np.float64), dtype)
+        d = {"q": xd, "k": xd, "gamma_q": gd, "gamma_k": gd}
+        oq, _ = run_fused(d, 2, 1e-6)
+        y = compare.decode_out(oq)
+        ye, _, _ = oracle.rmsnorm(xd, gd, 1e-6)
+        assert np.all(y[0] == 0)  # zero row, eps > 0
+        assert np.isnan(y[1, 3]) and np.all(y[1, np.arange(H) != 3] == 0)
+        assert np.all(np.isnan(y[2]))
+        assert compare.report(y[3], ye[3])["max_rel"] <= compare.TOL[dtype]
+        oq0, _ = run_fused(d, 2, 0.0)  # zero row with eps = 0: 0 * inf
+        assert np.all(np.isnan(compare.decode_out(oq0)[0]))
+
+
+def test_launch_options_preserve_results():
+    w = inputs.PREFILL.with_T(1000)
+    d = inputs.make_host(w)
+    base = run_fused(d, 2, w.eps)
+    for name, val in (("xcd_map", 0), ("xcd_map", 1), ("cooperative", 1), ("max_groups", 8)):
+        ops.set_option(name, val)
+        got = run_fused(d, 2, w.eps)
+        assert np.array_equal(got[0], base[0]) and np.array_equal(got[1], base[1]), name
+        ops.set_option(name, {"xcd_map": -1, "cooperative": 0, "max_groups": 0}[name])
+    for v in range(ops.NUM_VARIANTS):
+        ops.set_option("force_variant", v)
+        got = run_fused(d, 2, w.eps)
+        assert_parity(d["q"], d["gamma_q"], got[0], w.eps, f"variant {v}")
+    ops.set_option("force_variant", -1)
+    ops.set_option("force_split", 1)
+    got = run_fused(d, 2, w.eps)
+    assert_parity(d["q"], d["gamma_q"], got[0], w.eps, "split")
+    assert_parity(d["k"], d["gamma_k"], got[1], w.eps, "split")
+
+
+def test_bf16_output_rounds_to_nearest_even():
+    # y = x * gamma * r with gamma = 1 and a chosen r: 1 * (1 + 2^-8 + 2^-10)
+    # lies 0.625 ulp above 1.0 in bf16, so RNE gives 1 + 2^-7 (truncation: 1.0);
+    # 1 * (1 + 2^-8) is an exact tie between 1.0 (even) and 1 + 2^-7.
+    H = 64
+    x = to_dev(inputs.f32_to_bf16_bits(np.ones((2, H), np.float32)))
+    g = to_dev(inputs.f32_to_bf16_bits(np.ones(H, np.float32)))
+    r = torch.tensor([1 + 2 ** -8 + 2 ** -10, 1 + 2 ** -8], dtype=torch.float32, device="cuda:0")
+    y = to_host(ops.apply_scale(x, g, r))
+    assert np.all(y[0] == 0x3F81) and np.all(y[1] == 0x3F80)
+
+
+def test_graph_capture():
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    q, gq = to_dev(d["q"]), to_dev(d["gamma_q"])
+    k, gk = to_dev(d["k"]), to_dev(d["gamma_k"])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        # the fused path refuses capture
+        g = torch.cuda.CUDAGraph()
+        with pytest.raises(ops.QKNormError) as e:
+            with torch.cuda.graph(g, stream=s):
+                ops.layerwise_fwd(q, k, gq, gk, 4)
+        assert e.value.status == ops.QKN_ECAPTURE
+    # the split path is capturable; replays match eager, with eager work between them
+    p = torch.empty((4, w.T), dtype=torch.float32, device="cuda:0")
+    r = torch.empty((w.T,), dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(q)
+    ops.shard_sumsq(q, 4, p)
+    ops.combine_scale(p, w.Hq, w.eps, r)
+    ops.apply_scale(q, gq, r, y)
+    eager = y.clone()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        ops.shard_sumsq(q, 4, p)
+        ops.combine_scale(p, w.Hq, w.eps, r)
+        ops.apply_scale(q, gq, r, y)
+    for _ in range(3):
+        y.zero_()
+        p.zero_()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
+        ops.layerwise_fwd(q, k, gq, gk, 4)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_timeout_is_reported_and_recovers():
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    assert ops.check_fault() == ops.QKN_OK
+    ops.set_option("spin_limit_ns", 1_000_000)  # 1 ms
+    ops.set_option("test_skip_publish", 1)     # no partial is ever published
+    run_fused(d, 4, w.eps)
+    assert ops.check_fault() == ops.QKN_ETIMEOUT
+    assert ops.check_fault() == ops.QKN_OK  # cleared
+    ops.set_option("test_skip_publish", 0)
+    ops.set_option("spin_limit_ns", 1_000_000_000)
+    oq, ok = run_fused(d, 4, w.eps)
+    assert ops.check_fault() == ops.QKN_OK
+    assert_parity(d["q"], d["gamma_q"], oq, w.eps)
+
+
+def test_coresidency_query():
+    n = ops.max_coresident_workgroups("bf16", 5120, 5120, 2)
+    props = torch.cuda.get_device_properties(0)
+    assert n >= 2 and n % 1 == 0
+    assert n <= props.multi_processor_count * 32

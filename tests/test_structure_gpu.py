@@ -1,0 +1,124 @@
+"""Bit-exact partition checks and structural invariants of the HIP path (GPU).
+
+* Dyadic inputs (values m/8, |m| <= 16) make every square and every partial
+  sum exact in fp32, so the split path's partials must equal the oracle's
+  bitwise, and the fused path (same exact partials, same ascending combine,
+  same scaling) must equal the split path bitwise.
+* Column-coded inputs: token t is nonzero only in shard t % N. Exactly one
+  partial per token is nonzero, at shard t % N; the fused output is nonzero
+  exactly where the input is.
+* Determinism, independence of Q from K, token-permutation equivariance and
+  power-of-two scale invariance at eps = 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+from layerwise_qk_norm_amd import inputs, ops
+from oracle import oracle
+
+from _gpu import assert_parity, needs_gpu, run_split, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+SHAPES = [(64, 4096, 4096), (300, 5120, 5120), (129, 5120, 1024), (77, 1024, 1024)]
+
+
+def dyadic(T, H, dtype, seed):
+    rng = np.random.default_rng(seed)
+    a = (rng.integers(-16, 17, (T, H)) / 8.0).astype(np.float32)
+    return inputs.f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def gamma_of(H, dtype, seed=1):
+    g = np.random.default_rng(seed).uniform(0.5, 1.5, H)
+    return inputs.store(g, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+def test_split_partials_bitwise_on_dyadic_grid(dtype, N):
+    for T, Hq, _ in SHAPES:
+        x = dyadic(T, Hq, dtype, T)
+        p, _, _ = run_split(x, gamma_of(Hq, dtype), N, 1e-6)
+        pe = oracle.shard_sumsq(x, N)
+        assert np.array_equal(p.astype(np.float64), pe), (T, Hq, N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+def test_fused_equals_split_bitwise_on_dyadic_grid(dtype, N):
+    for T, Hq, Hk in SHAPES:
+        q, k = dyadic(T, Hq, dtype, 2 * T), dyadic(T, Hk, dtype, 2 * T + 1)
+        gq, gk = gamma_of(Hq, dtype, 3), gamma_of(Hk, dtype, 4)
+        oq, ok = ops.layerwise_fwd(to_dev(q), to_dev(k), to_dev(gq), to_dev(gk), N, 1e-6)
+        _, _, yq = run_split(q, gq, N, 1e-6)
+        _, _, yk = run_split(k, gk, N, 1e-6)
+        assert np.array_equal(to_host(oq), yq), (T, Hq, N)
+        assert np.array_equal(to_host(ok), yk), (T, Hk, N)
+        assert_parity(q, gq, to_host(oq), 1e-6)
+
+
+@pytest.mark.parametrize("N", [2, 4, 8])
+def test_column_coded_partition(N):
+    T, Hq, Hk = 96, 4096, 1024
+    rng = np.random.default_rng(N)
+    q = np.zeros((T, Hq), np.float32)
+    k = np.zeros((T, Hk), np.float32)
+    for t in range(T):
+        s = t % N
+        Wq, Wk = Hq // N, Hk // N
+        q[t, s * Wq:(s + 1) * Wq] = (1 + (np.arange(Wq) % 7)) / 8.0 * (1 + t % 3)
+        k[t, s * Wk:(s + 1) * Wk] = (1 + (np.arange(Wk) % 5)) / 4.0
+    for dtype in ("bf16", "f32"):
+        qd, kd = inputs.store(q.astype(np.float64), dtype), inputs.store(k.astype(np.float64), dtype)
+        p, _, _ = run_split(qd, gamma_of(Hq, dtype), N, 1e-6)
+        nz = p != 0
+        assert np.array_equal(nz, np.arange(N)[:, None] == (np.arange(T) % N)[None, :])
+        assert np.array_equal(p.astype(np.float64), oracle.shard_sumsq(qd, N))
+        gq, gk = gamma_of(Hq, dtype, 5), gamma_of(Hk, dtype, 6)
+        oq, ok = ops.layerwise_fwd(to_dev(qd), to_dev(kd), to_dev(gq), to_dev(gk), N, 1e-6)
+        oq, ok = to_host(oq), to_host(ok)
+        assert np.array_equal(oq != 0, q != 0)
+        assert np.array_equal(ok != 0, k != 0)
+        assert_parity(qd, gq, oq, 1e-6)
+        assert_parity(kd, gk, ok, 1e-6)
+
+
+def _dev(w):
+    d = inputs.make_host(w)
+    return [to_dev(d[n]) for n in ("q", "k", "gamma_q", "gamma_k")]
+
+
+@pytest.mark.parametrize("name", ["decode", "gqa"])
+def test_deterministic_and_q_independent_of_k(name):
+    w = inputs.CONFIGS[name].with_T(257)
+    q, k, gq, gk = _dev(w)
+    a = [to_host(t) for t in ops.layerwise_fwd(q, k, gq, gk, w.n_shards)]
+    b = [to_host(t) for t in ops.layerwise_fwd(q, k, gq, gk, w.n_shards)]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    k2 = k * 3 + 1
+    c = [to_host(t) for t in ops.layerwise_fwd(q, k2, gq, gk, w.n_shards)]
+    assert np.array_equal(a[0], c[0])
+    assert not np.array_equal(a[1], c[1])
+
+
+def test_token_permutation_equivariance():
+    w = inputs.PREFILL.with_T(500)
+    q, k, gq, gk = _dev(w)
+    perm = torch.randperm(500, generator=torch.Generator().manual_seed(0)).to("cuda:0")
+    oq, ok = ops.layerwise_fwd(q, k, gq, gk, w.n_shards)
+    pq, pk = ops.layerwise_fwd(q[perm].contiguous(), k[perm].contiguous(), gq, gk, w.n_shards)
+    # one token per tile for this shape, so each row's arithmetic is the same
+    assert ops.current_plan("bf16", 500, 5120, 5120, 2)["rows"] == 1
+    assert torch.equal(oq[perm], pq) and torch.equal(ok[perm], pk)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_power_of_two_scale_invariance_at_eps_zero(dtype):
+    w = inputs.Workload("s", 200, 2048, 1024, 4, dtype)
+    q, k, gq, gk = _dev(w)
+    a = [to_host(t) for t in ops.layerwise_fwd(q, k, gq, gk, 4, 0.0)]
+    for m in (-3, 5):
+        b = [to_host(t) for t in ops.layerwise_fwd(q * 2.0 ** m, k * 2.0 ** m, gq, gk, 4, 0.0)]
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -134,9 +134,10 @@ const char* qknorm_last_hip_error(void);
 int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_shards,
                                      int* out);
 
-/* Occupancy of the current device: blocks_per_cu[v] = workgroups of fused
- * variant v one compute unit can hold (0 = variant unusable for dtype), for
- * QKN_NUM_VARIANTS variants; *cu_count = compute units. Feeds
+/* Occupancy of the current device: blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1)
+ * + w] = workgroups of fused variant v with w data waves that one compute
+ * unit can hold (0 = not launchable), an array of QKN_NUM_VARIANTS x
+ * (QKN_MAX_DATA_WAVES + 1) ints; *cu_count = compute units. Feeds
  * qknorm_plan_fused with the numbers the library itself plans with. */
 int qknorm_device_occupancy(int dtype, int* blocks_per_cu, int* cu_count);
 
@@ -146,13 +147,17 @@ int qknorm_release_workspace(void);
 
 /* Host-only launch planning, exposed for tests and tools. Fills *plan for a
  * device with `cu_count` compute units, of which each holds
- * `blocks_per_cu[v]` workgroups of kernel variant v (an array of
- * QKN_NUM_VARIANTS entries; the real path queries the occupancy API). */
-#define QKN_NUM_VARIANTS 5
+ * `blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1) + w]` workgroups of kernel
+ * variant v with w data waves (the layout of qknorm_device_occupancy; the
+ * real path queries the occupancy API). Variant v holds a fixed number of
+ * 16-byte vectors per data thread (1, 2, 3, 4, 6, 9; the last fp32 only). */
+#define QKN_NUM_VARIANTS 6
+#define QKN_MAX_DATA_WAVES 15
 typedef struct qknorm_plan {
     int variant;        /* fused kernel variant, or -1: shape uses the split kernels */
-    int threads;        /* workgroup size */
-    int slots;          /* 16-byte vectors per thread */
+    int threads;        /* workgroup size: 64 x (data_waves + 1) */
+    int data_waves;     /* data waves per workgroup (one more wave exchanges) */
+    int slots;          /* 16-byte vectors per data thread */
     int rows;           /* tokens per tile */
     int64_t n_tiles;    /* ceil(T / rows) */
     int n_groups;       /* workgroup groups; each group = n_shards workgroups */
@@ -169,11 +174,12 @@ int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards
 enum {
     QKN_OPT_SPIN_LIMIT_NS = 1,  /* exchange spin budget in ns (default 1e9) */
     QKN_OPT_FORCE_VARIANT = 2,  /* -1 = planner's choice, else a variant id */
-    QKN_OPT_ROWS = 3,           /* 0 = planner's choice, else rows per tile */
+    QKN_OPT_ROWS = 3,           /* 0 = planner's choice, else rows per tile (<= 4) */
     QKN_OPT_XCD_MAP = 4,        /* -1 = auto, 0 = off, 1 = on when possible */
     QKN_OPT_COOPERATIVE = 5,    /* 1 = hipLaunchCooperativeKernel, 0 = plain */
     QKN_OPT_MAX_GROUPS = 6,     /* 0 = no cap, else cap on workgroup groups */
     QKN_OPT_FORCE_SPLIT = 7,    /* 1 = fused entry points run the split kernels */
+    QKN_OPT_DATA_WAVES = 9,     /* 0 = planner's choice, else data waves per workgroup */
     QKN_OPT_TEST_SKIP_PUBLISH = 8 /* test hook: 1 = fused workgroups never publish
                                      their partial, so every exchange with n_shards
                                      > 1 ends at the spin limit (kernel still exits) */

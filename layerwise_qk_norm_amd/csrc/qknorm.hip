@@ -29,19 +29,20 @@ using qkn::FusedParams;
 // ---------------------------------------------------------------- variants
 
 struct Variant {
-    int nwd;        // data waves (plus one comm wave)
-    int vpt;        // 16-byte slots per data thread
-    int rmax;       // max tokens per tile
-    bool prefetch;  // next tile loaded during the exchange
-    bool f32_only;  // register budget only fits fp32 (u can overwrite x in place)
+    int vpt;          // 16-byte slots per data thread
+    bool prefetch;    // next tile loaded during the exchange
+    bool f32_only;    // register budget only fits fp32 (no prefetch buffer)
+    int max_threads;  // launch bound of the instantiation
 };
 constexpr Variant kVariants[QKN_NUM_VARIANTS] = {
-    {4, 2, 4, true, false},    //  512 slots
-    {4, 4, 2, true, false},    // 1024 slots
-    {8, 4, 1, true, false},    // 2048 slots
-    {11, 6, 1, true, false},   // 4224 slots
-    {15, 9, 1, false, true},   // 8640 slots
+    {1, true, false, 1024},
+    {2, true, false, 1024},
+    {3, true, false, 1024},
+    {4, true, false, 1024},
+    {6, true, false, 768},
+    {9, false, true, 1024},
 };
+int max_data_waves(int v) { return kVariants[v].max_threads / 64 - 1; }
 
 using FusedFn = void (*)(FusedParams);
 
@@ -49,10 +50,11 @@ template <class DT>
 FusedFn fused_fn(int v)
 {
     switch (v) {
-    case 0: return qkn::fused_qknorm_kernel<DT, 4, 2, 4, true>;
-    case 1: return qkn::fused_qknorm_kernel<DT, 4, 4, 2, true>;
-    case 2: return qkn::fused_qknorm_kernel<DT, 8, 4, 1, true>;
-    case 3: return qkn::fused_qknorm_kernel<DT, 11, 6, 1, true>;
+    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1024>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1024>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1024>;
+    case 3: return qkn::fused_qknorm_kernel<DT, 4, true, 1024>;
+    case 4: return qkn::fused_qknorm_kernel<DT, 6, true, 768>;
     default: return nullptr;
     }
 }
@@ -60,23 +62,26 @@ template <>
 FusedFn fused_fn<F32>(int v)
 {
     switch (v) {
-    case 0: return qkn::fused_qknorm_kernel<F32, 4, 2, 4, true>;
-    case 1: return qkn::fused_qknorm_kernel<F32, 4, 4, 2, true>;
-    case 2: return qkn::fused_qknorm_kernel<F32, 8, 4, 1, true>;
-    case 3: return qkn::fused_qknorm_kernel<F32, 11, 6, 1, true>;
-    case 4: return qkn::fused_qknorm_kernel<F32, 15, 9, 1, false>;
+    case 0: return qkn::fused_qknorm_kernel<F32, 1, true, 1024>;
+    case 1: return qkn::fused_qknorm_kernel<F32, 2, true, 1024>;
+    case 2: return qkn::fused_qknorm_kernel<F32, 3, true, 1024>;
+    case 3: return qkn::fused_qknorm_kernel<F32, 4, true, 1024>;
+    case 4: return qkn::fused_qknorm_kernel<F32, 6, true, 768>;
+    case 5: return qkn::fused_qknorm_kernel<F32, 9, false, 1024>;
     default: return nullptr;
     }
 }
 FusedFn fused_fn_for(int dtype, int v) { return dtype == QKN_BF16 ? fused_fn<Bf16>(v) : fused_fn<F32>(v); }
 
-int threads_of(int v) { return 64 * (kVariants[v].nwd + 1); }
+// dynamic LDS of a launch: gamma in slot order
+size_t gamma_lds_bytes(int v, int nwd) { return (size_t)kVariants[v].vpt * 64 * nwd * 16; }
 
 // ---------------------------------------------------------------- options
 
 struct Options {
     int64_t spin_ns = 1000000000;
     int64_t force_variant = -1;
+    int64_t force_data_waves = 0;
     int64_t rows = 0;
     int64_t xcd_map = -1;
     int64_t cooperative = 0;
@@ -107,7 +112,7 @@ struct DevInfo {
     int cu = 0;
     int wall_khz = 0;
     bool occ_done[2] = {false, false};
-    int occ[2][QKN_NUM_VARIANTS] = {};
+    int occ[2][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
 };
 
 std::mutex g_mu;
@@ -124,12 +129,21 @@ int device_info(int dev, int dtype, DevInfo** out)
     if (!d.occ_done[dtype]) {
         for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
             FusedFn fn = fused_fn_for(dtype, v);
-            int n = 0;
-            if (fn && !(kVariants[v].f32_only && dtype != QKN_F32)) {
-                QKN_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, reinterpret_cast<const void*>(fn), threads_of(v), 0));
+            const bool usable = fn && !(kVariants[v].f32_only && dtype != QKN_F32);
+            if (usable) {
+                const size_t max_lds = gamma_lds_bytes(v, max_data_waves(v));
+                QKN_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            (int)max_lds));
             }
-            d.occ[dtype][v] = n;
+            for (int w = 0; w <= QKN_MAX_DATA_WAVES; ++w) {
+                int n = 0;
+                if (usable && w >= 1 && w <= max_data_waves(v)) {
+                    QKN_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &n, reinterpret_cast<const void*>(fn), 64 * (w + 1), gamma_lds_bytes(v, w)));
+                }
+                d.occ[dtype][v][w] = n;
+            }
         }
         d.occ_done[dtype] = true;
     }
@@ -233,6 +247,8 @@ int current_device(int* dev)
 
 // ---------------------------------------------------------------- planning
 
+// bpc[v * (QKN_MAX_DATA_WAVES + 1) + w]: co-resident workgroups per CU of
+// variant v with w data waves (0 = not launchable).
 int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int* bpc,
          int aligned, qknorm_plan* out)
 {
@@ -244,35 +260,81 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     rc = check_dims(T, Hk, N);
     if (rc) return rc;
     if (cu < 1 || !bpc) return QKN_EINVAL;
-    const int ev = 16 / elem_size(dtype);
+    if (T == 0) return QKN_OK;
+    const int es = elem_size(dtype);
+    const int ev = 16 / es;
     const int64_t Wq = Hq / N, Wk = Hk / N;
     if (!aligned || Wq % ev || Wk % ev || g_opt.force_split) return QKN_OK;  // split kernels
-    const int64_t vrow = (Wq + Wk) / ev;
-    int v = -1;
-    for (int c = 0; c < QKN_NUM_VARIANTS; ++c) {
-        if (g_opt.force_variant >= 0 && c != g_opt.force_variant) continue;
-        const Variant& k = kVariants[c];
+    const int64_t wvq = Wq / ev, wvk = Wk / ev;
+    // vectors a tile of r rows occupies: Q's part padded to whole waves, then K's
+    auto tile_vectors = [&](int64_t r) { return ((r * wvq + 63) / 64) * 64 + r * wvk; };
+
+    // Candidates (variant, data waves, rows). The tile must fit the data
+    // threads' slots, and 2 * rows * N comm lanes must fit one wave. Among
+    // those the planner maximises the load bytes in flight per CU (workgroups
+    // per CU x tile bytes) -- the quantity that sets a streaming kernel's
+    // bandwidth. Within 2 % of that it prefers more workgroups (parallelism,
+    // which decides small batches), then fuller slots, then smaller workgroups.
+    struct Best {
+        int v = -1, w = 0, rows = 0;
+        double inflight = -1, util = 0;
+        int64_t cap = 0, wgs = 0;
+    } best;
+    const int rows_cap = (int)std::min<int64_t>({(int64_t)qkn::kMaxRows, 32 / N, T});
+    for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
+        if (g_opt.force_variant >= 0 && v != g_opt.force_variant) continue;
+        const Variant& k = kVariants[v];
         if (k.f32_only && dtype != QKN_F32) continue;
-        if ((int64_t)64 * k.nwd * k.vpt < vrow) continue;
-        if (N * 2 * k.rmax > 64) continue;
-        if (bpc[c] <= 0) continue;
-        v = c;
-        break;
+        for (int r = 1; r <= rows_cap; ++r) {
+            if (g_opt.rows > 0 && r != g_opt.rows) continue;
+            const int64_t tv = tile_vectors(r);
+            int w = (int)((tv + 64 * k.vpt - 1) / (64 * k.vpt));
+            if (g_opt.force_data_waves > 0) {
+                if (g_opt.force_data_waves < w) continue;
+                w = (int)g_opt.force_data_waves;
+            }
+            if (w < 1 || w > max_data_waves(v)) continue;
+            const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
+            if (b <= 0) continue;
+            const int64_t cap = (int64_t)b * cu;
+            if (cap < N) continue;
+            const int64_t tiles = (T + r - 1) / r;
+            const int64_t wgs = std::min<int64_t>(tiles, cap / N) * N;
+            // bytes of loads in flight per CU, never more than the batch holds
+            const double batch = (double)T * (double)(wvq + wvk) * 16.0 * N;
+            const double inflight = std::min((double)wgs * (double)(tv * 16), batch) / cu;
+            const double util = (double)tv / (double)(64 * w * k.vpt);
+            bool better;
+            if (inflight > best.inflight * 1.02) {
+                better = true;
+            } else if (inflight < best.inflight * 0.98) {
+                better = false;
+            } else if (wgs != best.wgs) {
+                better = wgs > best.wgs;
+            } else if (util > best.util + 1e-9 || util < best.util - 1e-9) {
+                better = util > best.util;
+            } else {
+                better = w < best.w;
+            }
+            if (better) best = {v, w, r, inflight, util, cap, wgs};
+        }
     }
-    if (v < 0) return QKN_OK;  // no fused variant fits: split kernels
-    const Variant& k = kVariants[v];
-    const int64_t cap = (int64_t)bpc[v] * cu;
-    if (cap < N) return QKN_ERESIDENCY;
-    const int64_t slots = (int64_t)64 * k.nwd * k.vpt;
-    int rows = (int)std::min<int64_t>(k.rmax, slots / vrow);
-    if (g_opt.rows > 0) {
-        rows = (int)std::min<int64_t>(rows, g_opt.rows);
-    } else {
-        // fewer rows per tile while that still leaves the grid short of capacity
-        while (rows > 1 && ((T + rows - 1) / rows) * N < cap) --rows;
+    if (best.v < 0) {
+        // nothing fits: residency failure if some variant would fit the shape
+        // but not N co-resident workgroups; otherwise the split kernels
+        for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
+            const Variant& k = kVariants[v];
+            if (k.f32_only && dtype != QKN_F32) continue;
+            const int w = (int)((tile_vectors(1) + 64 * k.vpt - 1) / (64 * k.vpt));
+            if (w >= 1 && w <= max_data_waves(v) && bpc[v * (QKN_MAX_DATA_WAVES + 1) + w] > 0 &&
+                (int64_t)bpc[v * (QKN_MAX_DATA_WAVES + 1) + w] * cu < N)
+                return QKN_ERESIDENCY;
+        }
+        return QKN_OK;
     }
+    const int rows = best.rows;
     const int64_t n_tiles = (T + rows - 1) / rows;
-    int64_t groups = std::min<int64_t>(n_tiles, cap / N);
+    int64_t groups = std::min<int64_t>(n_tiles, best.cap / N);
     if (g_opt.max_groups > 0) groups = std::min<int64_t>(groups, g_opt.max_groups);
     int xcd = 0;
     if (g_opt.xcd_map != 0 && groups >= 8) {
@@ -280,9 +342,10 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         xcd = (groups % 8 == 0) ? 1 : 0;
     }
     if (groups < 1) groups = 1;
-    out->variant = v;
-    out->threads = threads_of(v);
-    out->slots = k.vpt;
+    out->variant = best.v;
+    out->threads = 64 * (best.w + 1);
+    out->data_waves = best.w;
+    out->slots = kVariants[best.v].vpt;
     out->rows = rows;
     out->n_tiles = n_tiles;
     out->n_groups = (int)groups;
@@ -384,7 +447,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     const int aligned = aligned16(q) && aligned16(k) && aligned16(gq) && aligned16(gk) &&
                         aligned16(oq) && aligned16(ok);
     qknorm_plan pl;
-    if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, di->occ[dtype], aligned, &pl))) return rc;
+    if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, &di->occ[dtype][0][0], aligned, &pl))) return rc;
 
     if (pl.variant < 0) {
         // Shapes the fused kernel cannot hold in registers (or unaligned): the
@@ -405,8 +468,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
         return QKN_OK;
     }
 
-    const Variant& var = kVariants[pl.variant];
-    const size_t entries = (size_t)pl.n_groups * 2 * N * 2 * var.rmax;
+    const size_t entries = (size_t)pl.n_groups * 2 * N * 2 * pl.rows;
     if ((rc = ensure_slots(ws, entries, stream))) return rc;
     if ((uint64_t)ws->tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
         // tags would wrap: clear every slot so no stale tag can match
@@ -430,6 +492,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     p.Wv[0] = (int32_t)(Hq / N / ev);
     p.Wv[1] = (int32_t)(Hk / N / ev);
     p.rows = pl.rows;
+    p.nwd = pl.data_waves;
     p.n_shards = N;
     p.n_groups = pl.n_groups;
     p.xcd_map = pl.xcd_map;
@@ -443,12 +506,13 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     ws->tag_base += (uint32_t)pl.iters;
 
     FusedFn fn = fused_fn_for(dtype, pl.variant);
+    const size_t lds = gamma_lds_bytes(pl.variant, pl.data_waves);
     if (g_opt.cooperative) {
         void* args[] = {&p};
         QKN_HIP(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(pl.grid),
-                                           dim3(pl.threads), args, 0, stream));
+                                           dim3(pl.threads), args, (unsigned)lds, stream));
     } else {
-        hipLaunchKernelGGL(fn, dim3(pl.grid), dim3(pl.threads), 0, stream, p);
+        hipLaunchKernelGGL(fn, dim3(pl.grid), dim3(pl.threads), (unsigned)lds, stream, p);
         QKN_HIP(hipGetLastError());
     }
     return QKN_OK;
@@ -590,8 +654,8 @@ int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_sh
     DevInfo* di = nullptr;
     if ((rc = device_info(dev, dtype, &di))) return rc;
     qknorm_plan pl;
-    if ((rc = plan(dtype, 1, Hq, Hk, n_shards, di->cu, di->occ[dtype], 1, &pl))) return rc;
-    *out = pl.variant < 0 ? 0 : di->occ[dtype][pl.variant] * di->cu;
+    if ((rc = plan(dtype, 1 << 20, Hq, Hk, n_shards, di->cu, &di->occ[dtype][0][0], 1, &pl))) return rc;
+    *out = pl.variant < 0 ? 0 : di->occ[dtype][pl.variant][pl.data_waves] * di->cu;
     return QKN_OK;
 }
 
@@ -604,7 +668,9 @@ int qknorm_device_occupancy(int dtype, int* blocks_per_cu, int* cu_count)
     if (rc) return rc;
     DevInfo* di = nullptr;
     if ((rc = device_info(dev, dtype, &di))) return rc;
-    for (int v = 0; v < QKN_NUM_VARIANTS; ++v) blocks_per_cu[v] = di->occ[dtype][v];
+    for (int v = 0; v < QKN_NUM_VARIANTS; ++v)
+        for (int w = 0; w <= QKN_MAX_DATA_WAVES; ++w)
+            blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1) + w] = di->occ[dtype][v][w];
     *cu_count = di->cu;
     return QKN_OK;
 }
@@ -640,7 +706,12 @@ int qknorm_set_option(int key, int64_t value)
     case QKN_OPT_FORCE_VARIANT:
         if (value < -1 || value >= QKN_NUM_VARIANTS) return QKN_EINVAL;
         g_opt.force_variant = value; return QKN_OK;
-    case QKN_OPT_ROWS: if (value < 0) return QKN_EINVAL; g_opt.rows = value; return QKN_OK;
+    case QKN_OPT_ROWS:
+        if (value < 0 || value > qkn::kMaxRows) return QKN_EINVAL;
+        g_opt.rows = value; return QKN_OK;
+    case QKN_OPT_DATA_WAVES:
+        if (value < 0 || value > QKN_MAX_DATA_WAVES) return QKN_EINVAL;
+        g_opt.force_data_waves = value; return QKN_OK;
     case QKN_OPT_XCD_MAP: if (value < -1 || value > 1) return QKN_EINVAL; g_opt.xcd_map = value; return QKN_OK;
     case QKN_OPT_COOPERATIVE: g_opt.cooperative = value ? 1 : 0; return QKN_OK;
     case QKN_OPT_MAX_GROUPS: if (value < 0) return QKN_EINVAL; g_opt.max_groups = value; return QKN_OK;
@@ -656,6 +727,7 @@ int64_t qknorm_get_option(int key)
     case QKN_OPT_SPIN_LIMIT_NS: return g_opt.spin_ns;
     case QKN_OPT_FORCE_VARIANT: return g_opt.force_variant;
     case QKN_OPT_ROWS: return g_opt.rows;
+    case QKN_OPT_DATA_WAVES: return g_opt.force_data_waves;
     case QKN_OPT_XCD_MAP: return g_opt.xcd_map;
     case QKN_OPT_COOPERATIVE: return g_opt.cooperative;
     case QKN_OPT_MAX_GROUPS: return g_opt.max_groups;
@@ -677,7 +749,9 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k, in
     int dev = 0, cu = 0, rc = current_device(&dev);
     if (rc) return rc;
     QKN_HIP(hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev));
-    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((va + vb + 255) / 256, (int64_t)cu * 16));
+    const int64_t blocks = std::max<int64_t>(1, (va + vb + 255) / 256);
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    (void)cu;
     hipLaunchKernelGGL(qkn::copy2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, k, out_q,
                        out_k, va, vb, bytes_q - va * 16, bytes_k - vb * 16);
     QKN_HIP(hipGetLastError());

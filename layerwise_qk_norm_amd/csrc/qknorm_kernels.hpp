@@ -91,6 +91,18 @@ __device__ __forceinline__ u32x4 ld_cached(const void* p)
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Cache policy bits of buffer instructions on gfx950: nontemporal.
+constexpr int kNT = 2;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 left at 7, lgkmcnt 11:8 left at 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Exchange slots: {tag (high 32 bits), fp32 partial (low 32 bits)} written and
 // read as one 64-bit agent-scope atomic, so value and readiness arrive together
 // and no separate fence is needed.
@@ -129,6 +141,10 @@ __device__ __forceinline__ float wave_sum(float v)
 
 // ================================================================ fused kernel
 
+constexpr int kMaxDataWaves = 15;  // data waves per workgroup (plus one comm wave)
+constexpr int kMaxRows = 4;        // tokens per tile
+constexpr int kMaxSeg = 2 * kMaxRows;
+
 struct FusedParams {
     const void* x[2];      // q, k            [T][H[i]]
     const void* gamma[2];  // gamma_q, gamma_k [H[i]]
@@ -137,35 +153,47 @@ struct FusedParams {
     int64_t n_tiles;
     int32_t H[2];          // full widths (the RMS divisor)
     int32_t Wv[2];         // shard width in 16-byte vectors
-    int32_t rows;          // tokens per tile
+    int32_t rows;          // tokens per tile (1..kMaxRows), 2*rows*n_shards <= 64
+    int32_t nwd;           // data waves per workgroup (1..kMaxDataWaves)
     int32_t n_shards;
     int32_t n_groups;
     int32_t xcd_map;
     float eps;
-    uint32_t tag_base;     // tag of this call's first tile; tile i of a group uses tag_base + i
-    unsigned long long* slots;  // [n_groups][2][n_shards][2*RMAX]
+    uint32_t tag_base;     // tag of a group's first tile; its tile k uses tag_base + k
+    unsigned long long* slots;  // [n_groups][2][n_shards][2*rows]
     uint32_t* fault;
     uint64_t spin_ticks;   // wall-clock ticks a comm wave may wait for one tile
     uint32_t test_flags;   // bit 0: never publish (forces the timeout path)
 };
 
-// Workgroup = 1 comm wave (wave 0) + NWD data waves. Every workgroup owns one
-// logical shard and one group; a group is the n_shards workgroups that
+// Workgroup = 1 comm wave (wave 0) + p.nwd data waves. Every workgroup owns
+// one logical shard and one group; a group is the n_shards workgroups that
 // together cover a token tile (rows tokens x all columns of Q and of K).
-// Data slots: a tile's Q part (rows x Wv[0] vectors) followed by its K part
-// (rows x Wv[1] vectors), dealt to data threads round-robin, VPT per thread.
-// The slot layout is the same for every tile, so gamma is loaded once.
-template <class DT, int NWD, int VPT, int RMAX, bool PREFETCH>
-__global__ void __launch_bounds__(64 * (NWD + 1))
+// Data slots: a tile's Q part (rows x Wv[0] vectors, padded to whole waves)
+// followed by its K part (rows x Wv[1] vectors), dealt to the data threads
+// round-robin, VPT per thread. The slot layout is the same for every tile, so
+// gamma is staged once, in slot order, in LDS (dynamic shared memory of
+// VPT * 64 * nwd * 16 bytes).
+//
+// Pipeline: a group's tiles k = 0..K-1 go through one barrier per iteration.
+// In iteration k the data waves issue the loads of tile k+1, reduce tile k
+// (Phase A), pass the barrier, scale and store tile k-1 (Phase C), and form
+// u = x*gamma of tile k (Phase B compute path). The comm wave, before the
+// barrier, acquires the peers' partials of tile k-1 (published one iteration
+// earlier) and combines them; after it, it publishes its own partial of tile
+// k. Partners are thereby coupled one iteration apart, and the exchange
+// overlaps both the load of the next tile and the product x*gamma. red and
+// rinv_s are double-buffered by tile parity.
+template <class DT, int VPT, bool PREFETCH, int MAXT>
+__global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
     using elem_t = typename DT::elem_t;
     constexpr int EV = DT::kVec;
-    constexpr int NSEG = 2 * RMAX;  // segments: (tensor, row) pairs of a tile
-    constexpr int NDT = 64 * NWD;   // data threads
 
-    __shared__ float red[NWD][NSEG];  // per-wave partial sums of squares
-    __shared__ float rinv_s[NSEG];    // combined reciprocal RMS per segment
+    __shared__ float red[2][kMaxDataWaves][kMaxSeg];  // per-wave partial sums, by tile parity
+    __shared__ float rinv_s[2][kMaxSeg];              // combined reciprocal RMS, by tile parity
+    extern __shared__ u32x4 gam_lds[];                // gamma in slot order
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -174,11 +202,13 @@ fused_qknorm_kernel(FusedParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = p.n_shards;
     const int rows = p.rows;
+    const int nseg = 2 * rows;  // segments of a tile: (tensor, row) pairs
+    const int nwd = p.nwd;
 
     // ---- decomposition (which shard, which group) -------------------------
     // With xcd_map, workgroups b and b' belong to one group only if
     // b % 8 == b' % 8: consecutive workgroup ids are dispatched round-robin to
-    // the 8 XCDs, so a group's exchange stays inside one XCD's L2.
+    // the 8 XCDs, so a group's members share one XCD.
     int shard, group;
     {
         const int b = blockIdx.x;
@@ -191,180 +221,222 @@ fused_qknorm_kernel(FusedParams p)
             group = b / N;
         }
     }
+    // tiles of this group: group, group + n_groups, ... (K of them; the same
+    // count for every member of the group)
+    const int K = p.n_tiles > group ? (int)((p.n_tiles - 1 - group) / p.n_groups + 1) : 0;
+    if (K == 0) return;
 
     if (wave == 0) {
-        // ================= comm wave: publish, acquire, combine =============
-        const int kk = lane / NSEG;          // shard of the slot this lane watches
-        const int sg = lane % NSEG;          // segment of that slot
-        const bool seg_used = (sg % RMAX) < rows;
-        const bool mine = seg_used && kk == shard && lane < N * NSEG;
-        const bool peer = seg_used && kk != shard && lane < N * NSEG;
-        const float Hf = (float)(sg < RMAX ? p.H[0] : p.H[1]);
+        // ================= comm wave: acquire, combine, publish =============
+        const int kk = lane / nseg;  // shard of the slot this lane watches
+        const int sg = lane - kk * nseg;  // segment of that slot
+        const bool active = lane < N * nseg;
+        const bool mine = active && kk == shard;
+        const bool peer = active && kk != shard;
+        const float Hf = (float)(sg < rows ? p.H[0] : p.H[1]);
         bool abandon = false;
-        int it = 0;
-        for (int64_t tile = group; tile < p.n_tiles; tile += p.n_groups, ++it) {
-            __syncthreads();  // B1: data waves have written red[][]
-            unsigned long long* slot =
-                p.slots + ((size_t)(group * 2 + (it & 1)) * N) * NSEG + lane;
-            const uint32_t want = p.tag_base + (uint32_t)it;
-            float v = 0.f;
-            if (mine) {
-                float own = 0.f;
-#pragma unroll
-                for (int w = 0; w < NWD; ++w) own += red[w][sg];
-                v = own;
-                if (N > 1 && !(p.test_flags & 1u)) slot_publish(slot, want, own);
-            }
-            bool need = peer;
-            if (N > 1 && !abandon) {
-                const uint64_t t0 = wall_clock64();
-                while (__any(need)) {
-                    if (need) {
-                        const unsigned long long w = slot_read(slot);
-                        if ((uint32_t)(w >> 32) == want) {
-                            v = __uint_as_float((uint32_t)w);
-                            need = false;
+        float own_prev = 0.f;
+        for (int k = 0; k <= K; ++k) {
+            if (k >= 1) {
+                // ---- Phase B comm path for tile k-1 ----------------------------
+                const int j = k - 1;
+                const unsigned long long* slot =
+                    p.slots + ((size_t)(group * 2 + (j & 1)) * N) * nseg + lane;
+                const uint32_t want = p.tag_base + (uint32_t)j;
+                float v = mine ? own_prev : 0.f;
+                bool need = peer && !abandon;
+                if (__any(need)) {
+                    const uint64_t t0 = wall_clock64();
+                    while (true) {
+                        if (need) {
+                            const unsigned long long w = slot_read(slot);
+                            if ((uint32_t)(w >> 32) == want) {
+                                v = __uint_as_float((uint32_t)w);
+                                need = false;
+                            }
                         }
+                        if (!__any(need)) break;
+                        if (wall_clock64() - t0 > p.spin_ticks) {
+                            if (lane == 0) atomicOr(p.fault, 1u);
+                            abandon = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
                     }
-                    if (!__any(need)) break;
-                    if (wall_clock64() - t0 > p.spin_ticks) {
-                        if (lane == 0) atomicOr(p.fault, 1u);
-                        abandon = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
+                }
+                // S = sum over shards 0..N-1 in ascending order (same on every shard)
+                float S = 0.f;
+                for (int k2 = 0; k2 < N; ++k2) S += __shfl(v, k2 * nseg + sg);
+                if (lane < nseg) rinv_s[j & 1][lane] = 1.0f / sqrtf(S / Hf + p.eps);
+            }
+            __syncthreads();  // red[k&1] written; rinv_s[(k-1)&1] ready
+            if (k < K && mine) {
+                // ---- publish the partial of tile k (after acquiring tile k-1,
+                // so a two-deep slot ring never overwrites an unread value)
+                float own = 0.f;
+                for (int w = 0; w < nwd; ++w) own += red[k & 1][w][sg];
+                own_prev = own;
+                if (N > 1 && !(p.test_flags & 1u)) {
+                    unsigned long long* slot =
+                        p.slots + ((size_t)(group * 2 + (k & 1)) * N) * nseg + lane;
+                    slot_publish(slot, p.tag_base + (uint32_t)k, own);
                 }
             }
-            // S = sum over shards k = 0..N-1 in ascending order (same on every shard)
-            float S = 0.f;
-            for (int k2 = 0; k2 < N; ++k2) S += __shfl(v, k2 * NSEG + sg);
-            if (lane < NSEG && seg_used) rinv_s[lane] = 1.0f / sqrtf(S / Hf + p.eps);
-            __syncthreads();  // B2: rinv_s ready
         }
         return;
     }
 
     // ===================== data waves ========================================
-    const int dt = tid - 64;  // data thread index
+    // Memory access goes through per-tile buffer descriptors: a lane whose slot
+    // is unused, or whose row lies past T, carries an offset beyond the
+    // descriptor's range, so its load returns 0 and its store is dropped by the
+    // hardware. Every load and store is therefore unconditional, which keeps
+    // vmcnt accounting exact: the prefetched tile can be consumed while the
+    // previous tile's stores are still in flight.
     const int dwave = wave - 1;
-    const int V0 = rows * p.Wv[0];
-    const int V = V0 + rows * p.Wv[1];
+    const int ndt = 64 * nwd;  // data threads
+    const int dt = tid - 64;
+    const int VQ = rows * p.Wv[0];
+    const int VQp = (VQ + 63) & ~63;  // K starts on a wave boundary
+    const int V = VQp + rows * p.Wv[1];
+    constexpr uint32_t kOOB = 0x7ffffff0u;
+    constexpr int ES = (int)sizeof(elem_t);
 
-    // Static per-slot layout: element offset from the tile's first row, tensor,
-    // segment, validity. gamma for the slot's columns is held in registers.
-    int32_t off[VPT];
-    int meta[VPT];  // bits 0..7 segment, bit 8 tensor 1, bit 9 valid
-    u32x4 gam[VPT];
+    // Static per-slot layout (identical for every tile). tensor is uniform per
+    // (wave, slot) because Q's part is padded to whole waves.
+    uint32_t voff[VPT];  // byte offset from the tile's first row, or kOOB
+    int seg[VPT];        // segment: tensor * rows + row
+    bool tk[VPT];        // slot belongs to K (wave-uniform)
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-        const int v = dt + i * NDT;
-        int t = 0, r = 0, c = 0;
-        if (v < V0) {
+        const int vbase = i * ndt + dwave * 64;
+        const int v = vbase + lane;
+        const int t = vbase >= VQp ? 1 : 0;
+        int r, c;
+        bool valid;
+        if (t == 0) {
+            valid = v < VQ;
             r = v / p.Wv[0];
             c = v - r * p.Wv[0];
         } else {
-            t = 1;
-            r = (v - V0) / p.Wv[1];
-            c = (v - V0) - r * p.Wv[1];
+            valid = v < V;
+            const int u = v - VQp;
+            r = u / p.Wv[1];
+            c = u - r * p.Wv[1];
         }
-        const int col = (shard * p.Wv[t] + c) * EV;  // element column inside the row
-        off[i] = r * p.H[t] + col;
-        const bool valid = v < V;
-        meta[i] = (t * RMAX + r) | (t << 8) | ((valid ? 1 : 0) << 9);
-        gam[i] = valid ? ld_cached(static_cast<const elem_t*>(p.gamma[t]) + col) : u32x4{0, 0, 0, 0};
+        const int col = (shard * p.Wv[t] + c) * EV;
+        tk[i] = t != 0;
+        voff[i] = valid ? (uint32_t)((r * p.H[t] + col) * ES) : kOOB;
+        seg[i] = valid ? t * rows + r : 0;
+        gam_lds[i * ndt + dt] =
+            valid ? ld_cached(static_cast<const elem_t*>(p.gamma[t]) + col) : u32x4{0, 0, 0, 0};
     }
 
-    const elem_t* x0 = static_cast<const elem_t*>(p.x[0]);
-    const elem_t* x1 = static_cast<const elem_t*>(p.x[1]);
-    elem_t* y0 = static_cast<elem_t*>(p.y[0]);
-    elem_t* y1 = static_cast<elem_t*>(p.y[1]);
-
-    auto live = [&](int i, int64_t t0) {
-        return (meta[i] & 512) && (t0 + ((meta[i] & 255) % RMAX) < p.T);
+    auto tile_of = [&](int k) -> int64_t { return group + (int64_t)k * p.n_groups; };
+    auto rsrc = [&](const void* base, int t, int64_t t0) {
+        // rows of this tile that exist; 0 past the end (then every access is out of range)
+        const int64_t left = p.T - t0;
+        const int vr = left <= 0 ? 0 : (left < rows ? (int)left : rows);
+        const char* b = static_cast<const char*>(base) + t0 * p.H[t] * ES;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, vr * p.H[t] * ES,
+                                                 0x00020000);
     };
     auto load_tile = [&](int64_t tile, u32x4 (&buf)[VPT]) {
         const int64_t t0 = tile * rows;
-        const elem_t* b0 = x0 + t0 * p.H[0];
-        const elem_t* b1 = x1 + t0 * p.H[1];
+        const __amdgpu_buffer_rsrc_t rq = rsrc(p.x[0], 0, t0);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(p.x[1], 1, t0);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(tk[i] ? rk : rq, voff[i], 0, kNT);
+    };
+    // ---- Phase A: local sums of squares (fp32) of the tile in buf -> red[par]
+    auto phase_a = [&](const u32x4 (&buf)[VPT], int par) {
+        float acc[kMaxSeg];
+#pragma unroll
+        for (int s = 0; s < kMaxSeg; ++s) acc[s] = 0.f;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            if (live(i, t0)) {
-                const elem_t* src = ((meta[i] & 256) ? b1 : b0) + off[i];
-                buf[i] = ld_stream(src);
-            } else {
-                buf[i] = u32x4{0, 0, 0, 0};
+            float f[EV];
+            unpack(DT{}, buf[i], f);
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < EV; ++e) sq = fmaf(f[e], f[e], sq);
+#pragma unroll
+            for (int s = 0; s < kMaxSeg; ++s) acc[s] += (seg[i] == s) ? sq : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxSeg; ++s) {
+            if (s < nseg) {
+                const float w = wave_sum(acc[s]);
+                if (lane == 0) red[par][dwave][s] = w;
             }
+        }
+    };
+    // ---- Phase B (compute path): u = x * gamma, independent of the exchange
+    auto phase_b = [&](const u32x4 (&buf)[VPT], float (&u)[VPT][EV]) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            float f[EV], g[EV];
+            unpack(DT{}, buf[i], f);
+            unpack(DT{}, gam_lds[i * ndt + dt], g);
+#pragma unroll
+            for (int e = 0; e < EV; ++e) u[i][e] = f[e] * g[e];
+        }
+    };
+    // ---- Phase C: y = u * rinv, one rounding to the output format, stored
+    auto phase_c = [&](const float (&u)[VPT][EV], int64_t tile, int par) {
+        const int64_t t0 = tile * rows;
+        const __amdgpu_buffer_rsrc_t oq = rsrc(p.y[0], 0, t0);
+        const __amdgpu_buffer_rsrc_t ok = rsrc(p.y[1], 1, t0);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const float r = rinv_s[par][seg[i]];
+            float o[EV];
+#pragma unroll
+            for (int e = 0; e < EV; ++e) o[e] = u[i][e] * r;
+            __builtin_amdgcn_raw_buffer_store_b128(pack(DT{}, o), tk[i] ? ok : oq, voff[i], 0, kNT);
         }
     };
 
     u32x4 cur[VPT];
     u32x4 nxt[VPT];
-    int64_t tile = group;
-    if (tile < p.n_tiles) load_tile(tile, cur);
+    float up[VPT][EV];  // u of the previous tile, waiting for its factor
 
-    for (; tile < p.n_tiles; tile += p.n_groups) {
-        const int64_t t0 = tile * rows;
-        if (!PREFETCH && tile != group) load_tile(tile, cur);
-
-        // ---- Phase A: local sums of squares (fp32) ---------------------------
-        float acc[NSEG];
+    // k = 0: no tile to finish yet
+    load_tile(tile_of(0), cur);
+    wait_vmcnt<0>();
+    if (PREFETCH) load_tile(tile_of(1), nxt);  // empty descriptor past the end
+    phase_a(cur, 0);
+    __syncthreads();
+    phase_b(cur, up);
+    if (PREFETCH) {
+        wait_vmcnt<0>();
 #pragma unroll
-        for (int s = 0; s < NSEG; ++s) acc[s] = 0.f;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            float f[EV];
-            unpack(DT{}, cur[i], f);
-            float sq = 0.f;
-#pragma unroll
-            for (int e = 0; e < EV; ++e) sq = fmaf(f[e], f[e], sq);
-            const int sg = meta[i] & 255;
-#pragma unroll
-            for (int s = 0; s < NSEG; ++s) acc[s] += (sg == s) ? sq : 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < NSEG; ++s) {
-            if ((s % RMAX) < rows) {
-                const float w = wave_sum(acc[s]);
-                if (lane == 0) red[dwave][s] = w;
-            }
-        }
-        __syncthreads();  // B1
-
-        // ---- prefetch the next tile while the exchange is in flight -----------
-        const int64_t next = tile + p.n_groups;
-        if (PREFETCH && next < p.n_tiles) load_tile(next, nxt);
-
-        // ---- Phase B (compute path): u = x * gamma, independent of the exchange
-        float u[VPT][EV];
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            float f[EV], g[EV];
-            unpack(DT{}, cur[i], f);
-            unpack(DT{}, gam[i], g);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) u[i][e] = f[e] * g[e];
-        }
-        __syncthreads();  // B2: rinv_s from the comm wave
-
-        // ---- Phase C: y = u * rinv, one rounding to the output format ----------
-        elem_t* o0 = y0 + t0 * p.H[0];
-        elem_t* o1 = y1 + t0 * p.H[1];
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            if (live(i, t0)) {
-                const float r = rinv_s[meta[i] & 255];
-                float o[EV];
-#pragma unroll
-                for (int e = 0; e < EV; ++e) o[e] = u[i][e] * r;
-                elem_t* dst = ((meta[i] & 256) ? o1 : o0) + off[i];
-                st_stream(dst, pack(DT{}, o));
-            }
-        }
+        for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
+    }
+    // k = 1 .. K-1: straight-line body, so vmcnt accounting stays exact
+    for (int k = 1; k < K; ++k) {
         if (PREFETCH) {
+            load_tile(tile_of(k + 1), nxt);
+        } else {
+            load_tile(tile_of(k), cur);
+            wait_vmcnt<0>();
+        }
+        phase_a(cur, k & 1);
+        __syncthreads();
+        phase_c(up, tile_of(k - 1), (k - 1) & 1);
+        phase_b(cur, up);
+        if (PREFETCH) {
+            // the VPT stores just issued may stay in flight; the prefetched
+            // loads were issued before them and must be complete
+            wait_vmcnt<VPT>();
 #pragma unroll
             for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
         }
     }
+    // k = K: finish the last tile
+    __syncthreads();
+    phase_c(up, tile_of(K - 1), (K - 1) & 1);
 }
 
 // ================================================================ split kernels
@@ -456,20 +528,18 @@ apply_scale_kernel(const void* x_, const void* g_, const float* rms_inv, int64_t
 // ================================================================ copy ceiling
 
 // Same access widths as the fused kernel (16-byte nontemporal loads and
-// stores); bytes beyond the last full vector are copied one byte at a time.
+// stores), one vector per thread over a grid that covers both buffers;
+// bytes beyond the last full vector are copied one byte at a time.
 __global__ void __launch_bounds__(256)
 copy2_kernel(const void* a, const void* b, void* oa, void* ob, int64_t va, int64_t vb,
              int64_t ta, int64_t tb)
 {
-    const int64_t n = va + vb;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < n; v += stride) {
-        if (v < va) {
-            st_stream(static_cast<char*>(oa) + v * 16, ld_stream(static_cast<const char*>(a) + v * 16));
-        } else {
-            const int64_t w = v - va;
-            st_stream(static_cast<char*>(ob) + w * 16, ld_stream(static_cast<const char*>(b) + w * 16));
-        }
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (v < va) {
+        st_stream(static_cast<char*>(oa) + v * 16, ld_stream(static_cast<const char*>(a) + v * 16));
+    } else if (v < va + vb) {
+        const int64_t w = v - va;
+        st_stream(static_cast<char*>(ob) + w * 16, ld_stream(static_cast<const char*>(b) + w * 16));
     }
     if (blockIdx.x == 0) {
         for (int64_t i = threadIdx.x; i < ta; i += 256)

@@ -21,10 +21,11 @@ _lock = threading.Lock()
 QKN_OK, QKN_EINVAL, QKN_EOVERLAP, QKN_ENOMEM, QKN_EHIP = 0, -1, -2, -3, -4
 QKN_ERESIDENCY, QKN_ETIMEOUT, QKN_ECAPTURE = -5, -6, -7
 QKN_BF16, QKN_F32 = 0, 1
-NUM_VARIANTS = 5
+NUM_VARIANTS = 6
+MAX_DATA_WAVES = 15
 MAX_SHARDS = 32
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
-       "max_groups": 6, "force_split": 7, "test_skip_publish": 8}
+       "max_groups": 6, "force_split": 7, "test_skip_publish": 8, "data_waves": 9}
 
 
 class QKNormError(RuntimeError):
@@ -38,7 +39,8 @@ class QKNormError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("variant", ctypes.c_int), ("threads", ctypes.c_int), ("slots", ctypes.c_int),
+    _fields_ = [("variant", ctypes.c_int), ("threads", ctypes.c_int),
+                ("data_waves", ctypes.c_int), ("slots", ctypes.c_int),
                 ("rows", ctypes.c_int), ("n_tiles", ctypes.c_int64), ("n_groups", ctypes.c_int),
                 ("grid", ctypes.c_int), ("xcd_map", ctypes.c_int), ("iters", ctypes.c_int)]
 
@@ -238,8 +240,14 @@ def get_option(name: str) -> int:
 
 def plan_fused(dtype: str, T: int, Hq: int, Hk: int, n_shards: int, cu_count: int,
                blocks_per_cu, aligned: bool = True) -> dict:
-    """Host-only launch plan for a device with the given capacity (no GPU needed)."""
-    arr = (ctypes.c_int * NUM_VARIANTS)(*blocks_per_cu)
+    """Host-only launch plan for a device with the given capacity (no GPU needed).
+
+    ``blocks_per_cu[v][w]``: co-resident workgroups per CU of variant v with w
+    data waves (NUM_VARIANTS x (MAX_DATA_WAVES + 1)).
+    """
+    flat = [int(x) for row in blocks_per_cu for x in row]
+    assert len(flat) == NUM_VARIANTS * (MAX_DATA_WAVES + 1)
+    arr = (ctypes.c_int * len(flat))(*flat)
     pl = Plan()
     _check(lib().qknorm_plan_fused(QKN_BF16 if dtype == "bf16" else QKN_F32, T, Hq, Hk, n_shards,
                                    cu_count, arr, 1 if aligned else 0, ctypes.byref(pl)),
@@ -256,12 +264,13 @@ def max_coresident_workgroups(dtype: str, Hq: int, Hk: int, n_shards: int) -> in
 
 
 def device_occupancy(dtype: str):
-    """(blocks_per_cu per fused variant, compute units) of the current device."""
-    arr = (ctypes.c_int * NUM_VARIANTS)()
+    """(blocks_per_cu[variant][data_waves], compute units) of the current device."""
+    arr = (ctypes.c_int * (NUM_VARIANTS * (MAX_DATA_WAVES + 1)))()
     cu = ctypes.c_int(0)
     _check(lib().qknorm_device_occupancy(QKN_BF16 if dtype == "bf16" else QKN_F32, arr,
                                          ctypes.byref(cu)), "qknorm_device_occupancy")
-    return list(arr), cu.value
+    w = MAX_DATA_WAVES + 1
+    return [list(arr[v * w:(v + 1) * w]) for v in range(NUM_VARIANTS)], cu.value
 
 
 def current_plan(dtype: str, T: int, Hq: int, Hk: int, n_shards: int, aligned: bool = True):

@@ -96,62 +96,117 @@ def test_split_entry_points_reject_bad_arguments():
 
 # ------------------------------------------------------------------ planner
 
-def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=BPC):
+CU = 256
+VPT = [1, 2, 3, 4, 6, 9]
+MAXW = [15, 15, 15, 15, 11, 15]
+VGPR = [32, 56, 80, 104, 168, 120]  # per-variant register use, roughly as compiled
+
+
+def occupancy_model(dtype="bf16", lds_kb=160, waves_per_simd=8):
+    """Synthetic blocks_per_cu[v][w]: register file, wave slots and LDS limits."""
+    table = []
+    for v in range(ops.NUM_VARIANTS):
+        row = [0] * (ops.MAX_DATA_WAVES + 1)
+        for w in range(1, MAXW[v] + 1):
+            if v == 5 and dtype != "f32":
+                continue
+            waves = w + 1
+            per_simd = -(-waves // 4)
+            by_regs = min(waves_per_simd, 512 // VGPR[v]) // per_simd
+            by_lds = (lds_kb * 1024) // (VPT[v] * 64 * w * 16 + 1024)
+            row[w] = max(0, min(by_regs, by_lds, 32 // waves))
+        table.append(row)
+    return table
+
+
+BPC = {"bf16": occupancy_model("bf16"), "f32": occupancy_model("f32")}
+
+
+def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=None):
+    bpc = bpc or BPC[dtype]
     if p["variant"] < 0:
         return
-    v = p["variant"]
-    cap = bpc[v] * cu
+    v, w = p["variant"], p["data_waves"]
+    assert p["threads"] == 64 * (w + 1) and 1 <= w <= MAXW[v]
+    assert p["slots"] == VPT[v]
+    cap = bpc[v][w] * cu
     assert p["grid"] == p["n_groups"] * N
     assert p["grid"] <= cap, "grid must not exceed co-resident capacity"
-    assert 1 <= p["rows"]
+    assert 1 <= p["rows"] <= 4
     assert N * 2 * p["rows"] <= 64
     assert p["n_tiles"] == -(-T // p["rows"])
     assert 1 <= p["n_groups"] <= p["n_tiles"]
     assert p["iters"] * p["n_groups"] >= p["n_tiles"] > (p["iters"] - 1) * p["n_groups"]
     ev = 8 if dtype == "bf16" else 4
-    vrow = (Hq // N + Hk // N) // ev
-    assert p["rows"] * vrow <= (p["threads"] - 64) * p["slots"]  # data threads x slots
+    wvq, wvk = Hq // N // ev, Hk // N // ev
+    # Q's part of a tile is padded to whole waves, then K's part follows
+    need = -(-p["rows"] * wvq // 64) * 64 + p["rows"] * wvk
+    assert need <= w * 64 * p["slots"]  # data threads x slots
     if p["xcd_map"]:
         assert p["n_groups"] % 8 == 0
 
 
+def plan(dtype, T, Hq, Hk, N, cu=CU, bpc=None, aligned=True):
+    return ops.plan_fused(dtype, T, Hq, Hk, N, cu, bpc or BPC[dtype], aligned)
+
+
 def test_plan_named_workloads():
     for w in (inputs.TINY, inputs.DECODE, inputs.PREFILL, inputs.GQA):
-        p = ops.plan_fused(w.dtype, w.T, w.Hq, w.Hk, w.n_shards, CU, BPC)
+        p = plan(w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
         assert p["variant"] >= 0, w.name
         check_plan(p, w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
-    d = ops.plan_fused("bf16", 64, 4096, 4096, 4, CU, BPC)
+    d = plan("bf16", 64, 4096, 4096, 4)
     assert d["rows"] == 1 and d["grid"] == 256 and d["xcd_map"] == 1
 
 
 def test_plan_every_sweep_point():
     for w in inputs.sweep():
-        p = ops.plan_fused(w.dtype, w.T, w.Hq, w.Hk, w.n_shards, CU, BPC)
+        p = plan(w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
         assert p["variant"] >= 0, w.name  # every sweep shape fits a fused variant
         check_plan(p, w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
 
 
 def test_plan_refuses_grid_beyond_residency():
+    one = [[1] * (ops.MAX_DATA_WAVES + 1) for _ in range(ops.NUM_VARIANTS)]
     with pytest.raises(ops.QKNormError) as e:
-        ops.plan_fused("bf16", 64, 4096, 4096, 8, 4, [1, 1, 1, 1, 1])  # capacity 4 < 8
+        plan("bf16", 64, 4096, 4096, 8, cu=4, bpc=one)  # capacity 4 < 8
     assert e.value.status == ops.QKN_ERESIDENCY
-    p = ops.plan_fused("bf16", 100000, 4096, 4096, 8, 4, [2, 2, 2, 2, 2])  # capacity exactly 8
+    two = [[2] * (ops.MAX_DATA_WAVES + 1) for _ in range(ops.NUM_VARIANTS)]
+    p = plan("bf16", 100000, 4096, 4096, 8, cu=4, bpc=two)  # capacity exactly 8
     assert p["grid"] == 8 and p["n_groups"] == 1
 
 
 def test_plan_split_fallbacks():
-    assert ops.plan_fused("bf16", 64, 4096, 4096, 4, CU, BPC, aligned=False)["variant"] == -1
-    assert ops.plan_fused("bf16", 64, 100, 100, 4, CU, BPC)["variant"] == -1  # 25-wide shards
+    assert plan("bf16", 64, 4096, 4096, 4, aligned=False)["variant"] == -1
+    assert plan("bf16", 64, 100, 100, 4)["variant"] == -1  # 25-wide shards
     # rows too wide for any bf16 variant's registers
-    assert ops.plan_fused("bf16", 64, 65536, 65536, 1, CU, BPC)["variant"] == -1
-    # variant unusable on this device (zero occupancy): next one up is used
-    p = ops.plan_fused("bf16", 64, 4096, 4096, 4, CU, [0, 3, 2, 1, 1])
-    assert p["variant"] == 1
+    assert plan("bf16", 64, 65536, 65536, 1)["variant"] == -1
+    # unlaunchable variants are skipped
+    t = occupancy_model("bf16")
+    t[0] = [0] * (ops.MAX_DATA_WAVES + 1)
+    t[1] = [0] * (ops.MAX_DATA_WAVES + 1)
+    p = plan("bf16", 64, 4096, 4096, 4, bpc=t)
+    assert p["variant"] >= 2
+    check_plan(p, "bf16", 64, 4096, 4096, 4, bpc=t)
+
+
+def test_plan_forced_options_are_honoured():
+    old = {n: ops.get_option(n) for n in ("force_variant", "data_waves", "rows")}
+    try:
+        ops.set_option("force_variant", 1)
+        ops.set_option("data_waves", 6)
+        ops.set_option("rows", 1)
+        p = plan("bf16", 16384, 5120, 5120, 2)
+        assert (p["variant"], p["data_waves"], p["rows"]) == (1, 6, 1)
+        check_plan(p, "bf16", 16384, 5120, 5120, 2)
+    finally:
+        for n, v in old.items():
+            ops.set_option(n, v)
 
 
 def test_plan_many_shards_uses_narrow_tiles():
     for N in (16, 32):
-        p = ops.plan_fused("bf16", 4096, 4096, 4096, N, CU, BPC)
+        p = plan("bf16", 4096, 4096, 4096, N)
         assert p["variant"] >= 0 and N * 2 * p["rows"] <= 64
         check_plan(p, "bf16", 4096, 4096, 4096, N)
 
@@ -167,10 +222,12 @@ def test_plan_randomised_invariants():
         Hk = N * ev * rnd.randint(1, 600)
         T = rnd.choice([1, 2, 3, 7, 63, 64, 65, 1000, 4097, rnd.randint(1, 200000)])
         cu = rnd.choice([1, 8, 80, 256])
-        bpc = [rnd.randint(0, 8) for _ in range(5)]
+        bpc = [[rnd.randint(0, 8) if w else 0 for w in range(ops.MAX_DATA_WAVES + 1)]
+               for _ in range(ops.NUM_VARIANTS)]
         try:
-            p = ops.plan_fused(dt, T, Hq, Hk, N, cu, bpc)
+            p = plan(dt, T, Hq, Hk, N, cu=cu, bpc=bpc)
         except ops.QKNormError as e:
+            assert e.value.status == ops.QKN_ERESIDENCY if hasattr(e, "value") else True
             assert e.status == ops.QKN_ERESIDENCY
             continue
         check_plan(p, dt, T, Hq, Hk, N, cu, bpc)

@@ -149,9 +149,11 @@ int qknorm_release_workspace(void);
  * device with `cu_count` compute units, of which each holds
  * `blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1) + w]` workgroups of kernel
  * variant v with w data waves (the layout of qknorm_device_occupancy; the
- * real path queries the occupancy API). Variant v holds a fixed number of
- * 16-byte vectors per data thread (1, 2, 3, 4, 6, 9; the last fp32 only). */
-#define QKN_NUM_VARIANTS 6
+ * real path queries the occupancy API). Variants 0-5 hold 1, 2, 3, 4, 6, 9
+ * 16-byte vectors per data thread (5: fp32 only) and scale a tile one
+ * iteration after reducing it; variants 6-9 hold 1, 2, 3, 4 and scale it two
+ * iterations later, which decouples the shards of a group further. */
+#define QKN_NUM_VARIANTS 10
 #define QKN_MAX_DATA_WAVES 15
 typedef struct qknorm_plan {
     int variant;        /* fused kernel variant, or -1: shape uses the split kernels */
@@ -191,6 +193,14 @@ int64_t qknorm_get_option(int key);
  * (bytes_q, bytes_k bytes) with the fused kernel's access widths. */
 int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
                       int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
+
+/* Measurement helper: issues `repeats` back-to-back fused calls with the same
+ * arguments (as qknorm_layerwise_fwd_<dtype>, dtype = QKN_BF16 or QKN_F32)
+ * from C, so that launch-rate-bound shapes can be timed without a host
+ * language's per-call overhead. Returns the first non-OK status. */
+int qknorm_bench_fused(int dtype, const void* q, const void* k, const void* gamma_q,
+                       const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
+                       float eps, void* out_q, void* out_k, int repeats, hipStream_t stream);
 
 #ifdef __cplusplus
 }

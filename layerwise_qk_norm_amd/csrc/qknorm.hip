@@ -16,6 +16,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 
 #include "qknorm_kernels.hpp"
@@ -32,15 +33,20 @@ struct Variant {
     int vpt;          // 16-byte slots per data thread
     bool prefetch;    // next tile loaded during the exchange
     bool f32_only;    // register budget only fits fp32 (no prefetch buffer)
+    int lag;          // tiles between a tile's reduction and its scaling
     int max_threads;  // launch bound of the instantiation
 };
 constexpr Variant kVariants[QKN_NUM_VARIANTS] = {
-    {1, true, false, 1024},
-    {2, true, false, 1024},
-    {3, true, false, 1024},
-    {4, true, false, 1024},
-    {6, true, false, 768},
-    {9, false, true, 1024},
+    {1, true, false, 1, 1024},
+    {2, true, false, 1, 1024},
+    {3, true, false, 1, 1024},
+    {4, true, false, 1, 1024},
+    {6, true, false, 1, 768},
+    {9, false, true, 1, 1024},
+    {1, true, false, 2, 1024},
+    {2, true, false, 2, 1024},
+    {3, true, false, 2, 768},
+    {4, true, false, 2, 512},
 };
 int max_data_waves(int v) { return kVariants[v].max_threads / 64 - 1; }
 
@@ -50,11 +56,15 @@ template <class DT>
 FusedFn fused_fn(int v)
 {
     switch (v) {
-    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1024>;
-    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1024>;
-    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1024>;
-    case 3: return qkn::fused_qknorm_kernel<DT, 4, true, 1024>;
-    case 4: return qkn::fused_qknorm_kernel<DT, 6, true, 768>;
+    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1, 1024>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1, 1024>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1, 1024>;
+    case 3: return qkn::fused_qknorm_kernel<DT, 4, true, 1, 1024>;
+    case 4: return qkn::fused_qknorm_kernel<DT, 6, true, 1, 768>;
+    case 6: return qkn::fused_qknorm_kernel<DT, 1, true, 2, 1024>;
+    case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024>;
+    case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768>;
+    case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512>;
     default: return nullptr;
     }
 }
@@ -62,12 +72,16 @@ template <>
 FusedFn fused_fn<F32>(int v)
 {
     switch (v) {
-    case 0: return qkn::fused_qknorm_kernel<F32, 1, true, 1024>;
-    case 1: return qkn::fused_qknorm_kernel<F32, 2, true, 1024>;
-    case 2: return qkn::fused_qknorm_kernel<F32, 3, true, 1024>;
-    case 3: return qkn::fused_qknorm_kernel<F32, 4, true, 1024>;
-    case 4: return qkn::fused_qknorm_kernel<F32, 6, true, 768>;
-    case 5: return qkn::fused_qknorm_kernel<F32, 9, false, 1024>;
+    case 0: return qkn::fused_qknorm_kernel<F32, 1, true, 1, 1024>;
+    case 1: return qkn::fused_qknorm_kernel<F32, 2, true, 1, 1024>;
+    case 2: return qkn::fused_qknorm_kernel<F32, 3, true, 1, 1024>;
+    case 3: return qkn::fused_qknorm_kernel<F32, 4, true, 1, 1024>;
+    case 4: return qkn::fused_qknorm_kernel<F32, 6, true, 1, 768>;
+    case 5: return qkn::fused_qknorm_kernel<F32, 9, false, 1, 1024>;
+    case 6: return qkn::fused_qknorm_kernel<F32, 1, true, 2, 1024>;
+    case 7: return qkn::fused_qknorm_kernel<F32, 2, true, 2, 1024>;
+    case 8: return qkn::fused_qknorm_kernel<F32, 3, true, 2, 768>;
+    case 9: return qkn::fused_qknorm_kernel<F32, 4, true, 2, 512>;
     default: return nullptr;
     }
 }
@@ -77,6 +91,20 @@ FusedFn fused_fn_for(int dtype, int v) { return dtype == QKN_BF16 ? fused_fn<Bf1
 size_t gamma_lds_bytes(int v, int nwd) { return (size_t)kVariants[v].vpt * 64 * nwd * 16; }
 
 // ---------------------------------------------------------------- options
+
+// Plans are cached per (device, dtype, shape, alignment); any option change
+// bumps g_opt_epoch, which invalidates every cached plan.
+struct PlanKey {
+    int dev, dtype, n_shards, aligned;
+    int64_t T, Hq, Hk;
+    uint64_t epoch;
+    bool operator<(const PlanKey& o) const
+    {
+        return std::tie(dev, dtype, n_shards, aligned, T, Hq, Hk, epoch) <
+               std::tie(o.dev, o.dtype, o.n_shards, o.aligned, o.T, o.Hq, o.Hk, o.epoch);
+    }
+};
+uint64_t g_opt_epoch = 0;
 
 struct Options {
     int64_t spin_ns = 1000000000;
@@ -269,54 +297,103 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // vectors a tile of r rows occupies: Q's part padded to whole waves, then K's
     auto tile_vectors = [&](int64_t r) { return ((r * wvq + 63) / 64) * 64 + r * wvk; };
 
-    // Candidates (variant, data waves, rows). The tile must fit the data
-    // threads' slots, and 2 * rows * N comm lanes must fit one wave. Among
-    // those the planner maximises the load bytes in flight per CU (workgroups
-    // per CU x tile bytes) -- the quantity that sets a streaming kernel's
-    // bandwidth. Within 2 % of that it prefers more workgroups (parallelism,
-    // which decides small batches), then fuller slots, then smaller workgroups.
+    // Candidates (variant, data waves, rows, workgroups per CU). The tile must
+    // fit the data threads' slots, and 2 * rows * N comm lanes must fit one
+    // wave. Each candidate is scored by how far it lies, on a log scale, from
+    // about 20 KB of loads in flight per CU and about 8 waves per CU, with
+    // small preferences for more rows per tile, fuller slots and more vectors
+    // per thread. The rule and its constants were fitted to launch timings of
+    // 18 shapes on MI355X (mean 3 % from the best launch of each shape).
     struct Best {
-        int v = -1, w = 0, rows = 0;
-        double inflight = -1, util = 0;
-        int64_t cap = 0, wgs = 0;
+        int v = -1, w = 0, rows = 0, wpc = 0;
+        double score = 0;
+        int64_t wgs = 0;
     } best;
-    const int rows_cap = (int)std::min<int64_t>({(int64_t)qkn::kMaxRows, 32 / N, T});
-    for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
-        if (g_opt.force_variant >= 0 && v != g_opt.force_variant) continue;
+    // With peers to wait for, the two-tile lag decouples partners; a lag-1
+    // variant is used only where no lag-2 variant holds the same slots.
+    auto has_lag2 = [&](int vpt) {
+        for (const Variant& x : kVariants)
+            if (x.lag == 2 && x.vpt == vpt) return true;
+        return false;
+    };
+    auto allowed = [&](int v) {
         const Variant& k = kVariants[v];
-        if (k.f32_only && dtype != QKN_F32) continue;
-        for (int r = 1; r <= rows_cap; ++r) {
-            if (g_opt.rows > 0 && r != g_opt.rows) continue;
-            const int64_t tv = tile_vectors(r);
-            int w = (int)((tv + 64 * k.vpt - 1) / (64 * k.vpt));
-            if (g_opt.force_data_waves > 0) {
-                if (g_opt.force_data_waves < w) continue;
-                w = (int)g_opt.force_data_waves;
+        if (k.f32_only && dtype != QKN_F32) return false;
+        if (g_opt.force_variant >= 0) return v == g_opt.force_variant;
+        if (N == 1) return k.lag == 1;
+        return k.lag == 2 || !has_lag2(k.vpt);
+    };
+    const int rows_cap = (int)std::min<int64_t>({(int64_t)qkn::kMaxRows, 32 / N, T});
+    const double batch = (double)T * (double)(wvq + wvk) * 16.0 * N;  // bytes read per call
+    auto consider = [&](int v, int w, int r, int wpc) {
+        const Variant& k = kVariants[v];
+        const int64_t tv = tile_vectors(r);
+        if (w < 1 || w > max_data_waves(v) || (int64_t)64 * w * k.vpt < tv) return;
+        const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
+        if (b <= 0 || wpc > b || (int64_t)b * cu < N) return;
+        const int64_t tiles = (T + r - 1) / r;
+        const int64_t groups = std::min<int64_t>(tiles, (int64_t)wpc * cu / N);
+        if (groups < 1) return;
+        const int64_t wgs = groups * N;
+        const double inflight = std::min((double)wgs * (double)(tv * 16), batch) / cu;
+        const double waves = (double)wgs / cu * (w + 1);
+        const double util = (double)tv / (double)(64 * w * k.vpt);
+        double sc = std::fabs(std::log2(std::max(inflight, 1.0) / (20.0 * 1024))) +
+                    0.5 * std::fabs(std::log2(std::max(waves, 0.1) / 8.0)) - 0.1 * r -
+                    0.5 * util - 0.2 * std::log2((double)k.vpt);
+        // a batch smaller than the in-flight target is latency-bound: every
+        // token gets its own workgroup group if the device can hold them
+        if (batch / cu < 20.0 * 1024) sc += std::log2((double)(T * N) / (double)wgs);
+        if (best.v < 0 || sc < best.score) {
+            best.v = v;
+            best.w = w;
+            best.rows = r;
+            best.wpc = wpc;
+            best.score = sc;
+            best.wgs = wgs;
+        }
+    };
+    // Launches measured fastest on MI355X for the prefill-sized Q/K shards of
+    // the letter's models (width 5120 split 1, 2, 4 or 8 ways; 5120/1024 split
+    // 4 ways), used for batches of at least 4096 tokens when nothing is forced
+    // and the device can hold them.
+    struct Tuned {
+        int dtype, wq, wk, n, v, w, rows, wpc;
+    };
+    static const Tuned kTuned[] = {
+        {QKN_BF16, 5120, 5120, 1, 4, 4, 1, 1},
+        {QKN_BF16, 2560, 2560, 2, 9, 5, 2, 1},
+        {QKN_BF16, 1280, 1280, 4, 7, 10, 4, 1},
+        {QKN_BF16, 640, 640, 8, 8, 3, 3, 2},
+        {QKN_BF16, 1280, 256, 4, 8, 2, 2, 3},
+    };
+    const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0;
+    if (!forced && T >= 4096) {
+        for (const Tuned& t : kTuned) {
+            if (t.dtype == dtype && t.wq == Wq && t.wk == Wk && t.n == N && t.rows <= rows_cap)
+                consider(t.v, t.w, t.rows, t.wpc);
+        }
+    }
+    if (best.v < 0) {
+        for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
+            if (!allowed(v)) continue;
+            const Variant& k = kVariants[v];
+            for (int r = 1; r <= rows_cap; ++r) {
+                if (g_opt.rows > 0 && r != g_opt.rows) continue;
+                const int64_t tv = tile_vectors(r);
+                int w = (int)((tv + 64 * k.vpt - 1) / (64 * k.vpt));
+                if (g_opt.force_data_waves > 0) {
+                    if (g_opt.force_data_waves < w) continue;
+                    w = (int)g_opt.force_data_waves;
+                }
+                if (w < 1 || w > max_data_waves(v)) continue;
+                const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
+                const int64_t tiles = (T + r - 1) / r;
+                for (int wpc = 1; wpc <= b; ++wpc) {
+                    consider(v, w, r, wpc);
+                    if ((int64_t)wpc * cu / N >= tiles) break;  // more would idle
+                }
             }
-            if (w < 1 || w > max_data_waves(v)) continue;
-            const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
-            if (b <= 0) continue;
-            const int64_t cap = (int64_t)b * cu;
-            if (cap < N) continue;
-            const int64_t tiles = (T + r - 1) / r;
-            const int64_t wgs = std::min<int64_t>(tiles, cap / N) * N;
-            // bytes of loads in flight per CU, never more than the batch holds
-            const double batch = (double)T * (double)(wvq + wvk) * 16.0 * N;
-            const double inflight = std::min((double)wgs * (double)(tv * 16), batch) / cu;
-            const double util = (double)tv / (double)(64 * w * k.vpt);
-            bool better;
-            if (inflight > best.inflight * 1.02) {
-                better = true;
-            } else if (inflight < best.inflight * 0.98) {
-                better = false;
-            } else if (wgs != best.wgs) {
-                better = wgs > best.wgs;
-            } else if (util > best.util + 1e-9 || util < best.util - 1e-9) {
-                better = util > best.util;
-            } else {
-                better = w < best.w;
-            }
-            if (better) best = {v, w, r, inflight, util, cap, wgs};
         }
     }
     if (best.v < 0) {
@@ -334,7 +411,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     }
     const int rows = best.rows;
     const int64_t n_tiles = (T + rows - 1) / rows;
-    int64_t groups = std::min<int64_t>(n_tiles, best.cap / N);
+    int64_t groups = best.wgs / N;
     if (g_opt.max_groups > 0) groups = std::min<int64_t>(groups, g_opt.max_groups);
     int xcd = 0;
     if (g_opt.xcd_map != 0 && groups >= 8) {
@@ -446,8 +523,17 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
 
     const int aligned = aligned16(q) && aligned16(k) && aligned16(gq) && aligned16(gk) &&
                         aligned16(oq) && aligned16(ok);
+    static std::map<PlanKey, qknorm_plan> cache;
+    const PlanKey key{dev, dtype, N, aligned, T, Hq, Hk, g_opt_epoch};
     qknorm_plan pl;
-    if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, &di->occ[dtype][0][0], aligned, &pl))) return rc;
+    auto hit = cache.find(key);
+    if (hit != cache.end()) {
+        pl = hit->second;
+    } else {
+        if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, &di->occ[dtype][0][0], aligned, &pl))) return rc;
+        if (cache.size() > 4096) cache.clear();
+        cache.emplace(key, pl);
+    }
 
     if (pl.variant < 0) {
         // Shapes the fused kernel cannot hold in registers (or unaligned): the
@@ -468,7 +554,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
         return QKN_OK;
     }
 
-    const size_t entries = (size_t)pl.n_groups * 2 * N * 2 * pl.rows;
+    const size_t entries = (size_t)pl.n_groups * 2 * kVariants[pl.variant].lag * N * 2 * pl.rows;
     if ((rc = ensure_slots(ws, entries, stream))) return rc;
     if ((uint64_t)ws->tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
         // tags would wrap: clear every slot so no stale tag can match
@@ -701,6 +787,8 @@ int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards
 
 int qknorm_set_option(int key, int64_t value)
 {
+    std::lock_guard<std::mutex> lock(g_mu);
+    ++g_opt_epoch;
     switch (key) {
     case QKN_OPT_SPIN_LIMIT_NS: if (value < 1) return QKN_EINVAL; g_opt.spin_ns = value; return QKN_OK;
     case QKN_OPT_FORCE_VARIANT:
@@ -755,6 +843,20 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k, in
     hipLaunchKernelGGL(qkn::copy2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, k, out_q,
                        out_k, va, vb, bytes_q - va * 16, bytes_k - vb * 16);
     QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+int qknorm_bench_fused(int dtype, const void* q, const void* k, const void* gamma_q,
+                       const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
+                       float eps, void* out_q, void* out_k, int repeats, hipStream_t stream)
+{
+    if (dtype != QKN_BF16 && dtype != QKN_F32) return QKN_EINVAL;
+    if (repeats < 0) return QKN_EINVAL;
+    for (int i = 0; i < repeats; ++i) {
+        const int rc = layerwise_fwd(dtype, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps,
+                                     out_q, out_k, stream);
+        if (rc) return rc;
+    }
     return QKN_OK;
 }
 

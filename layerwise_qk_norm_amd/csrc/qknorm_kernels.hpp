@@ -177,14 +177,15 @@ struct FusedParams {
 //
 // Pipeline: a group's tiles k = 0..K-1 go through one barrier per iteration.
 // In iteration k the data waves issue the loads of tile k+1, reduce tile k
-// (Phase A), pass the barrier, scale and store tile k-1 (Phase C), and form
+// (Phase A), pass the barrier, scale and store tile k-LAG (Phase C), and form
 // u = x*gamma of tile k (Phase B compute path). The comm wave, before the
-// barrier, acquires the peers' partials of tile k-1 (published one iteration
-// earlier) and combines them; after it, it publishes its own partial of tile
-// k. Partners are thereby coupled one iteration apart, and the exchange
-// overlaps both the load of the next tile and the product x*gamma. red and
-// rinv_s are double-buffered by tile parity.
-template <class DT, int VPT, bool PREFETCH, int MAXT>
+// barrier, acquires the peers' partials of tile k-LAG (published LAG
+// iterations earlier) and combines them; after it, it publishes its own
+// partial of tile k. A member can thus run LAG-1 iterations ahead of its
+// partners without waiting, and the exchange overlaps the loads of the next
+// tiles and the products x*gamma. u is held for LAG tiles; the slot ring is
+// 2*LAG deep; red and rinv_s are double-buffered by tile parity.
+template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT>
 __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
@@ -235,14 +236,16 @@ fused_qknorm_kernel(FusedParams p)
         const bool peer = active && kk != shard;
         const float Hf = (float)(sg < rows ? p.H[0] : p.H[1]);
         bool abandon = false;
-        float own_prev = 0.f;
-        for (int k = 0; k <= K; ++k) {
-            if (k >= 1) {
-                // ---- Phase B comm path for tile k-1 ----------------------------
-                const int j = k - 1;
+        constexpr int RING = 2 * LAG;  // slot ring depth
+        float own0 = 0.f, own1 = 0.f;  // own partials of the last tiles (even, odd)
+        for (int k = 0; k < K + LAG; ++k) {
+            if (k >= LAG) {
+                // ---- Phase B comm path for tile k-LAG ---------------------------
+                const int j = k - LAG;
                 const unsigned long long* slot =
-                    p.slots + ((size_t)(group * 2 + (j & 1)) * N) * nseg + lane;
+                    p.slots + ((size_t)(group * RING + (j % RING)) * N) * nseg + lane;
                 const uint32_t want = p.tag_base + (uint32_t)j;
+                const float own_prev = (LAG == 2 && (j & 1)) ? own1 : own0;
                 float v = mine ? own_prev : 0.f;
                 bool need = peer && !abandon;
                 if (__any(need)) {
@@ -269,16 +272,17 @@ fused_qknorm_kernel(FusedParams p)
                 for (int k2 = 0; k2 < N; ++k2) S += __shfl(v, k2 * nseg + sg);
                 if (lane < nseg) rinv_s[j & 1][lane] = 1.0f / sqrtf(S / Hf + p.eps);
             }
-            __syncthreads();  // red[k&1] written; rinv_s[(k-1)&1] ready
+            __syncthreads();  // red[k&1] written; rinv_s[(k-LAG)&1] ready
             if (k < K && mine) {
-                // ---- publish the partial of tile k (after acquiring tile k-1,
-                // so a two-deep slot ring never overwrites an unread value)
+                // ---- publish the partial of tile k (after acquiring tile k-LAG:
+                // a peer reads tile k-2*LAG before it publishes tile k-LAG, so a
+                // 2*LAG-deep ring never overwrites an unread value)
                 float own = 0.f;
                 for (int w = 0; w < nwd; ++w) own += red[k & 1][w][sg];
-                own_prev = own;
+                if (LAG == 2 && (k & 1)) own1 = own; else own0 = own;
                 if (N > 1 && !(p.test_flags & 1u)) {
                     unsigned long long* slot =
-                        p.slots + ((size_t)(group * 2 + (k & 1)) * N) * nseg + lane;
+                        p.slots + ((size_t)(group * RING + (k % RING)) * N) * nseg + lane;
                     slot_publish(slot, p.tag_base + (uint32_t)k, own);
                 }
             }
@@ -332,8 +336,8 @@ fused_qknorm_kernel(FusedParams p)
             valid ? ld_cached(static_cast<const elem_t*>(p.gamma[t]) + col) : u32x4{0, 0, 0, 0};
     }
 
-    auto tile_of = [&](int k) -> int64_t { return group + (int64_t)k * p.n_groups; };
-    auto rsrc = [&](const void* base, int t, int64_t t0) {
+    auto tile_of = [&](int k) __attribute__((always_inline)) -> int64_t { return group + (int64_t)k * p.n_groups; };
+    auto rsrc = [&](const void* base, int t, int64_t t0) __attribute__((always_inline)) {
         // rows of this tile that exist; 0 past the end (then every access is out of range)
         const int64_t left = p.T - t0;
         const int vr = left <= 0 ? 0 : (left < rows ? (int)left : rows);
@@ -341,7 +345,7 @@ fused_qknorm_kernel(FusedParams p)
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, vr * p.H[t] * ES,
                                                  0x00020000);
     };
-    auto load_tile = [&](int64_t tile, u32x4 (&buf)[VPT]) {
+    auto load_tile = [&](int64_t tile, u32x4 (&buf)[VPT]) __attribute__((always_inline)) {
         const int64_t t0 = tile * rows;
         const __amdgpu_buffer_rsrc_t rq = rsrc(p.x[0], 0, t0);
         const __amdgpu_buffer_rsrc_t rk = rsrc(p.x[1], 1, t0);
@@ -350,7 +354,7 @@ fused_qknorm_kernel(FusedParams p)
             buf[i] = __builtin_amdgcn_raw_buffer_load_b128(tk[i] ? rk : rq, voff[i], 0, kNT);
     };
     // ---- Phase A: local sums of squares (fp32) of the tile in buf -> red[par]
-    auto phase_a = [&](const u32x4 (&buf)[VPT], int par) {
+    auto phase_a = [&](const u32x4 (&buf)[VPT], int par) __attribute__((always_inline)) {
         float acc[kMaxSeg];
 #pragma unroll
         for (int s = 0; s < kMaxSeg; ++s) acc[s] = 0.f;
@@ -373,7 +377,7 @@ fused_qknorm_kernel(FusedParams p)
         }
     };
     // ---- Phase B (compute path): u = x * gamma, independent of the exchange
-    auto phase_b = [&](const u32x4 (&buf)[VPT], float (&u)[VPT][EV]) {
+    auto phase_b = [&](const u32x4 (&buf)[VPT], float (&u)[VPT][EV]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             float f[EV], g[EV];
@@ -384,7 +388,7 @@ fused_qknorm_kernel(FusedParams p)
         }
     };
     // ---- Phase C: y = u * rinv, one rounding to the output format, stored
-    auto phase_c = [&](const float (&u)[VPT][EV], int64_t tile, int par) {
+    auto phase_c = [&](const float (&u)[VPT][EV], int64_t tile, int par) __attribute__((always_inline)) {
         const int64_t t0 = tile * rows;
         const __amdgpu_buffer_rsrc_t oq = rsrc(p.y[0], 0, t0);
         const __amdgpu_buffer_rsrc_t ok = rsrc(p.y[1], 1, t0);
@@ -400,43 +404,76 @@ fused_qknorm_kernel(FusedParams p)
 
     u32x4 cur[VPT];
     u32x4 nxt[VPT];
-    float up[VPT][EV];  // u of the previous tile, waiting for its factor
+    float up0[VPT][EV];  // u of tiles with k % LAG == 0, waiting for their factor
+    float up1[VPT][EV];  // u of tiles with k % LAG == 1 (LAG == 2 only)
 
-    // k = 0: no tile to finish yet
-    load_tile(tile_of(0), cur);
-    wait_vmcnt<0>();
-    if (PREFETCH) load_tile(tile_of(1), nxt);  // empty descriptor past the end
-    phase_a(cur, 0);
-    __syncthreads();
-    phase_b(cur, up);
-    if (PREFETCH) {
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
-    }
-    // k = 1 .. K-1: straight-line body, so vmcnt accounting stays exact
-    for (int k = 1; k < K; ++k) {
+    // one iteration k >= 1 of the steady state; u holds tile k-LAG on entry
+    // (finished here) and tile k on exit
+    auto step = [&](int k, float (&u)[VPT][EV], bool finish) __attribute__((always_inline)) {
         if (PREFETCH) {
-            load_tile(tile_of(k + 1), nxt);
+            load_tile(tile_of(k + 1), nxt);  // empty descriptor past the end
         } else {
             load_tile(tile_of(k), cur);
             wait_vmcnt<0>();
         }
         phase_a(cur, k & 1);
         __syncthreads();
-        phase_c(up, tile_of(k - 1), (k - 1) & 1);
-        phase_b(cur, up);
+        if (finish) phase_c(u, tile_of(k - LAG), (k - LAG) & 1);
+        phase_b(cur, u);
         if (PREFETCH) {
-            // the VPT stores just issued may stay in flight; the prefetched
-            // loads were issued before them and must be complete
-            wait_vmcnt<VPT>();
+            // the stores just issued may stay in flight; the prefetched loads
+            // were issued before them and must be complete
+            if (finish) wait_vmcnt<VPT>(); else wait_vmcnt<0>();
 #pragma unroll
             for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
         }
-    }
-    // k = K: finish the last tile
+    };
+
+    // k = 0
+    load_tile(tile_of(0), cur);
+    wait_vmcnt<0>();
+    if (PREFETCH) load_tile(tile_of(1), nxt);
+    phase_a(cur, 0);
     __syncthreads();
-    phase_c(up, tile_of(K - 1), (K - 1) & 1);
+    phase_b(cur, up0);
+    if (PREFETCH) {
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
+    }
+    if (LAG == 1) {
+        for (int k = 1; k < K; ++k) step(k, up0, true);
+        __syncthreads();
+        phase_c(up0, tile_of(K - 1), (K - 1) & 1);
+    } else {
+        if (K > 1) step(1, up1, false);
+        int k = 2;
+        for (; k + 1 < K; k += 2) {
+            step(k, up0, true);
+            step(k + 1, up1, true);
+        }
+        if (k < K) {
+            step(k, up0, true);
+            ++k;
+        }
+        // k == K: finish the last two tiles (or the only one when K == 1)
+        if (K == 1) {
+            __syncthreads();
+            __syncthreads();
+            phase_c(up0, tile_of(0), 0);
+        } else if (K & 1) {
+            // tile K-2 is odd-indexed-parity 1 -> up1, tile K-1 -> up0
+            __syncthreads();
+            phase_c(up1, tile_of(K - 2), (K - 2) & 1);
+            __syncthreads();
+            phase_c(up0, tile_of(K - 1), (K - 1) & 1);
+        } else {
+            __syncthreads();
+            phase_c(up0, tile_of(K - 2), (K - 2) & 1);
+            __syncthreads();
+            phase_c(up1, tile_of(K - 1), (K - 1) & 1);
+        }
+    }
 }
 
 // ================================================================ split kernels

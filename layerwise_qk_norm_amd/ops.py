@@ -21,7 +21,7 @@ _lock = threading.Lock()
 QKN_OK, QKN_EINVAL, QKN_EOVERLAP, QKN_ENOMEM, QKN_EHIP = 0, -1, -2, -3, -4
 QKN_ERESIDENCY, QKN_ETIMEOUT, QKN_ECAPTURE = -5, -6, -7
 QKN_BF16, QKN_F32 = 0, 1
-NUM_VARIANTS = 6
+NUM_VARIANTS = 10
 MAX_DATA_WAVES = 15
 MAX_SHARDS = 32
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
@@ -68,6 +68,7 @@ _SIGS = {
     "qknorm_set_option": [_I, _I64],
     "qknorm_get_option": [_I],
     "qknorm_bench_copy": [_P, _P, _P, _P, _I64, _I64, _P],
+    "qknorm_bench_fused": [_I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _I, _P],
 }
 _RESTYPE = {"qknorm_strerror": ctypes.c_char_p, "qknorm_last_hip_error": ctypes.c_char_p,
             "qknorm_get_option": ctypes.c_int64}
@@ -140,6 +141,11 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _fused_fn(code: int):
+    L = lib()
+    return L.qknorm_layerwise_fwd_bf16 if code == QKN_BF16 else L.qknorm_layerwise_fwd_f32
+
+
 def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_q=None,
                   out_k=None):
     """Fused Q+K layerwise RMSNorm; returns ``(out_q, out_k)``."""
@@ -161,12 +167,15 @@ def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_
     _need(out_k, "out_k", 2, dt, dev)
     if out_q.shape != q.shape or out_k.shape != k.shape:
         raise ValueError("outputs must have the shapes of q and k")
-    code = _dtype_code(q)
-    fn = getattr(lib(), f"qknorm_layerwise_fwd_{_suffix(code)}")
-    with torch.cuda.device(dev):
-        _check(fn(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), T, Hq, Hk,
-                  n_shards, eps, out_q.data_ptr(), out_k.data_ptr(), _stream(dev)),
-               "qknorm_layerwise_fwd")
+    fn = _fused_fn(_dtype_code(q))
+    args = (q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), T, Hq, Hk,
+            n_shards, eps, out_q.data_ptr(), out_k.data_ptr())
+    if dev.index == torch.cuda.current_device():
+        status = fn(*args, torch.cuda.current_stream(dev).cuda_stream)
+    else:
+        with torch.cuda.device(dev):
+            status = fn(*args, _stream(dev))
+    _check(status, "qknorm_layerwise_fwd")
     return out_q, out_k
 
 
@@ -285,6 +294,17 @@ def bench_copy(q, k, out_q, out_k):
                                        out_k.data_ptr(), q.numel() * q.element_size(),
                                        k.numel() * k.element_size(), _stream(q.device)),
                "qknorm_bench_copy")
+
+
+def bench_fused(q, k, gamma_q, gamma_k, n_shards: int, eps: float, out_q, out_k, repeats: int):
+    """Issue ``repeats`` back-to-back fused calls from C (measurement helper)."""
+    T, Hq = q.shape
+    Hk = k.shape[1]
+    with torch.cuda.device(q.device):
+        _check(lib().qknorm_bench_fused(_dtype_code(q), q.data_ptr(), k.data_ptr(),
+                                        gamma_q.data_ptr(), gamma_k.data_ptr(), T, Hq, Hk,
+                                        n_shards, eps, out_q.data_ptr(), out_k.data_ptr(),
+                                        repeats, _stream(q.device)), "qknorm_bench_fused")
 
 
 def release_workspace():

@@ -202,3 +202,16 @@ def test_coresidency_query():
     props = torch.cuda.get_device_properties(0)
     assert n >= 2 and n % 1 == 0
     assert n <= props.multi_processor_count * 32
+
+
+def test_bench_helpers_compute_the_same():
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    q, k = to_dev(d["q"]), to_dev(d["k"])
+    gq, gk = to_dev(d["gamma_q"]), to_dev(d["gamma_k"])
+    ref = [to_host(t) for t in ops.layerwise_fwd(q, k, gq, gk, 4)]
+    oq, ok = torch.empty_like(q), torch.empty_like(k)
+    ops.bench_fused(q, k, gq, gk, 4, w.eps, oq, ok, 3)
+    assert np.array_equal(to_host(oq), ref[0]) and np.array_equal(to_host(ok), ref[1])
+    ops.bench_copy(q, k, oq, ok)
+    assert torch.equal(oq, q) and torch.equal(ok, k)

@@ -80,8 +80,11 @@ def device_workload(w, torch, sets=1):
     return d, gq, gk, bufs
 
 
-def cpu_baseline(w, d, budget_s=12.0):
-    """The fp64 oracle on the first rows of the workload, sized to ~budget_s."""
+def cpu_baseline(w, d, budget_s=10.0):
+    """The fp64 oracle on the workload's rows, sized to about budget_s of CPU time.
+
+    Rows are taken from the front of the batch; when one pass over every row takes less
+    than the budget, whole passes are repeated until it is spent."""
     from oracle import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     probe = min(w.T, 256)
@@ -90,15 +93,21 @@ def cpu_baseline(w, d, budget_s=12.0):
         oracle.rmsnorm(d[n][:probe], d["gamma_" + n], w.eps, threads=threads)
     per_row = (time.perf_counter() - t0) / probe
     rows = int(max(probe, min(w.T, budget_s / max(per_row, 1e-9))))
+    passes, sec = 0, 0.0
     t0 = time.perf_counter()
-    for n in ("q", "k"):
-        oracle.rmsnorm(d[n][:rows], d["gamma_" + n], w.eps, threads=threads)
-    sec = time.perf_counter() - t0
-    nbytes = w.with_T(rows).algorithmic_bytes()
+    while True:
+        for n in ("q", "k"):
+            oracle.rmsnorm(d[n][:rows], d["gamma_" + n], w.eps, threads=threads)
+        passes += 1
+        sec = time.perf_counter() - t0
+        if sec >= 0.8 * budget_s or rows < w.T:
+            break
+    nbytes = w.with_T(rows).algorithmic_bytes() * passes
+    what = f"all {w.T} tokens" if rows == w.T else f"first {rows} of {w.T} tokens"
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"first {rows} of {w.T} tokens of the prefill workload (Q and K, "
-                      f"fp64 C loops, rows split over {threads} threads), {sec:.2f} s"}
+            "sample": f"{passes} pass(es) over {what} of the prefill workload (Q and K, fp64 C "
+                      f"loops, rows split over {threads} threads), {sec:.2f} s"}
 
 
 def main():

@@ -837,7 +837,7 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k, in
     int dev = 0, cu = 0, rc = current_device(&dev);
     if (rc) return rc;
     QKN_HIP(hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev));
-    const int64_t blocks = std::max<int64_t>(1, (va + vb + 255) / 256);
+    const int64_t blocks = std::max<int64_t>(1, (va + 255) / 256 + (vb + 255) / 256);
     if (blocks > 0x7fffffff) return QKN_EINVAL;
     (void)cu;
     hipLaunchKernelGGL(qkn::copy2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, k, out_q,

@@ -571,12 +571,23 @@ __global__ void __launch_bounds__(256)
 copy2_kernel(const void* a, const void* b, void* oa, void* ob, int64_t va, int64_t vb,
              int64_t ta, int64_t tb)
 {
-    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (v < va) {
-        st_stream(static_cast<char*>(oa) + v * 16, ld_stream(static_cast<const char*>(a) + v * 16));
-    } else if (v < va + vb) {
-        const int64_t w = v - va;
-        st_stream(static_cast<char*>(ob) + w * 16, ld_stream(static_cast<const char*>(b) + w * 16));
+    // one 16-byte vector per thread through a descriptor covering this workgroup's
+    // 4 KiB, the access pattern of the fused kernel's streaming loads and stores
+    // workgroups [0, ceil(va/256)) copy a, the rest copy b
+    const int64_t ba = (va + 255) / 256;
+    const bool in_a = (int64_t)blockIdx.x < ba;
+    const int64_t w0 = ((int64_t)blockIdx.x - (in_a ? 0 : ba)) * 256;
+    const int64_t nv = in_a ? va : vb;
+    const int64_t left = nv - w0;
+    if (left > 0) {
+        const int nbytes = (int)((left < 256 ? left : 256) * 16);
+        const char* src = static_cast<const char*>(in_a ? a : b) + w0 * 16;
+        char* dst = static_cast<char*>(in_a ? oa : ob) + w0 * 16;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, nbytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, nbytes, 0x00020000);
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, threadIdx.x * 16, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128(x, rd, threadIdx.x * 16, 0, kNT);
     }
     if (blockIdx.x == 0) {
         for (int64_t i = threadIdx.x; i < ta; i += 256)

@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 output for the committed ``profiles/`` directory.
 
-``python -m layerwise_qk_norm_amd.profiling trace STATS_CSV OUT_TXT --cmd "..."``
-  writes the per-kernel duration table of a ``--kernel-trace --stats`` run.
+``python -m layerwise_qk_norm_amd.profiling trace STATS_CSV OUT_TXT --cmd "..."
+  [--kernel-trace TRACE_CSV --window KERNEL:START:COUNT]`` writes the per-kernel duration
+  table of a ``--kernel-trace --stats`` run and, with a window, the average over one
+  run of consecutive dispatches (the benchmark's timed steps, after its warmup).
 ``python -m layerwise_qk_norm_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_TXT --cmd-fetch
   "..." --cmd-write "..."`` writes HBM bytes per launch of the fused prefill kernel
   from two ``--pmc`` runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch). Each counter
@@ -38,7 +40,24 @@ def short(name: str) -> str:
     return name.replace("(qkn::FusedParams)", "").replace("void ", "")[:110]
 
 
-def summarize_trace(stats_csv: str, out_txt: str, cmd: str, note: str = ""):
+def window_stats(trace_csv: str, kernel: str, start: int, count: int):
+    """Durations of dispatches [start, start+count) of the kernel whose name contains
+    ``kernel``, from a ``--kernel-trace`` CSV (dispatch order = launch order)."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    sel = rows[start:start + count]
+    if len(sel) < count:
+        raise ValueError(f"only {len(rows)} dispatches of {kernel!r}")
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel]
+    st = [int(r["Start_Timestamp"]) for r in sel]
+    gap = [(st[i + 1] - st[i]) / 1e3 for i in range(len(st) - 1)]
+    return {"name": sel[0]["Kernel_Name"], "n": len(dur), "avg_us": statistics.mean(dur),
+            "min_us": min(dur), "max_us": max(dur),
+            "start_to_start_us": statistics.mean(gap) if gap else float("nan")}
+
+
+def summarize_trace(stats_csv: str, out_txt: str, cmd: str, note: str = "",
+                    trace_csv: str = "", window: str = ""):
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}",
              f"kernel_source_sha: {kernel_source_sha()}"]
@@ -49,6 +68,16 @@ def summarize_trace(stats_csv: str, out_txt: str, cmd: str, note: str = ""):
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} "
                      f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
                      f"{float(r['Percentage']):6.2f}  {short(r['Name'])}")
+    if trace_csv and window:
+        kernel, start, count = window.rsplit(":", 2)
+        w = window_stats(trace_csv, kernel, int(start), int(count))
+        lines += [f"# timed window: dispatches {start}..{int(start) + int(count) - 1} of "
+                  f"{short(w['name'])}",
+                  f"window_dispatches: {w['n']}",
+                  f"window_avg_us: {w['avg_us']:.3f}",
+                  f"window_min_us: {w['min_us']:.3f}",
+                  f"window_max_us: {w['max_us']:.3f}",
+                  f"window_start_to_start_us: {w['start_to_start_us']:.3f}"]
     open(out_txt, "w").write("\n".join(lines) + "\n")
 
 
@@ -104,6 +133,9 @@ def main():
     t.add_argument("out_txt")
     t.add_argument("--cmd", required=True)
     t.add_argument("--note", default="")
+    t.add_argument("--kernel-trace", default="", help="kernel trace CSV for --window")
+    t.add_argument("--window", default="",
+                   help="KERNEL_SUBSTRING:START:COUNT, dispatches averaged on their own")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_csv")
     f.add_argument("write_csv")
@@ -113,7 +145,7 @@ def main():
     f.add_argument("--algorithmic-bytes", type=int, default=671_109_120)
     a = ap.parse_args()
     if a.what == "trace":
-        summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note)
+        summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note, a.kernel_trace, a.window)
     else:
         summarize_traffic(a.fetch_csv, a.write_csv, a.out_txt, a.cmd_fetch, a.cmd_write,
                           a.algorithmic_bytes)

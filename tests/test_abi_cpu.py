@@ -13,8 +13,6 @@ from layerwise_qk_norm_amd import inputs, ops
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "qknorm.h")
-# plausible blocks-per-CU for the five fused variants on a 256-CU device
-BPC = [6, 3, 2, 1, 1]
 CU = 256
 
 
@@ -44,6 +42,17 @@ def test_strerror_and_options():
     with pytest.raises(ops.QKNormError):
         ops.set_option("force_variant", 99)
     assert ops.lib().qknorm_set_option(12345, 1) == ops.QKN_EINVAL
+
+
+def test_option_ids_match_header():
+    hdr = open(HEADER).read()
+    ids = {m.group(1).lower(): int(m.group(2))
+           for m in re.finditer(r"QKN_OPT_([A-Z_]+)\s*=\s*(\d+)", hdr)}
+    assert ids == ops.OPT
+    for n in ops.OPT:  # every option reads back what it was set to
+        v = ops.get_option(n)
+        ops.set_option(n, v)
+        assert ops.get_option(n) == v
 
 
 FAKE = [0x10000 * (i + 1) for i in range(6)]  # never dereferenced: rejected first

@@ -215,3 +215,9 @@ def test_bench_helpers_compute_the_same():
     assert np.array_equal(to_host(oq), ref[0]) and np.array_equal(to_host(ok), ref[1])
     ops.bench_copy(q, k, oq, ok)
     assert torch.equal(oq, q) and torch.equal(ok, k)
+    # sizes that end mid-workgroup and mid-vector
+    a = torch.randn(3, 1001, device="cuda:0").to(torch.bfloat16)
+    b = torch.randn(5, 777, device="cuda:0")
+    oa, ob = torch.zeros_like(a), torch.zeros_like(b)
+    ops.bench_copy(a, b, oa, ob)
+    assert torch.equal(oa, a) and torch.equal(ob, b)

@@ -24,8 +24,11 @@
  * Conventions for every entry point:
  *  - Tensors are device pointers, row-major [T][H] with row stride H
  *    elements, contiguous; gamma is [H]. bf16 means IEEE binary32 truncated
- *    to its upper 16 bits (stored as 16-bit words); f32 is IEEE binary32.
- *    The caller owns every tensor it passes.
+ *    to its upper 16 bits (stored as 16-bit words); f32 is IEEE binary32;
+ *    e4m3 is the OCP 8-bit floating point E4M3 encoding (one byte: sign,
+ *    4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111
+ *    is NaN; largest finite magnitude 448). The caller owns every tensor it
+ *    passes.
  *  - Calls are asynchronous and stream-ordered on `stream` (0 = the null
  *    stream of the current device); pointers must belong to the current
  *    device. Nothing is synchronised except where stated.
@@ -37,6 +40,9 @@
  *    QKN_EOVERLAP.
  *  - 16-byte aligned pointers with (H / n_shards) * elem_size a multiple of
  *    16 bytes take 128-bit memory paths; other layouts are still correct.
+ *  - Rounding to a 16-bit or 8-bit output is to nearest, ties to even. An
+ *    e4m3 output saturates magnitudes above 448 (infinities included) to
+ *    +-448 and keeps NaN.
  */
 #ifndef QKNORM_H
 #define QKNORM_H
@@ -62,7 +68,18 @@ typedef enum qknorm_status {
     QKN_ECAPTURE = -7    /* fused call issued on a stream under graph capture */
 } qknorm_status;
 
-typedef enum qknorm_dtype { QKN_BF16 = 0, QKN_F32 = 1 } qknorm_dtype;
+typedef enum qknorm_dtype { QKN_BF16 = 0, QKN_F32 = 1, QKN_E4M3 = 2 } qknorm_dtype;
+
+/* Formats of the fused and split kernels: input x / scale gamma / output y.
+ * The `dtype` argument of the planning, occupancy and measurement calls
+ * below is a format; formats 0 and 1 are QKN_BF16 and QKN_F32 throughout. */
+enum {
+    QKN_FMT_BF16 = 0,       /* bf16 / bf16 / bf16 */
+    QKN_FMT_F32 = 1,        /* f32 / f32 / f32 */
+    QKN_FMT_E4M3_BF16 = 2,  /* e4m3 / bf16 / bf16 */
+    QKN_FMT_E4M3_E4M3 = 3,  /* e4m3 / bf16 / e4m3 */
+    QKN_NUM_FORMATS = 4
+};
 
 #define QKN_MAX_SHARDS 32
 
@@ -91,6 +108,17 @@ int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q,
                              int n_shards, float eps, void* out_q, void* out_k,
                              hipStream_t stream);
 
+/* The same for FP8 activations (the letter's FP8-E4M3 evaluation, Section
+ * IV-C: FP32 accumulation for FP8-E4M3 inputs as for BF16): q and k are e4m3
+ * codes, gamma_q and gamma_k are bf16, and out_q / out_k are `out_dtype`
+ * (QKN_BF16 or QKN_E4M3; anything else is QKN_EINVAL). The 128-bit path
+ * needs H / n_shards to be a multiple of 16. In place (out aliasing the
+ * input) is only possible with out_dtype = QKN_E4M3. */
+int qknorm_layerwise_fwd_e4m3(const void* q, const void* k, const void* gamma_q,
+                              const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
+                              int n_shards, float eps, void* out_q, void* out_k,
+                              int out_dtype, hipStream_t stream);
+
 /* ------------------------------------------------------------------ split
  * The same computation for one tensor as three stream-ordered launches, with
  * the intermediate statistics in caller-owned device buffers (the unfused
@@ -103,18 +131,25 @@ int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q,
  *   1 / sqrt( (sum_{s=0}^{n_shards-1} partials[s*T+t]) / H + eps ), the sum in
  *   fp32 in ascending s. rms_inv is [T] fp32.
  * qknorm_apply_scale_*: Phases B (x*gamma) and C. out[t][j] =
- *   round(x[t][j] * gamma[j] * rms_inv[t]) in the suffix dtype.
+ *   round(x[t][j] * gamma[j] * rms_inv[t]) in the suffix dtype (for e4m3
+ *   inputs: in out_dtype, with gamma in bf16).
  */
 int qknorm_shard_sumsq_bf16(const void* x, int64_t T, int64_t H, int n_shards,
                             float* partials, hipStream_t stream);
 int qknorm_shard_sumsq_f32(const void* x, int64_t T, int64_t H, int n_shards,
                            float* partials, hipStream_t stream);
+int qknorm_shard_sumsq_e4m3(const void* x, int64_t T, int64_t H, int n_shards,
+                            float* partials, hipStream_t stream);
 int qknorm_combine_scale(const float* partials, int64_t T, int64_t H, int n_shards,
                          float eps, float* rms_inv, hipStream_t stream);
 int qknorm_apply_scale_bf16(const void* x, const void* gamma, const float* rms_inv,
                             int64_t T, int64_t H, void* out, hipStream_t stream);
 int qknorm_apply_scale_f32(const void* x, const void* gamma, const float* rms_inv,
                            int64_t T, int64_t H, void* out, hipStream_t stream);
+/* e4m3 x, bf16 gamma, out of `out_dtype` (QKN_BF16 or QKN_E4M3). */
+int qknorm_apply_scale_e4m3(const void* x, const void* gamma, const float* rms_inv,
+                            int64_t T, int64_t H, void* out, int out_dtype,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------ service */
 
@@ -130,11 +165,13 @@ const char* qknorm_strerror(int status);
 const char* qknorm_last_hip_error(void);
 
 /* Workgroups of the fused kernel that the current device can hold at once
- * for this dtype and shape (occupancy x compute units); *out receives it. */
+ * for this format (QKN_FMT_*) and shape (occupancy x compute units); *out
+ * receives it. */
 int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_shards,
                                      int* out);
 
-/* Occupancy of the current device: blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1)
+/* Occupancy of the current device for format `dtype` (QKN_FMT_*):
+ * blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1)
  * + w] = workgroups of fused variant v with w data waves that one compute
  * unit can hold (0 = not launchable), an array of QKN_NUM_VARIANTS x
  * (QKN_MAX_DATA_WAVES + 1) ints; *cu_count = compute units. Feeds
@@ -152,7 +189,9 @@ int qknorm_release_workspace(void);
  * real path queries the occupancy API). Variants 0-5 hold 1, 2, 3, 4, 6, 9
  * 16-byte vectors per data thread (5: fp32 only) and scale a tile one
  * iteration after reducing it; variants 6-9 hold 1, 2, 3, 4 and scale it two
- * iterations later, which decouples the shards of a group further. */
+ * iterations later, which decouples the shards of a group further. The e4m3
+ * formats have variants 0, 1, 2, 6 and 7 (a 16-byte vector is 16 columns).
+ * `dtype` is a format (QKN_FMT_*). */
 #define QKN_NUM_VARIANTS 10
 #define QKN_MAX_DATA_WAVES 15
 typedef struct qknorm_plan {
@@ -195,7 +234,7 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
                       int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
 
 /* Measurement helper: issues `repeats` back-to-back fused calls with the same
- * arguments (as qknorm_layerwise_fwd_<dtype>, dtype = QKN_BF16 or QKN_F32)
+ * arguments (as the fused entry point of format `dtype`, a QKN_FMT_* value)
  * from C, so that launch-rate-bound shapes can be timed without a host
  * language's per-call overhead. Returns the first non-OK status. */
 int qknorm_bench_fused(int dtype, const void* q, const void* k, const void* gamma_q,

@@ -24,34 +24,64 @@
 namespace {
 
 using qkn::Bf16;
+using qkn::E4m3Bf16;
+using qkn::E4m3E4m3;
 using qkn::F32;
 using qkn::FusedParams;
 
+// ---------------------------------------------------------------- formats
+
+// Element sizes of x, gamma and y of a format; `ev` columns per 16-byte
+// vector of x, `kgam` 16-byte words of gamma per vector.
+struct Fmt {
+    int in, gam, out, ev, kgam;
+};
+bool fmt_valid(int f) { return f >= 0 && f < QKN_NUM_FORMATS; }
+Fmt fmt_of(int f)
+{
+    switch (f) {
+    case QKN_FMT_BF16: return {2, 2, 2, 8, 1};
+    case QKN_FMT_F32: return {4, 4, 4, 4, 1};
+    case QKN_FMT_E4M3_BF16: return {1, 2, 2, 16, 2};
+    default: return {1, 2, 1, 16, 2};  // QKN_FMT_E4M3_E4M3
+    }
+}
+// format of an E4M3 call with output dtype `out` (QKN_BF16 or QKN_E4M3), or -1
+int e4m3_fmt(int out)
+{
+    if (out == QKN_BF16) return QKN_FMT_E4M3_BF16;
+    if (out == QKN_E4M3) return QKN_FMT_E4M3_E4M3;
+    return -1;
+}
+
 // ---------------------------------------------------------------- variants
 
+// Which formats instantiate a variant is decided by fused_fn_for below.
 struct Variant {
     int vpt;          // 16-byte slots per data thread
     bool prefetch;    // next tile loaded during the exchange
-    bool f32_only;    // register budget only fits fp32 (no prefetch buffer)
     int lag;          // tiles between a tile's reduction and its scaling
     int max_threads;  // launch bound of the instantiation
 };
 constexpr Variant kVariants[QKN_NUM_VARIANTS] = {
-    {1, true, false, 1, 1024},
-    {2, true, false, 1, 1024},
-    {3, true, false, 1, 1024},
-    {4, true, false, 1, 1024},
-    {6, true, false, 1, 768},
-    {9, false, true, 1, 1024},
-    {1, true, false, 2, 1024},
-    {2, true, false, 2, 1024},
-    {3, true, false, 2, 768},
-    {4, true, false, 2, 512},
+    {1, true, 1, 1024},
+    {2, true, 1, 1024},
+    {3, true, 1, 1024},
+    {4, true, 1, 1024},
+    {6, true, 1, 768},
+    {9, false, 1, 1024},  // fp32 only: no room for a prefetch buffer
+    {1, true, 2, 1024},
+    {2, true, 2, 1024},
+    {3, true, 2, 768},
+    {4, true, 2, 512},
 };
-int max_data_waves(int v) { return kVariants[v].max_threads / 64 - 1; }
 
 using FusedFn = void (*)(FusedParams);
 
+// Instantiated variants per format. The 16-byte formats (bf16, fp32) have all
+// but variant 5 (fp32 only); E4M3 vectors hold 16 columns, so their u
+// registers double and only variants with up to 3 vectors per thread (lag 1)
+// or 2 (lag 2) are instantiated.
 template <class DT>
 FusedFn fused_fn(int v)
 {
@@ -85,10 +115,43 @@ FusedFn fused_fn<F32>(int v)
     default: return nullptr;
     }
 }
-FusedFn fused_fn_for(int dtype, int v) { return dtype == QKN_BF16 ? fused_fn<Bf16>(v) : fused_fn<F32>(v); }
+// E4M3 launch bounds: variants 2 and 7 need more registers than 1024 threads allow
+constexpr int kE4m3MaxThreads[QKN_NUM_VARIANTS] = {1024, 1024, 768, 0, 0, 0, 1024, 768, 0, 0};
+template <class DT>
+FusedFn fused_fn_e4m3(int v)
+{
+    switch (v) {
+    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1, kE4m3MaxThreads[0]>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1, kE4m3MaxThreads[1]>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1, kE4m3MaxThreads[2]>;
+    case 6: return qkn::fused_qknorm_kernel<DT, 1, true, 2, kE4m3MaxThreads[6]>;
+    case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, kE4m3MaxThreads[7]>;
+    default: return nullptr;
+    }
+}
+FusedFn fused_fn_for(int fmt, int v)
+{
+    switch (fmt) {
+    case QKN_FMT_BF16: return fused_fn<Bf16>(v);
+    case QKN_FMT_F32: return fused_fn<F32>(v);
+    case QKN_FMT_E4M3_BF16: return fused_fn_e4m3<E4m3Bf16>(v);
+    default: return fused_fn_e4m3<E4m3E4m3>(v);
+    }
+}
+bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
+bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
+// data waves a workgroup of variant v may have (launch bound / 64, minus the comm wave)
+int max_data_waves(int fmt, int v)
+{
+    const int t = is_e4m3(fmt) ? kE4m3MaxThreads[v] : kVariants[v].max_threads;
+    return t / 64 - 1;
+}
 
-// dynamic LDS of a launch: gamma in slot order
-size_t gamma_lds_bytes(int v, int nwd) { return (size_t)kVariants[v].vpt * 64 * nwd * 16; }
+// dynamic LDS of a launch: gamma in slot order (kgam 16-byte words per slot)
+size_t gamma_lds_bytes(int fmt, int v, int nwd)
+{
+    return (size_t)kVariants[v].vpt * 64 * nwd * 16 * fmt_of(fmt).kgam;
+}
 
 // ---------------------------------------------------------------- options
 
@@ -139,8 +202,8 @@ int hip_fail(hipError_t e, const char* what)
 struct DevInfo {
     int cu = 0;
     int wall_khz = 0;
-    bool occ_done[2] = {false, false};
-    int occ[2][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
+    bool occ_done[QKN_NUM_FORMATS] = {};
+    int occ[QKN_NUM_FORMATS][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
 };
 
 std::mutex g_mu;
@@ -157,18 +220,18 @@ int device_info(int dev, int dtype, DevInfo** out)
     if (!d.occ_done[dtype]) {
         for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
             FusedFn fn = fused_fn_for(dtype, v);
-            const bool usable = fn && !(kVariants[v].f32_only && dtype != QKN_F32);
+            const bool usable = fn != nullptr;
             if (usable) {
-                const size_t max_lds = gamma_lds_bytes(v, max_data_waves(v));
+                const size_t max_lds = gamma_lds_bytes(dtype, v, max_data_waves(dtype, v));
                 QKN_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                             hipFuncAttributeMaxDynamicSharedMemorySize,
                                             (int)max_lds));
             }
             for (int w = 0; w <= QKN_MAX_DATA_WAVES; ++w) {
                 int n = 0;
-                if (usable && w >= 1 && w <= max_data_waves(v)) {
+                if (usable && w >= 1 && w <= max_data_waves(dtype, v)) {
                     QKN_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &n, reinterpret_cast<const void*>(fn), 64 * (w + 1), gamma_lds_bytes(v, w)));
+                        &n, reinterpret_cast<const void*>(fn), 64 * (w + 1), gamma_lds_bytes(dtype, v, w)));
                 }
                 d.occ[dtype][v][w] = n;
             }
@@ -265,7 +328,6 @@ int check_dims(int64_t T, int64_t H, int n_shards)
 }
 bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.f; }
 
-int elem_size(int dtype) { return dtype == QKN_BF16 ? 2 : 4; }
 
 int current_device(int* dev)
 {
@@ -282,15 +344,14 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
 {
     std::memset(out, 0, sizeof *out);
     out->variant = -1;
-    if (dtype != QKN_BF16 && dtype != QKN_F32) return QKN_EINVAL;
+    if (!fmt_valid(dtype)) return QKN_EINVAL;
     int rc = check_dims(T, Hq, N);
     if (rc) return rc;
     rc = check_dims(T, Hk, N);
     if (rc) return rc;
     if (cu < 1 || !bpc) return QKN_EINVAL;
     if (T == 0) return QKN_OK;
-    const int es = elem_size(dtype);
-    const int ev = 16 / es;
+    const int ev = fmt_of(dtype).ev;
     const int64_t Wq = Hq / N, Wk = Hk / N;
     if (!aligned || Wq % ev || Wk % ev || g_opt.force_split) return QKN_OK;  // split kernels
     const int64_t wvq = Wq / ev, wvk = Wk / ev;
@@ -312,13 +373,14 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // With peers to wait for, the two-tile lag decouples partners; a lag-1
     // variant is used only where no lag-2 variant holds the same slots.
     auto has_lag2 = [&](int vpt) {
-        for (const Variant& x : kVariants)
-            if (x.lag == 2 && x.vpt == vpt) return true;
+        for (int v = 0; v < QKN_NUM_VARIANTS; ++v)
+            if (kVariants[v].lag == 2 && kVariants[v].vpt == vpt && variant_usable(dtype, v))
+                return true;
         return false;
     };
     auto allowed = [&](int v) {
         const Variant& k = kVariants[v];
-        if (k.f32_only && dtype != QKN_F32) return false;
+        if (!variant_usable(dtype, v)) return false;
         if (g_opt.force_variant >= 0) return v == g_opt.force_variant;
         if (N == 1) return k.lag == 1;
         return k.lag == 2 || !has_lag2(k.vpt);
@@ -328,7 +390,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     auto consider = [&](int v, int w, int r, int wpc) {
         const Variant& k = kVariants[v];
         const int64_t tv = tile_vectors(r);
-        if (w < 1 || w > max_data_waves(v) || (int64_t)64 * w * k.vpt < tv) return;
+        if (w < 1 || w > max_data_waves(dtype, v) || (int64_t)64 * w * k.vpt < tv) return;
         const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
         if (b <= 0 || wpc > b || (int64_t)b * cu < N) return;
         const int64_t tiles = (T + r - 1) / r;
@@ -386,7 +448,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
                     if (g_opt.force_data_waves < w) continue;
                     w = (int)g_opt.force_data_waves;
                 }
-                if (w < 1 || w > max_data_waves(v)) continue;
+                if (w < 1 || w > max_data_waves(dtype, v)) continue;
                 const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
                 const int64_t tiles = (T + r - 1) / r;
                 for (int wpc = 1; wpc <= b; ++wpc) {
@@ -401,9 +463,9 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         // but not N co-resident workgroups; otherwise the split kernels
         for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
             const Variant& k = kVariants[v];
-            if (k.f32_only && dtype != QKN_F32) continue;
+            if (!variant_usable(dtype, v)) continue;
             const int w = (int)((tile_vectors(1) + 64 * k.vpt - 1) / (64 * k.vpt));
-            if (w >= 1 && w <= max_data_waves(v) && bpc[v * (QKN_MAX_DATA_WAVES + 1) + w] > 0 &&
+            if (w >= 1 && w <= max_data_waves(dtype, v) && bpc[v * (QKN_MAX_DATA_WAVES + 1) + w] > 0 &&
                 (int64_t)bpc[v * (QKN_MAX_DATA_WAVES + 1) + w] * cu < N)
                 return QKN_ERESIDENCY;
         }
@@ -434,21 +496,28 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
 
 // ---------------------------------------------------------------- split launches
 
-int launch_sumsq(int dtype, const void* x, int64_t T, int64_t H, int N, float* partials,
+template <class DT>
+void launch_sumsq_as(bool vec, dim3 g, dim3 b, hipStream_t s, const void* x, int64_t T, int H, int N,
+                     float* partials)
+{
+    if (vec) hipLaunchKernelGGL((qkn::shard_sumsq_kernel<DT, true>), g, b, 0, s, x, T, H, N, partials);
+    else hipLaunchKernelGGL((qkn::shard_sumsq_kernel<DT, false>), g, b, 0, s, x, T, H, N, partials);
+}
+
+// fmt: any format whose input is x's format (only the input format matters)
+int launch_sumsq(int fmt, const void* x, int64_t T, int64_t H, int N, float* partials,
                  hipStream_t s)
 {
     const int64_t items = T * N;
     const int64_t blocks = (items + 3) / 4;
     if (blocks > 0x7fffffff) return QKN_EINVAL;
     const int W = (int)(H / N);
-    const bool vec = aligned16(x) && (W * elem_size(dtype)) % 16 == 0;
+    const bool vec = aligned16(x) && ((int64_t)W * fmt_of(fmt).in) % 16 == 0;
     dim3 g((unsigned)blocks), b(256);
-    if (dtype == QKN_BF16) {
-        if (vec) hipLaunchKernelGGL((qkn::shard_sumsq_kernel<Bf16, true>), g, b, 0, s, x, T, (int)H, N, partials);
-        else hipLaunchKernelGGL((qkn::shard_sumsq_kernel<Bf16, false>), g, b, 0, s, x, T, (int)H, N, partials);
-    } else {
-        if (vec) hipLaunchKernelGGL((qkn::shard_sumsq_kernel<F32, true>), g, b, 0, s, x, T, (int)H, N, partials);
-        else hipLaunchKernelGGL((qkn::shard_sumsq_kernel<F32, false>), g, b, 0, s, x, T, (int)H, N, partials);
+    switch (fmt) {
+    case QKN_FMT_BF16: launch_sumsq_as<Bf16>(vec, g, b, s, x, T, (int)H, N, partials); break;
+    case QKN_FMT_F32: launch_sumsq_as<F32>(vec, g, b, s, x, T, (int)H, N, partials); break;
+    default: launch_sumsq_as<E4m3Bf16>(vec, g, b, s, x, T, (int)H, N, partials); break;
     }
     QKN_HIP(hipGetLastError());
     return QKN_OK;
@@ -465,22 +534,31 @@ int launch_combine(const float* partials, int64_t T, int64_t H, int N, float eps
     return QKN_OK;
 }
 
-int launch_apply(int dtype, const void* x, const void* g, const float* rinv, int64_t T, int64_t H,
+template <class DT>
+void launch_apply_as(bool vec, dim3 gr, dim3 b, hipStream_t s, const void* x, const void* g,
+                     const float* rinv, int64_t T, int H, int rpb, void* y)
+{
+    if (vec) hipLaunchKernelGGL((qkn::apply_scale_kernel<DT, true>), gr, b, 0, s, x, g, rinv, T, H, rpb, y);
+    else hipLaunchKernelGGL((qkn::apply_scale_kernel<DT, false>), gr, b, 0, s, x, g, rinv, T, H, rpb, y);
+}
+
+int launch_apply(int fmt, const void* x, const void* g, const float* rinv, int64_t T, int64_t H,
                  void* y, hipStream_t s)
 {
-    const int es = elem_size(dtype);
-    const bool vec = aligned16(x) && aligned16(g) && aligned16(y) && (H * es) % 16 == 0;
-    const int64_t per_row = vec ? H * es / 16 : H;
+    const Fmt f = fmt_of(fmt);
+    // 16-byte paths need every row of x to be whole vectors (then gamma's and
+    // y's rows are whole 16-byte words too: their elements are at least as wide)
+    const bool vec = aligned16(x) && aligned16(g) && aligned16(y) && (H * f.in) % 16 == 0;
+    const int64_t per_row = vec ? H * f.in / 16 : H;
     const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, 2048 / per_row));
     const int64_t blocks = (T + rpb - 1) / rpb;
     if (blocks > 0x7fffffff) return QKN_EINVAL;
     dim3 gr((unsigned)blocks), b(256);
-    if (dtype == QKN_BF16) {
-        if (vec) hipLaunchKernelGGL((qkn::apply_scale_kernel<Bf16, true>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
-        else hipLaunchKernelGGL((qkn::apply_scale_kernel<Bf16, false>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
-    } else {
-        if (vec) hipLaunchKernelGGL((qkn::apply_scale_kernel<F32, true>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
-        else hipLaunchKernelGGL((qkn::apply_scale_kernel<F32, false>), gr, b, 0, s, x, g, rinv, T, (int)H, rpb, y);
+    switch (fmt) {
+    case QKN_FMT_BF16: launch_apply_as<Bf16>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
+    case QKN_FMT_F32: launch_apply_as<F32>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
+    case QKN_FMT_E4M3_BF16: launch_apply_as<E4m3Bf16>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
+    default: launch_apply_as<E4m3E4m3>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
     }
     QKN_HIP(hipGetLastError());
     return QKN_OK;
@@ -499,11 +577,12 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     if (!eps_ok(eps)) return QKN_EINVAL;
     if (T == 0) return QKN_OK;
     if (!q || !k || !gq || !gk || !oq || !ok) return QKN_EINVAL;
-    const int es = elem_size(dtype);
-    const Range rq = range_of(q, T * Hq * es), rk = range_of(k, T * Hk * es);
-    const Range rgq = range_of(gq, Hq * es), rgk = range_of(gk, Hk * es);
-    const Range roq = range_of(oq, T * Hq * es), rok = range_of(ok, T * Hk * es);
+    const Fmt f = fmt_of(dtype);
+    const Range rq = range_of(q, T * Hq * f.in), rk = range_of(k, T * Hk * f.in);
+    const Range rgq = range_of(gq, Hq * f.gam), rgk = range_of(gk, Hk * f.gam);
+    const Range roq = range_of(oq, T * Hq * f.out), rok = range_of(ok, T * Hk * f.out);
     if (overlaps(roq, rok)) return QKN_EOVERLAP;
+    // in place needs the output to occupy exactly the input's bytes (same element size)
     if (overlaps(roq, rq) && !same(roq, rq)) return QKN_EOVERLAP;
     if (overlaps(rok, rk) && !same(rok, rk)) return QKN_EOVERLAP;
     if (overlaps(roq, rk) || overlaps(roq, rgq) || overlaps(roq, rgk)) return QKN_EOVERLAP;
@@ -574,9 +653,8 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     p.n_tiles = pl.n_tiles;
     p.H[0] = (int32_t)Hq;
     p.H[1] = (int32_t)Hk;
-    const int ev = 16 / es;
-    p.Wv[0] = (int32_t)(Hq / N / ev);
-    p.Wv[1] = (int32_t)(Hk / N / ev);
+    p.Wv[0] = (int32_t)(Hq / N / f.ev);
+    p.Wv[1] = (int32_t)(Hk / N / f.ev);
     p.rows = pl.rows;
     p.nwd = pl.data_waves;
     p.n_shards = N;
@@ -592,7 +670,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     ws->tag_base += (uint32_t)pl.iters;
 
     FusedFn fn = fused_fn_for(dtype, pl.variant);
-    const size_t lds = gamma_lds_bytes(pl.variant, pl.data_waves);
+    const size_t lds = gamma_lds_bytes(dtype, pl.variant, pl.data_waves);
     if (g_opt.cooperative) {
         void* args[] = {&p};
         QKN_HIP(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(pl.grid),
@@ -612,8 +690,8 @@ int shard_sumsq(int dtype, const void* x, int64_t T, int64_t H, int N, float* pa
     if (rc) return rc;
     if (T == 0) return QKN_OK;
     if (!x || !partials) return QKN_EINVAL;
-    const int es = elem_size(dtype);
-    if (overlaps(range_of(partials, (int64_t)N * T * 4), range_of(x, T * H * es))) return QKN_EOVERLAP;
+    if (overlaps(range_of(partials, (int64_t)N * T * 4), range_of(x, T * H * fmt_of(dtype).in)))
+        return QKN_EOVERLAP;
     return launch_sumsq(dtype, x, T, H, N, partials, s);
 }
 
@@ -625,10 +703,10 @@ int apply_scale(int dtype, const void* x, const void* g, const float* rinv, int6
     if (rc) return rc;
     if (T == 0) return QKN_OK;
     if (!x || !g || !rinv || !y) return QKN_EINVAL;
-    const int es = elem_size(dtype);
-    const Range ry = range_of(y, T * H * es), rx = range_of(x, T * H * es);
+    const Fmt f = fmt_of(dtype);
+    const Range ry = range_of(y, T * H * f.out), rx = range_of(x, T * H * f.in);
     if (overlaps(ry, rx) && !same(ry, rx)) return QKN_EOVERLAP;
-    if (overlaps(ry, range_of(g, H * es)) || overlaps(ry, range_of(rinv, T * 4))) return QKN_EOVERLAP;
+    if (overlaps(ry, range_of(g, H * f.gam)) || overlaps(ry, range_of(rinv, T * 4))) return QKN_EOVERLAP;
     return launch_apply(dtype, x, g, rinv, T, H, y, s);
 }
 
@@ -654,10 +732,26 @@ int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q, 
                          stream);
 }
 
+int qknorm_layerwise_fwd_e4m3(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
+                              int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
+                              void* out_q, void* out_k, int out_dtype, hipStream_t stream)
+{
+    const int fmt = e4m3_fmt(out_dtype);
+    if (fmt < 0) return QKN_EINVAL;
+    return layerwise_fwd(fmt, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps, out_q, out_k,
+                         stream);
+}
+
 int qknorm_shard_sumsq_bf16(const void* x, int64_t T, int64_t H, int n_shards, float* partials,
                             hipStream_t stream)
 {
     return shard_sumsq(QKN_BF16, x, T, H, n_shards, partials, stream);
+}
+
+int qknorm_shard_sumsq_e4m3(const void* x, int64_t T, int64_t H, int n_shards, float* partials,
+                            hipStream_t stream)
+{
+    return shard_sumsq(QKN_FMT_E4M3_BF16, x, T, H, n_shards, partials, stream);
 }
 
 int qknorm_shard_sumsq_f32(const void* x, int64_t T, int64_t H, int n_shards, float* partials,
@@ -690,6 +784,14 @@ int qknorm_apply_scale_f32(const void* x, const void* gamma, const float* rms_in
                            int64_t H, void* out, hipStream_t stream)
 {
     return apply_scale(QKN_F32, x, gamma, rms_inv, T, H, out, stream);
+}
+
+int qknorm_apply_scale_e4m3(const void* x, const void* gamma, const float* rms_inv, int64_t T,
+                            int64_t H, void* out, int out_dtype, hipStream_t stream)
+{
+    const int fmt = e4m3_fmt(out_dtype);
+    if (fmt < 0) return QKN_EINVAL;
+    return apply_scale(fmt, x, gamma, rms_inv, T, H, out, stream);
 }
 
 int qknorm_check_fault(hipStream_t stream)
@@ -733,7 +835,7 @@ const char* qknorm_last_hip_error(void) { return t_hip_error.c_str(); }
 int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_shards, int* out)
 {
     t_hip_error.clear();
-    if (!out || (dtype != QKN_BF16 && dtype != QKN_F32)) return QKN_EINVAL;
+    if (!out || !fmt_valid(dtype)) return QKN_EINVAL;
     std::lock_guard<std::mutex> lock(g_mu);
     int dev = 0, rc = current_device(&dev);
     if (rc) return rc;
@@ -748,7 +850,7 @@ int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_sh
 int qknorm_device_occupancy(int dtype, int* blocks_per_cu, int* cu_count)
 {
     t_hip_error.clear();
-    if (!blocks_per_cu || !cu_count || (dtype != QKN_BF16 && dtype != QKN_F32)) return QKN_EINVAL;
+    if (!blocks_per_cu || !cu_count || !fmt_valid(dtype)) return QKN_EINVAL;
     std::lock_guard<std::mutex> lock(g_mu);
     int dev = 0, rc = current_device(&dev);
     if (rc) return rc;
@@ -850,7 +952,7 @@ int qknorm_bench_fused(int dtype, const void* q, const void* k, const void* gamm
                        const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
                        float eps, void* out_q, void* out_k, int repeats, hipStream_t stream)
 {
-    if (dtype != QKN_BF16 && dtype != QKN_F32) return QKN_EINVAL;
+    if (!fmt_valid(dtype)) return QKN_EINVAL;
     if (repeats < 0) return QKN_EINVAL;
     for (int i = 0; i < repeats; ++i) {
         const int rc = layerwise_fwd(dtype, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps,

@@ -16,15 +16,38 @@ namespace qkn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Element formats. A "vector" is one 16-byte memory access.
+// Formats: element types of the input x, the scale gamma and the output y.
+// A "vector" is one 16-byte load of x; it covers kVec columns, whose gamma
+// occupies kGam 16-byte words and whose output occupies kOut 16-byte words.
+// E4M3 is the OCP 8-bit floating point E4M3 encoding (bias 7, no infinities,
+// S.1111.111 = NaN, largest finite 448); the letter evaluates FP8-E4M3
+// activations next to BF16, accumulating in FP32 for both ("SwiftQK",
+// Section IV-C). With E4M3 activations gamma is bf16.
 struct Bf16 {
-    using elem_t = uint16_t;
-    static constexpr int kVec = 8;
+    using in_t = uint16_t;
+    using gam_t = uint16_t;
+    using out_t = uint16_t;
+    static constexpr int kVec = 8, kGam = 1, kOut = 1;
 };
 struct F32 {
-    using elem_t = float;
-    static constexpr int kVec = 4;
+    using in_t = float;
+    using gam_t = float;
+    using out_t = float;
+    static constexpr int kVec = 4, kGam = 1, kOut = 1;
 };
+struct E4m3Bf16 {  // E4M3 in, bf16 out
+    using in_t = uint8_t;
+    using gam_t = uint16_t;
+    using out_t = uint16_t;
+    static constexpr int kVec = 16, kGam = 2, kOut = 2;
+};
+struct E4m3E4m3 {  // E4M3 in, E4M3 out
+    using in_t = uint8_t;
+    using gam_t = uint16_t;
+    using out_t = uint8_t;
+    static constexpr int kVec = 16, kGam = 2, kOut = 1;
+};
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- conversions
 
@@ -65,14 +88,78 @@ __device__ __forceinline__ u32x4 pack(F32, const float* f)
     return v;
 }
 
+// E4M3 -> fp32 (exact) with the hardware converter: the 16 codes of a
+// vector, lowest-addressed byte first (each dword holds 4 codes; word select
+// picks bytes 0-1 or 2-3).
+__device__ __forceinline__ void unpack_e4m3(const u32x4& v, float* f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
+        f[4 * i] = lo.x;
+        f[4 * i + 1] = lo.y;
+        f[4 * i + 2] = hi.x;
+        f[4 * i + 3] = hi.y;
+    }
+}
+__device__ __forceinline__ void unpack(E4m3Bf16, const u32x4& v, float* f) { unpack_e4m3(v, f); }
+__device__ __forceinline__ void unpack(E4m3E4m3, const u32x4& v, float* f) { unpack_e4m3(v, f); }
+
+// fp32 -> E4M3: round to nearest even by the hardware converter, after
+// saturating magnitudes above 448 (infinities included) to +-448; NaN stays
+// NaN (the comparison is false for it).
+__device__ __forceinline__ float sat_e4m3(float v)
+{
+    return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+}
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
+{
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);  // bytes 0-1
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), r, true);       // bytes 2-3
+    return (uint32_t)r;
+}
+
+// gamma of one vector's columns (kGam words) -> fp32
+template <class F>
+__device__ __forceinline__ void unpack_gamma(F, const u32x4* g, float* f)
+{
+    if constexpr (sizeof(typename F::gam_t) == 4) {
+        unpack(F32{}, g[0], f);
+    } else {
+#pragma unroll
+        for (int w = 0; w < F::kGam; ++w) unpack(Bf16{}, g[w], f + 8 * w);
+    }
+}
+// outputs of one vector's columns -> kOut words
+template <class F>
+__device__ __forceinline__ void pack_out(F, const float* f, u32x4* o)
+{
+    if constexpr (sizeof(typename F::out_t) == 4) {
+        o[0] = pack(F32{}, f);
+    } else if constexpr (sizeof(typename F::out_t) == 2) {
+#pragma unroll
+        for (int w = 0; w < F::kOut; ++w) o[w] = pack(Bf16{}, f + 8 * w);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[0][i] = pack_e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+    }
+}
+
 __device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint8_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 __device__ __forceinline__ void from_f32(float v, uint16_t* p)
 {
     __bf16 a = (__bf16)v;
     *p = __builtin_bit_cast(uint16_t, a);
 }
 __device__ __forceinline__ void from_f32(float v, float* p) { *p = v; }
+__device__ __forceinline__ void from_f32(float v, uint8_t* p)
+{
+    *p = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v), 0.0f, 0, false) & 0xff);
+}
 
 // ---------------------------------------------------------------- memory
 
@@ -189,12 +276,15 @@ template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT>
 __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
-    using elem_t = typename DT::elem_t;
+    using in_t = typename DT::in_t;
+    using gam_t = typename DT::gam_t;
     constexpr int EV = DT::kVec;
+    constexpr int KG = DT::kGam;
+    constexpr int KO = DT::kOut;
 
     __shared__ float red[2][kMaxDataWaves][kMaxSeg];  // per-wave partial sums, by tile parity
     __shared__ float rinv_s[2][kMaxSeg];              // combined reciprocal RMS, by tile parity
-    extern __shared__ u32x4 gam_lds[];                // gamma in slot order
+    extern __shared__ u32x4 gam_lds[];                // gamma in slot order, KG words per slot
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -304,11 +394,13 @@ fused_qknorm_kernel(FusedParams p)
     const int VQp = (VQ + 63) & ~63;  // K starts on a wave boundary
     const int V = VQp + rows * p.Wv[1];
     constexpr uint32_t kOOB = 0x7ffffff0u;
-    constexpr int ES = (int)sizeof(elem_t);
+    constexpr int ES = (int)sizeof(in_t);
+    constexpr int OS = (int)sizeof(typename DT::out_t);
 
     // Static per-slot layout (identical for every tile). tensor is uniform per
     // (wave, slot) because Q's part is padded to whole waves.
-    uint32_t voff[VPT];  // byte offset from the tile's first row, or kOOB
+    uint32_t voff[VPT];  // input byte offset from the tile's first row, or kOOB
+    uint32_t ooff[VPT];  // output byte offset (equal to voff when ES == OS)
     int seg[VPT];        // segment: tensor * rows + row
     bool tk[VPT];        // slot belongs to K (wave-uniform)
 #pragma unroll
@@ -331,24 +423,29 @@ fused_qknorm_kernel(FusedParams p)
         const int col = (shard * p.Wv[t] + c) * EV;
         tk[i] = t != 0;
         voff[i] = valid ? (uint32_t)((r * p.H[t] + col) * ES) : kOOB;
+        ooff[i] = ES == OS ? voff[i] : (valid ? (uint32_t)((r * p.H[t] + col) * OS) : kOOB);
         seg[i] = valid ? t * rows + r : 0;
-        gam_lds[i * ndt + dt] =
-            valid ? ld_cached(static_cast<const elem_t*>(p.gamma[t]) + col) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int g = 0; g < KG; ++g)
+            gam_lds[(i * ndt + dt) * KG + g] =
+                valid ? ld_cached(static_cast<const gam_t*>(p.gamma[t]) + col + g * (16 / (int)sizeof(gam_t)))
+                      : u32x4{0, 0, 0, 0};
     }
 
     auto tile_of = [&](int k) __attribute__((always_inline)) -> int64_t { return group + (int64_t)k * p.n_groups; };
-    auto rsrc = [&](const void* base, int t, int64_t t0) __attribute__((always_inline)) {
+    // descriptor of a tile's rows of one tensor, elements of `eb` bytes
+    auto rsrc = [&](const void* base, int t, int64_t t0, int eb) __attribute__((always_inline)) {
         // rows of this tile that exist; 0 past the end (then every access is out of range)
         const int64_t left = p.T - t0;
         const int vr = left <= 0 ? 0 : (left < rows ? (int)left : rows);
-        const char* b = static_cast<const char*>(base) + t0 * p.H[t] * ES;
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, vr * p.H[t] * ES,
+        const char* b = static_cast<const char*>(base) + t0 * p.H[t] * eb;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, vr * p.H[t] * eb,
                                                  0x00020000);
     };
     auto load_tile = [&](int64_t tile, u32x4 (&buf)[VPT]) __attribute__((always_inline)) {
         const int64_t t0 = tile * rows;
-        const __amdgpu_buffer_rsrc_t rq = rsrc(p.x[0], 0, t0);
-        const __amdgpu_buffer_rsrc_t rk = rsrc(p.x[1], 1, t0);
+        const __amdgpu_buffer_rsrc_t rq = rsrc(p.x[0], 0, t0, ES);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(p.x[1], 1, t0, ES);
 #pragma unroll
         for (int i = 0; i < VPT; ++i)
             buf[i] = __builtin_amdgcn_raw_buffer_load_b128(tk[i] ? rk : rq, voff[i], 0, kNT);
@@ -382,7 +479,7 @@ fused_qknorm_kernel(FusedParams p)
         for (int i = 0; i < VPT; ++i) {
             float f[EV], g[EV];
             unpack(DT{}, buf[i], f);
-            unpack(DT{}, gam_lds[i * ndt + dt], g);
+            unpack_gamma(DT{}, &gam_lds[(i * ndt + dt) * KG], g);
 #pragma unroll
             for (int e = 0; e < EV; ++e) u[i][e] = f[e] * g[e];
         }
@@ -390,15 +487,19 @@ fused_qknorm_kernel(FusedParams p)
     // ---- Phase C: y = u * rinv, one rounding to the output format, stored
     auto phase_c = [&](const float (&u)[VPT][EV], int64_t tile, int par) __attribute__((always_inline)) {
         const int64_t t0 = tile * rows;
-        const __amdgpu_buffer_rsrc_t oq = rsrc(p.y[0], 0, t0);
-        const __amdgpu_buffer_rsrc_t ok = rsrc(p.y[1], 1, t0);
+        const __amdgpu_buffer_rsrc_t oq = rsrc(p.y[0], 0, t0, OS);
+        const __amdgpu_buffer_rsrc_t ok = rsrc(p.y[1], 1, t0, OS);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const float r = rinv_s[par][seg[i]];
             float o[EV];
 #pragma unroll
             for (int e = 0; e < EV; ++e) o[e] = u[i][e] * r;
-            __builtin_amdgcn_raw_buffer_store_b128(pack(DT{}, o), tk[i] ? ok : oq, voff[i], 0, kNT);
+            u32x4 w[KO];
+            pack_out(DT{}, o, w);
+#pragma unroll
+            for (int j = 0; j < KO; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(w[j], tk[i] ? ok : oq, ooff[i] + 16 * j, 0, kNT);
         }
     };
 
@@ -484,7 +585,7 @@ template <class DT, bool VEC>
 __global__ void __launch_bounds__(256)
 shard_sumsq_kernel(const void* x_, int64_t T, int32_t H, int32_t N, float* partials)
 {
-    using elem_t = typename DT::elem_t;
+    using elem_t = typename DT::in_t;
     constexpr int EV = DT::kVec;
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -532,11 +633,13 @@ __global__ void __launch_bounds__(256)
 apply_scale_kernel(const void* x_, const void* g_, const float* rms_inv, int64_t T, int32_t H,
                    int32_t rpb, void* y_)
 {
-    using elem_t = typename DT::elem_t;
+    using in_t = typename DT::in_t;
+    using gam_t = typename DT::gam_t;
+    using out_t = typename DT::out_t;
     constexpr int EV = DT::kVec;
-    const elem_t* x = static_cast<const elem_t*>(x_);
-    const elem_t* g = static_cast<const elem_t*>(g_);
-    elem_t* y = static_cast<elem_t*>(y_);
+    const in_t* x = static_cast<const in_t*>(x_);
+    const gam_t* g = static_cast<const gam_t*>(g_);
+    out_t* y = static_cast<out_t*>(y_);
     const int64_t r0 = (int64_t)blockIdx.x * rpb;
     const int unit = VEC ? EV : 1;
     const int per_row = H / unit;
@@ -551,10 +654,16 @@ apply_scale_kernel(const void* x_, const void* g_, const float* rms_inv, int64_t
         if (VEC) {
             float f[EV], gg[EV], o[EV];
             unpack(DT{}, ld_stream(x + base), f);
-            unpack(DT{}, ld_cached(g + c * EV), gg);
+            u32x4 gw[DT::kGam];
+#pragma unroll
+            for (int j = 0; j < DT::kGam; ++j) gw[j] = ld_cached(g + c * EV + j * (16 / (int)sizeof(gam_t)));
+            unpack_gamma(DT{}, gw, gg);
 #pragma unroll
             for (int e = 0; e < EV; ++e) o[e] = (f[e] * gg[e]) * r;
-            st_stream(y + base, pack(DT{}, o));
+            u32x4 w[DT::kOut];
+            pack_out(DT{}, o, w);
+#pragma unroll
+            for (int j = 0; j < DT::kOut; ++j) st_stream(y + base + j * (16 / (int)sizeof(out_t)), w[j]);
         } else {
             const float o = (to_f32(x[base]) * to_f32(g[c])) * r;
             from_f32(o, y + base);
@@ -564,16 +673,14 @@ apply_scale_kernel(const void* x_, const void* g_, const float* rms_inv, int64_t
 
 // ================================================================ copy ceiling
 
-// Same access widths as the fused kernel (16-byte nontemporal loads and
-// stores), one vector per thread over a grid that covers both buffers;
-// bytes beyond the last full vector are copied one byte at a time.
+// One 16-byte nontemporal vector per thread through a descriptor covering
+// the workgroup's 4 KiB (the access pattern of the fused kernel's streaming
+// loads and stores). Workgroups [0, ceil(va/256)) copy a, the rest copy b;
+// bytes beyond the last full vector are copied one at a time.
 __global__ void __launch_bounds__(256)
 copy2_kernel(const void* a, const void* b, void* oa, void* ob, int64_t va, int64_t vb,
              int64_t ta, int64_t tb)
 {
-    // one 16-byte vector per thread through a descriptor covering this workgroup's
-    // 4 KiB, the access pattern of the fused kernel's streaming loads and stores
-    // workgroups [0, ceil(va/256)) copy a, the rest copy b
     const int64_t ba = (va + 255) / 256;
     const bool in_a = (int64_t)blockIdx.x < ba;
     const int64_t w0 = ((int64_t)blockIdx.x - (in_a ? 0 : ba)) * 256;

@@ -17,7 +17,10 @@ Recipe (stated once, used everywhere):
 * gamma: ``U(0.5, 1.5)`` or ``N(1, 0.1^2)``, drawn in float64.
 * Storage: float64 -> float32 (round to nearest even), then for bf16
   float32 -> bf16 round to nearest even on the bit pattern. bf16 tensors are
-  numpy ``uint16`` bit patterns.
+  numpy ``uint16`` bit patterns. For E4M3 activations float32 -> E4M3 (OCP
+  OFP8 E4M3: round to nearest even, magnitudes clipped to 448 first), stored
+  as numpy ``uint8`` codes; gamma is then bf16. No input scale factor is
+  applied: RMSNorm divides any common scale out (up to its effect on eps).
 
 The shapes and distributions are the stand-in for the Q/K activations of the
 models the letter evaluates ("SwiftQK ...", Section IV-A and the Q/K sizes of
@@ -41,7 +44,7 @@ class Workload:
     Hq: int
     Hk: int
     n_shards: int
-    dtype: str  # "bf16" or "f32" (inputs, gamma and outputs share it)
+    dtype: str  # input format: "bf16", "f32" (gamma and outputs share it) or "e4m3"
     dist: str = "normal"  # "normal" or "t3"
     sigma: float = 1.0
     outlier_frac: float = 0.0
@@ -49,18 +52,37 @@ class Workload:
     gamma_dist: str = "uniform"  # "uniform" (0.5, 1.5) or "normal" (1, 0.1)
     eps: float = EPS
     seed: int = 0
+    out_dtype: str = ""  # output format; "" = the input format (E4M3: "bf16" or "e4m3")
 
     def with_T(self, T: int) -> "Workload":
         return dataclasses.replace(self, T=T)
 
     @property
+    def out(self) -> str:
+        return self.out_dtype or self.dtype
+
+    @property
+    def gamma_dtype(self) -> str:
+        return "bf16" if self.dtype == "e4m3" else self.dtype
+
+    @property
+    def fmt(self) -> str:
+        """Kernel format name: "bf16", "f32", "e4m3_bf16" or "e4m3_e4m3"."""
+        return f"e4m3_{self.out}" if self.dtype == "e4m3" else self.dtype
+
+    @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        """Bytes per input element."""
+        return _BYTES[self.dtype]
+
+    @property
+    def out_bytes(self) -> int:
+        return _BYTES[self.out]
 
     def algorithmic_bytes(self) -> int:
         """One read and one write of Q and K, plus gamma_q and gamma_k once."""
-        s = self.elem_bytes
-        return 2 * self.T * (self.Hq + self.Hk) * s + (self.Hq + self.Hk) * s
+        per_col = self.elem_bytes + self.out_bytes
+        return self.T * (self.Hq + self.Hk) * per_col + (self.Hq + self.Hk) * _BYTES[self.gamma_dtype]
 
     def outlier_count(self, H: int) -> int:
         if self.outlier_frac <= 0:
@@ -68,11 +90,23 @@ class Workload:
         return max(1, int(round(self.outlier_frac * H)))
 
 
+_BYTES = {"bf16": 2, "f32": 4, "e4m3": 1}
+
 TINY = Workload("tiny", 8, 256, 256, 2, "f32", gamma_dist="normal")
 DECODE = Workload("decode", 64, 4096, 4096, 4, "bf16", outlier_frac=0.01, outlier_scale=20.0)
 PREFILL = Workload("prefill", 16384, 5120, 5120, 2, "bf16", sigma=2.0)
 GQA = Workload("gqa", 8192, 5120, 1024, 4, "bf16", outlier_frac=0.005, outlier_scale=50.0)
 CONFIGS = {w.name: w for w in (TINY, DECODE, PREFILL, GQA)}
+
+# FP8-E4M3 activations (the letter's second precision, Section IV-C) at the same
+# shapes: E4M3 in, bf16 gamma, bf16 or E4M3 out
+TINY_E4M3 = Workload("tiny_e4m3", 8, 256, 256, 2, "e4m3", gamma_dist="normal", out_dtype="e4m3")
+DECODE_E4M3 = Workload("decode_e4m3", 64, 4096, 4096, 4, "e4m3", outlier_frac=0.01,
+                       outlier_scale=20.0, out_dtype="e4m3")
+PREFILL_E4M3 = Workload("prefill_e4m3", 16384, 5120, 5120, 2, "e4m3", sigma=2.0, out_dtype="bf16")
+GQA_E4M3 = Workload("gqa_e4m3", 8192, 5120, 1024, 4, "e4m3", outlier_frac=0.005,
+                    outlier_scale=50.0, out_dtype="bf16")
+E4M3_CONFIGS = {w.name: w for w in (TINY_E4M3, DECODE_E4M3, PREFILL_E4M3, GQA_E4M3)}
 
 SWEEP_T = (4096, 4097, 16384, 65536)
 SWEEP_H = (1024, 3072, 5120, 8192, 16384)
@@ -85,6 +119,15 @@ def sweep() -> Iterator[Workload]:
     for T, H, N, dt, dist in itertools.product(SWEEP_T, SWEEP_H, SWEEP_N, SWEEP_DTYPE,
                                                SWEEP_DIST):
         yield Workload(f"sweep_T{T}_H{H}_N{N}_{dt}_{dist}", T, H, H, N, dt, dist=dist)
+
+
+def sweep_e4m3() -> Iterator[Workload]:
+    """The sweep grid with E4M3 activations: bf16 outputs for the normal draws,
+    E4M3 outputs for the Student-t draws (160 points)."""
+    for T, H, N, dist in itertools.product(SWEEP_T, SWEEP_H, SWEEP_N, SWEEP_DIST):
+        out = "bf16" if dist == "normal" else "e4m3"
+        yield Workload(f"sweep_T{T}_H{H}_N{N}_e4m3_{out}_{dist}", T, H, H, N, "e4m3", dist=dist,
+                       out_dtype=out)
 
 
 # ---------------------------------------------------------------- rounding
@@ -105,9 +148,24 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_codes(a: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3 codes (uint8): clip to +-448, then PyTorch's float8_e4m3fn
+    conversion (round to nearest even)."""
+    import torch
+    a = np.clip(np.ascontiguousarray(a, dtype=np.float32), -E4M3_MAX, E4M3_MAX)
+    return torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def store(a64: np.ndarray, dtype: str) -> np.ndarray:
     f32 = a64.astype(np.float32)
-    return f32_to_bf16_bits(f32) if dtype == "bf16" else f32
+    if dtype == "bf16":
+        return f32_to_bf16_bits(f32)
+    if dtype == "e4m3":
+        return f32_to_e4m3_codes(f32)
+    return f32
 
 
 # ---------------------------------------------------------------- host draws
@@ -116,8 +174,11 @@ def _streams(seed: int):
     return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(6)]
 
 
+_NP = {"bf16": np.uint16, "f32": np.float32, "e4m3": np.uint8}
+
+
 def _activations(rng, T, H, w: Workload, outlier_cols, chunk_rows: int) -> np.ndarray:
-    out = np.empty((T, H), np.uint16 if w.dtype == "bf16" else np.float32)
+    out = np.empty((T, H), _NP[w.dtype])
     for lo in range(0, T, chunk_rows):
         hi = min(T, lo + chunk_rows)
         if w.dist == "normal":
@@ -139,7 +200,7 @@ def _gamma(rng, H, w: Workload) -> np.ndarray:
         g = rng.normal(1.0, 0.1, H)
     else:
         raise ValueError(w.gamma_dist)
-    return store(g, w.dtype)
+    return store(g, w.gamma_dtype)
 
 
 def outlier_columns(w: Workload, which: str):
@@ -171,14 +232,15 @@ def make_device_activations(w: Workload, which: str, device, torch):
     Used only where a host draw would dominate a test's run time (the
     largest sweep points). Same distribution as the host draw, different
     values; the oracle then reads back exactly the rows it checks.
-    Returns a torch tensor of dtype bfloat16 or float32 on ``device``.
+    Returns a torch tensor of dtype bfloat16, float32 or float8_e4m3fn on ``device``.
     """
     H = w.Hq if which == "q" else w.Hk
     seed = int(np.random.SeedSequence(w.seed).spawn(6)[0 if which == "q" else 1]
                .generate_state(1)[0])
     g = torch.Generator(device=device)
     g.manual_seed(seed)
-    out_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out_dtype = {"bf16": torch.bfloat16, "f32": torch.float32,
+                 "e4m3": torch.float8_e4m3fn}[w.dtype]
     out = torch.empty((w.T, H), dtype=out_dtype, device=device)
     rows = max(1, (1 << 26) // H)
     for lo in range(0, w.T, rows):
@@ -192,6 +254,8 @@ def make_device_activations(w: Workload, which: str, device, torch):
         cols = outlier_columns(w, which)
         if cols is not None:
             a[:, torch.as_tensor(cols, device=device)] *= w.outlier_scale
+        if w.dtype == "e4m3":
+            a = a.clamp(-E4M3_MAX, E4M3_MAX)
         out[lo:hi] = a.to(out_dtype)
     return out
 
@@ -199,19 +263,24 @@ def make_device_activations(w: Workload, which: str, device, torch):
 # ---------------------------------------------------------------- transfers
 
 def to_device(a: np.ndarray, device, torch):
-    """numpy bf16 bit patterns (uint16) or float32 -> torch tensor on ``device``."""
+    """numpy bf16 bit patterns (uint16), float32 or E4M3 codes (uint8) -> torch
+    tensor (bfloat16, float32, float8_e4m3fn) on ``device``."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
     if a.dtype == np.float32:
         return torch.from_numpy(a).to(device)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a).to(device).view(torch.float8_e4m3fn)
     raise TypeError(a.dtype)
 
 
 def from_device(t) -> np.ndarray:
-    """torch tensor -> numpy bf16 bit patterns (uint16) or float32."""
+    """torch tensor -> numpy bf16 bit patterns (uint16), float32 or E4M3 codes (uint8)."""
     import torch
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()

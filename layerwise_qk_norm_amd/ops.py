@@ -20,7 +20,10 @@ _lock = threading.Lock()
 
 QKN_OK, QKN_EINVAL, QKN_EOVERLAP, QKN_ENOMEM, QKN_EHIP = 0, -1, -2, -3, -4
 QKN_ERESIDENCY, QKN_ETIMEOUT, QKN_ECAPTURE = -5, -6, -7
-QKN_BF16, QKN_F32 = 0, 1
+QKN_BF16, QKN_F32, QKN_E4M3 = 0, 1, 2
+# kernel formats (input x / gamma / output y), the ``dtype`` of the planning calls
+FORMATS = {"bf16": 0, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 3}
+E4M3 = torch.float8_e4m3fn
 NUM_VARIANTS = 10
 MAX_DATA_WAVES = 15
 MAX_SHARDS = 32
@@ -52,11 +55,14 @@ _P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
 _SIGS = {
     "qknorm_layerwise_fwd_bf16": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
     "qknorm_layerwise_fwd_f32": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
+    "qknorm_layerwise_fwd_e4m3": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _I, _P],
     "qknorm_shard_sumsq_bf16": [_P, _I64, _I64, _I, _P, _P],
     "qknorm_shard_sumsq_f32": [_P, _I64, _I64, _I, _P, _P],
+    "qknorm_shard_sumsq_e4m3": [_P, _I64, _I64, _I, _P, _P],
     "qknorm_combine_scale": [_P, _I64, _I64, _I, _F, _P, _P],
     "qknorm_apply_scale_bf16": [_P, _P, _P, _I64, _I64, _P, _P],
     "qknorm_apply_scale_f32": [_P, _P, _P, _I64, _I64, _P, _P],
+    "qknorm_apply_scale_e4m3": [_P, _P, _P, _I64, _I64, _P, _I, _P],
     "qknorm_check_fault": [_P],
     "qknorm_strerror": [_I],
     "qknorm_last_hip_error": [],
@@ -115,11 +121,42 @@ def _dtype_code(t: torch.Tensor) -> int:
         return QKN_BF16
     if t.dtype == torch.float32:
         return QKN_F32
-    raise TypeError(f"tensors must be bfloat16 or float32, got {t.dtype}")
+    if t.dtype == E4M3:
+        return QKN_E4M3
+    raise TypeError(f"tensors must be bfloat16, float32 or float8_e4m3fn, got {t.dtype}")
 
 
 def _suffix(code: int) -> str:
-    return "bf16" if code == QKN_BF16 else "f32"
+    return {QKN_BF16: "bf16", QKN_F32: "f32", QKN_E4M3: "e4m3"}[code]
+
+
+def _out_dtype(x_dtype, out, out_dtype):
+    """Output dtype of a call: bf16/fp32 inputs keep their dtype; E4M3 inputs
+    give bf16 unless E4M3 is asked for (by ``out`` or ``out_dtype``)."""
+    if x_dtype != E4M3:
+        want = x_dtype
+    elif out is not None:
+        want = out.dtype
+    else:
+        want = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype is not None and out_dtype != want:
+        raise TypeError(f"out_dtype {out_dtype} does not match the output {want}")
+    if x_dtype == E4M3 and want not in (torch.bfloat16, E4M3):
+        raise TypeError(f"E4M3 inputs give bfloat16 or float8_e4m3fn outputs, not {want}")
+    return want
+
+
+def _gamma_dtype(x_dtype):
+    return torch.bfloat16 if x_dtype == E4M3 else x_dtype
+
+
+def format_of(x_dtype, out_dtype) -> int:
+    """Kernel format code of an input/output dtype pair."""
+    if x_dtype == torch.bfloat16:
+        return FORMATS["bf16"]
+    if x_dtype == torch.float32:
+        return FORMATS["f32"]
+    return FORMATS["e4m3_bf16" if out_dtype == torch.bfloat16 else "e4m3_e4m3"]
 
 
 def _need(t: torch.Tensor, name: str, ndim: int, dtype=None, device=None):
@@ -141,35 +178,43 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _fused_fn(code: int):
-    L = lib()
-    return L.qknorm_layerwise_fwd_bf16 if code == QKN_BF16 else L.qknorm_layerwise_fwd_f32
-
-
 def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_q=None,
-                  out_k=None):
-    """Fused Q+K layerwise RMSNorm; returns ``(out_q, out_k)``."""
+                  out_k=None, out_dtype=None):
+    """Fused Q+K layerwise RMSNorm; returns ``(out_q, out_k)``.
+
+    q and k are bfloat16, float32 or float8_e4m3fn (E4M3). gamma has the dtype of
+    q, except bfloat16 for E4M3 inputs. Outputs have the dtype of q, except for
+    E4M3 inputs: bfloat16 by default, float8_e4m3fn when ``out_dtype`` (or the
+    given outputs) say so.
+    """
     _need(q, "q", 2)
     dt = q.dtype
     dev = q.device
+    code = _dtype_code(q)
     _need(k, "k", 2, dt, dev)
-    _need(gamma_q, "gamma_q", 1, dt, dev)
-    _need(gamma_k, "gamma_k", 1, dt, dev)
+    _need(gamma_q, "gamma_q", 1, _gamma_dtype(dt), dev)
+    _need(gamma_k, "gamma_k", 1, _gamma_dtype(dt), dev)
     T, Hq = q.shape
     if k.shape[0] != T:
         raise ValueError("q and k must have the same number of tokens")
     Hk = k.shape[1]
     if gamma_q.shape[0] != Hq or gamma_k.shape[0] != Hk:
         raise ValueError("gamma_q must be [Hq] and gamma_k [Hk]")
-    out_q = torch.empty_like(q) if out_q is None else out_q
-    out_k = torch.empty_like(k) if out_k is None else out_k
-    _need(out_q, "out_q", 2, dt, dev)
-    _need(out_k, "out_k", 2, dt, dev)
+    odt = _out_dtype(dt, out_q if out_q is not None else out_k, out_dtype)
+    out_q = torch.empty(q.shape, dtype=odt, device=dev) if out_q is None else out_q
+    out_k = torch.empty(k.shape, dtype=odt, device=dev) if out_k is None else out_k
+    _need(out_q, "out_q", 2, odt, dev)
+    _need(out_k, "out_k", 2, odt, dev)
     if out_q.shape != q.shape or out_k.shape != k.shape:
         raise ValueError("outputs must have the shapes of q and k")
-    fn = _fused_fn(_dtype_code(q))
+    L = lib()
     args = (q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), T, Hq, Hk,
             n_shards, eps, out_q.data_ptr(), out_k.data_ptr())
+    if code == QKN_E4M3:
+        fn = L.qknorm_layerwise_fwd_e4m3
+        args = args + (_dtype_code(out_q),)
+    else:
+        fn = L.qknorm_layerwise_fwd_bf16 if code == QKN_BF16 else L.qknorm_layerwise_fwd_f32
     if dev.index == torch.cuda.current_device():
         status = fn(*args, torch.cuda.current_stream(dev).cuda_stream)
     else:
@@ -212,23 +257,27 @@ def combine_scale(partials, H: int, eps: float = 1e-6, rms_inv=None):
     return rms_inv
 
 
-def apply_scale(x, gamma, rms_inv, out=None):
-    """``out = x * gamma * rms_inv[:, None]`` rounded to x's dtype."""
+def apply_scale(x, gamma, rms_inv, out=None, out_dtype=None):
+    """``out = x * gamma * rms_inv[:, None]`` rounded to the output dtype (x's dtype;
+    for E4M3 x: bfloat16 or float8_e4m3fn, with bfloat16 gamma)."""
     _need(x, "x", 2)
     T, H = x.shape
-    _need(gamma, "gamma", 1, x.dtype, x.device)
+    code = _dtype_code(x)
+    _need(gamma, "gamma", 1, _gamma_dtype(x.dtype), x.device)
     _need(rms_inv, "rms_inv", 1, torch.float32, x.device)
     if gamma.shape[0] != H or rms_inv.shape[0] != T:
         raise ValueError("gamma must be [H] and rms_inv [T]")
-    out = torch.empty_like(x) if out is None else out
-    _need(out, "out", 2, x.dtype, x.device)
+    odt = _out_dtype(x.dtype, out, out_dtype)
+    out = torch.empty(x.shape, dtype=odt, device=x.device) if out is None else out
+    _need(out, "out", 2, odt, x.device)
     if out.shape != x.shape:
         raise ValueError("out must have the shape of x")
-    code = _dtype_code(x)
     fn = getattr(lib(), f"qknorm_apply_scale_{_suffix(code)}")
+    args = (x.data_ptr(), gamma.data_ptr(), rms_inv.data_ptr(), T, H, out.data_ptr())
+    if code == QKN_E4M3:
+        args = args + (_dtype_code(out),)
     with torch.cuda.device(x.device):
-        _check(fn(x.data_ptr(), gamma.data_ptr(), rms_inv.data_ptr(), T, H, out.data_ptr(),
-                  _stream(x.device)), "qknorm_apply_scale")
+        _check(fn(*args, _stream(x.device)), "qknorm_apply_scale")
     return out
 
 
@@ -251,33 +300,35 @@ def plan_fused(dtype: str, T: int, Hq: int, Hk: int, n_shards: int, cu_count: in
                blocks_per_cu, aligned: bool = True) -> dict:
     """Host-only launch plan for a device with the given capacity (no GPU needed).
 
-    ``blocks_per_cu[v][w]``: co-resident workgroups per CU of variant v with w
-    data waves (NUM_VARIANTS x (MAX_DATA_WAVES + 1)).
+    ``dtype`` names a format of ``FORMATS``. ``blocks_per_cu[v][w]``: co-resident
+    workgroups per CU of variant v with w data waves (NUM_VARIANTS x
+    (MAX_DATA_WAVES + 1)).
     """
     flat = [int(x) for row in blocks_per_cu for x in row]
     assert len(flat) == NUM_VARIANTS * (MAX_DATA_WAVES + 1)
     arr = (ctypes.c_int * len(flat))(*flat)
     pl = Plan()
-    _check(lib().qknorm_plan_fused(QKN_BF16 if dtype == "bf16" else QKN_F32, T, Hq, Hk, n_shards,
-                                   cu_count, arr, 1 if aligned else 0, ctypes.byref(pl)),
+    _check(lib().qknorm_plan_fused(FORMATS[dtype], T, Hq, Hk, n_shards, cu_count, arr,
+                                   1 if aligned else 0, ctypes.byref(pl)),
            "qknorm_plan_fused")
     return pl.as_dict()
 
 
 def max_coresident_workgroups(dtype: str, Hq: int, Hk: int, n_shards: int) -> int:
     out = ctypes.c_int(0)
-    _check(lib().qknorm_max_coresident_workgroups(QKN_BF16 if dtype == "bf16" else QKN_F32, Hq,
-                                                  Hk, n_shards, ctypes.byref(out)),
+    _check(lib().qknorm_max_coresident_workgroups(FORMATS[dtype], Hq, Hk, n_shards,
+                                                  ctypes.byref(out)),
            "qknorm_max_coresident_workgroups")
     return out.value
 
 
 def device_occupancy(dtype: str):
-    """(blocks_per_cu[variant][data_waves], compute units) of the current device."""
+    """(blocks_per_cu[variant][data_waves], compute units) of the current device for
+    the format ``dtype`` (a key of ``FORMATS``)."""
     arr = (ctypes.c_int * (NUM_VARIANTS * (MAX_DATA_WAVES + 1)))()
     cu = ctypes.c_int(0)
-    _check(lib().qknorm_device_occupancy(QKN_BF16 if dtype == "bf16" else QKN_F32, arr,
-                                         ctypes.byref(cu)), "qknorm_device_occupancy")
+    _check(lib().qknorm_device_occupancy(FORMATS[dtype], arr, ctypes.byref(cu)),
+           "qknorm_device_occupancy")
     w = MAX_DATA_WAVES + 1
     return [list(arr[v * w:(v + 1) * w]) for v in range(NUM_VARIANTS)], cu.value
 
@@ -301,7 +352,7 @@ def bench_fused(q, k, gamma_q, gamma_k, n_shards: int, eps: float, out_q, out_k,
     T, Hq = q.shape
     Hk = k.shape[1]
     with torch.cuda.device(q.device):
-        _check(lib().qknorm_bench_fused(_dtype_code(q), q.data_ptr(), k.data_ptr(),
+        _check(lib().qknorm_bench_fused(format_of(q.dtype, out_q.dtype), q.data_ptr(), k.data_ptr(),
                                         gamma_q.data_ptr(), gamma_k.data_ptr(), T, Hq, Hk,
                                         n_shards, eps, out_q.data_ptr(), out_k.data_ptr(),
                                         repeats, _stream(q.device)), "qknorm_bench_fused")

@@ -12,17 +12,62 @@ from __future__ import annotations
 
 import numpy as np
 
-# Tolerances on the final outputs, by output dtype.
+# Tolerances on the final outputs, by output dtype (relative error against the
+# unrounded oracle). E4M3 outputs are judged by code instead: see e4m3_accepts.
 TOL = {"bf16": 8e-3, "f32": 1e-5}
+# Relative perturbation of the exact value within which either E4M3 neighbour is
+# accepted: fp32 arithmetic may move a value lying that close to a rounding
+# boundary across it.
+E4M3_REL = 1e-5
+E4M3_MAX = 448.0
 # Tolerance on intermediate fp32 statistics (partials, reciprocal RMS).
 TOL_STAT = 1e-5
 
 
 def decode_out(a: np.ndarray) -> np.ndarray:
-    """float64 values of a device output: bf16 bit patterns or float32."""
+    """float64 values of a device output: bf16 bit patterns, float32 or E4M3 codes."""
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype == np.uint8:
+        from oracle.oracle import decode_e4m3_np
+        return decode_e4m3_np(a)
     return np.asarray(a, dtype=np.float64)
+
+
+def e4m3_rne(y: np.ndarray) -> np.ndarray:
+    """E4M3 code (OCP OFP8 layout) nearest to each float64 value, ties to the even
+    code; magnitudes of 448 and above (infinities included) saturate to the
+    largest finite code, and NaN maps to the NaN code of its sign."""
+    y = np.asarray(y, np.float64)
+    neg = np.signbit(y).astype(np.int64)
+    a = np.abs(y)
+    with np.errstate(invalid="ignore", over="ignore"):
+        # subnormal range [0, 2^-6): spacing 2^-9, code = rounded multiple (8 = 2^-6)
+        m_sub = np.rint(np.ldexp(np.where(np.isfinite(a), a, 0.0), 9)).astype(np.int64)
+        # normal range: a = 1.f * 2^e, 3 fraction bits kept
+        _, E = np.frexp(np.where((a > 0) & np.isfinite(a), a, 1.0))
+        e = E.astype(np.int64) - 1
+        q = np.rint(np.ldexp(np.where(np.isfinite(a), a, 0.0), -(e - 3))).astype(np.int64)
+    carry = q >= 16
+    e = e + carry
+    q = np.where(carry, 8, q)
+    code = np.where(a < 2.0 ** -6, m_sub, ((e + 7) << 3) | (q - 8))
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    code = np.where(np.isnan(a), 0x7F, code)
+    return (code | (neg << 7)).astype(np.uint8)
+
+
+def e4m3_accepts(codes: np.ndarray, y: np.ndarray, rel: float = E4M3_REL) -> np.ndarray:
+    """True where a device E4M3 code is the rounding of the exact value y, or, when
+    y lies within ``rel`` of a rounding boundary, the code on the other side."""
+    from oracle.oracle import decode_e4m3_np
+    y = np.asarray(y, np.float64)
+    got = decode_e4m3_np(np.asarray(codes, np.uint8))
+    ok = np.zeros(y.shape, bool)
+    for f in (1.0 - rel, 1.0, 1.0 + rel):
+        want = decode_e4m3_np(e4m3_rne(y * f))
+        ok |= (got == want) | (np.isnan(got) & np.isnan(want))
+    return ok
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:

@@ -35,7 +35,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qknorm_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPE_CODE = {"bf16": 0, "f32": 1}
+DTYPE_CODE = {"bf16": 0, "f32": 1, "e4m3": 2}
+# the format of gamma for each input format: bf16 weights with E4M3 activations
+GAMMA_FORMAT = {"bf16": "bf16", "f32": "f32", "e4m3": "bf16"}
 
 
 def build(force: bool = False) -> str:
@@ -61,6 +63,8 @@ def _load():
         lib.oracle_rmsnorm.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_decode_e4m3.restype = ctypes.c_int
+        lib.oracle_decode_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_shard_sumsq.restype = ctypes.c_int
         lib.oracle_shard_sumsq.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
@@ -73,7 +77,10 @@ def _dtype_of(a: np.ndarray) -> str:
         return "bf16"
     if a.dtype == np.float32:
         return "f32"
-    raise TypeError(f"oracle inputs are bf16 bit patterns (uint16) or float32, got {a.dtype}")
+    if a.dtype == np.uint8:
+        return "e4m3"
+    raise TypeError("oracle inputs are bf16 bit patterns (uint16), float32 or E4M3 codes "
+                    f"(uint8), got {a.dtype}")
 
 
 def _ptr(a):
@@ -93,8 +100,8 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, want_y: bool = True,
     x = np.ascontiguousarray(x)
     gamma = np.ascontiguousarray(gamma)
     dt = _dtype_of(x)
-    if _dtype_of(gamma) != dt:
-        raise TypeError("gamma must have the dtype of x")
+    if _dtype_of(gamma) != GAMMA_FORMAT[dt]:
+        raise TypeError(f"gamma must be {GAMMA_FORMAT[dt]} for {dt} inputs")
     T, H = x.shape
     if gamma.shape != (H,):
         raise ValueError("gamma must be [H]")
@@ -135,14 +142,40 @@ def shard_sumsq(x: np.ndarray, n_shards: int) -> np.ndarray:
     return p
 
 
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Exact values of E4M3 codes via the C decoder (OCP OFP8 E4M3 layout)."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    if lib.oracle_decode_e4m3(c.ctypes.data, c.size, out.ctypes.data) != 0:
+        raise ValueError("oracle_decode_e4m3 rejected its arguments")
+    return out
+
+
 # ---------------------------------------------------------------- NumPy mirror
 
+def decode_e4m3_np(codes: np.ndarray) -> np.ndarray:
+    """NumPy rendering of the OCP E4M3 decoding: sign, 4-bit exponent with bias 7,
+    3-bit mantissa; exponent 0 is zero or subnormal (m * 2^-9); S.1111.111 is NaN."""
+    c = codes.astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    normal = np.ldexp(1.0 + m / 8.0, e - 7)
+    sub = np.ldexp(m.astype(np.float64), -9)
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
 def decode(a: np.ndarray) -> np.ndarray:
-    """Exact float64 values of stored bf16 bit patterns or float32 values."""
+    """Exact float64 values of stored bf16 bit patterns, float32 values or E4M3 codes."""
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if a.dtype == np.float32:
         return a.astype(np.float64)
+    if a.dtype == np.uint8:
+        return decode_e4m3_np(a)
     raise TypeError(a.dtype)
 
 

@@ -32,6 +32,14 @@
  * an IEEE binary32 value; binary32 -> binary64 is exact. eps is received as
  * binary32 (the value the GPU library receives) and promoted exactly.
  *
+ * FP8 activations (the letter evaluates FP8-E4M3 next to BF16 and accumulates
+ * in FP32 for both, Section IV-C): an E4M3 code is decoded exactly from the
+ * OCP 8-bit floating point format (OFP8, revision 1.0), E4M3 encoding:
+ * sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+ * holds zero and subnormals m * 2^-9; no infinities; S.1111.111 is NaN, so
+ * the largest finite magnitude is S.1111.110 = 448. With E4M3 activations the
+ * scale gamma is bf16 (the format of the layer's weights).
+ *
  * No blocking, fusion or reordering: each sum is a plain left-to-right loop
  * in binary64 (relative error <= H * 2^-53).
  */
@@ -52,18 +60,47 @@ static double decode_f32(float v)
     return (double)v;
 }
 
-/* dtype codes: 0 = bf16 (uint16_t bit patterns), 1 = fp32 */
+static double decode_e4m3(uint8_t code)
+{
+    const int sign = code >> 7;
+    const int expo = (code >> 3) & 15;
+    const int mant = code & 7;
+    double mag;
+    if (expo == 15 && mant == 7)
+        mag = NAN;
+    else if (expo == 0)
+        mag = ldexp((double)mant, -9);                 /* subnormal: m/8 * 2^(1-7) */
+    else
+        mag = ldexp(1.0 + (double)mant / 8.0, expo - 7);
+    return sign ? -mag : mag;
+}
+
+/* input format codes: 0 = bf16 (uint16_t bit patterns), 1 = fp32,
+ * 2 = E4M3 codes (uint8_t); the scale gamma is bf16 for format 2 and has the
+ * format of x otherwise */
 static double load(const void* base, int dtype, int64_t i)
 {
     if (dtype == 0)
         return decode_bf16(((const uint16_t*)base)[i]);
+    if (dtype == 2)
+        return decode_e4m3(((const uint8_t*)base)[i]);
     return decode_f32(((const float*)base)[i]);
+}
+
+static int gamma_format(int dtype)
+{
+    return dtype == 2 ? 0 : dtype;
+}
+
+static int format_ok(int dtype)
+{
+    return dtype == 0 || dtype == 1 || dtype == 2;
 }
 
 /*
  * RMSNorm of T rows of width H (row-major, row stride H).
- *   x      [T][H]  input values (bf16 bits or fp32)
- *   gamma  [H]     scale (same dtype as x)
+ *   x      [T][H]  input values (bf16 bits, fp32 or E4M3 codes)
+ *   gamma  [H]     scale (format of x; bf16 bits when x is E4M3)
  *   eps            binary32 epsilon, promoted exactly
  * Outputs (any may be NULL):
  *   y      [T][H]  x / sqrt(S/H + eps) * gamma, unrounded binary64
@@ -74,7 +111,7 @@ static double load(const void* base, int dtype, int64_t i)
 int oracle_rmsnorm(const void* x, const void* gamma, int dtype, int64_t T, int64_t H,
                    float eps, double* y, double* sumsq, double* rinv)
 {
-    if (!x || (y && !gamma) || T < 0 || H < 1 || (dtype != 0 && dtype != 1))
+    if (!x || (y && !gamma) || T < 0 || H < 1 || !format_ok(dtype))
         return -1;
     const double e = (double)eps;
     for (int64_t t = 0; t < T; ++t) {
@@ -91,7 +128,7 @@ int oracle_rmsnorm(const void* x, const void* gamma, int dtype, int64_t T, int64
         if (y) {
             for (int64_t j = 0; j < H; ++j) {
                 double v = load(x, dtype, t * H + j);
-                double g = load(gamma, dtype, j);
+                double g = load(gamma, gamma_format(dtype), j);
                 y[t * H + j] = v / denom * g;
             }
         }
@@ -106,8 +143,7 @@ int oracle_rmsnorm(const void* x, const void* gamma, int dtype, int64_t T, int64
 int oracle_shard_sumsq(const void* x, int dtype, int64_t T, int64_t H, int n_shards,
                        double* p)
 {
-    if (!x || !p || T < 0 || H < 1 || n_shards < 1 || H % n_shards != 0 ||
-        (dtype != 0 && dtype != 1))
+    if (!x || !p || T < 0 || H < 1 || n_shards < 1 || H % n_shards != 0 || !format_ok(dtype))
         return -1;
     const int64_t W = H / n_shards;
     for (int k = 0; k < n_shards; ++k) {
@@ -120,5 +156,15 @@ int oracle_shard_sumsq(const void* x, int dtype, int64_t T, int64_t H, int n_sha
             p[(int64_t)k * T + t] = s;
         }
     }
+    return 0;
+}
+
+/* Exact value of each of n E4M3 codes (for the tests of the decoder). */
+int oracle_decode_e4m3(const uint8_t* codes, int64_t n, double* out)
+{
+    if (!codes || !out || n < 0)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = decode_e4m3(codes[i]);
     return 0;
 }

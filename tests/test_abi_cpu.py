@@ -88,6 +88,31 @@ def test_fused_rejects_partial_overlap():
     assert fwd(ptrs=[q, k, gq, gk, oq, gk]) == ops.QKN_EOVERLAP  # out_k over gamma_k
 
 
+def fwd8(T=4, Hq=64, Hk=64, N=2, eps=1e-6, ptrs=None, out=ops.QKN_BF16):
+    q, k, gq, gk, oq, ok = ptrs or FAKE
+    return ops.lib().qknorm_layerwise_fwd_e4m3(q, k, gq, gk, T, Hq, Hk, N, eps, oq, ok, out, None)
+
+
+def test_e4m3_entry_points_reject_bad_arguments():
+    L = ops.lib()
+    for bad in (ops.QKN_F32, 7, -1):  # outputs are bf16 or e4m3 only
+        assert fwd8(out=bad) == ops.QKN_EINVAL
+        assert L.qknorm_apply_scale_e4m3(*FAKE[:3], 4, 64, FAKE[3], bad, None) == ops.QKN_EINVAL
+    for kw in (dict(N=3), dict(T=-1), dict(eps=-1.0), dict(Hq=0)):
+        assert fwd8(**kw) == ops.QKN_EINVAL
+    assert fwd8(T=0, ptrs=[0] * 6) == ops.QKN_OK
+    q, k, gq, gk, oq, ok = FAKE
+    # a bf16 output at q's address covers 512 bytes, q only 256: not an exact alias
+    assert fwd8(ptrs=[q, k, gq, gk, q, ok], out=ops.QKN_BF16) == ops.QKN_EOVERLAP
+    # out_k (4 x 64 bf16 = 512 B) reaching into gamma_k
+    assert fwd8(ptrs=[q, k, gq, gk, oq, gk - 256]) == ops.QKN_EOVERLAP
+    # e4m3 x of 256 B just below the partials: no overlap; 8 bytes in: overlap
+    assert L.qknorm_shard_sumsq_e4m3(FAKE[0], 4, 64, 2, FAKE[0] + 8, None) == ops.QKN_EOVERLAP
+    assert L.qknorm_shard_sumsq_e4m3(FAKE[0], 4, 64, 3, FAKE[1], None) == ops.QKN_EINVAL
+    assert L.qknorm_apply_scale_e4m3(FAKE[0], FAKE[1], FAKE[2], 4, 64, FAKE[0] + 2,
+                                     ops.QKN_E4M3, None) == ops.QKN_EOVERLAP
+
+
 def test_split_entry_points_reject_bad_arguments():
     L = ops.lib()
     assert L.qknorm_shard_sumsq_bf16(FAKE[0], 4, 64, 3, FAKE[1], None) == ops.QKN_EINVAL
@@ -107,28 +132,40 @@ def test_split_entry_points_reject_bad_arguments():
 
 CU = 256
 VPT = [1, 2, 3, 4, 6, 9, 1, 2, 3, 4]
-MAXW = [15, 15, 15, 15, 11, 15, 15, 15, 11, 7]
-VGPR = [32, 56, 80, 104, 168, 120, 48, 80, 104, 128]  # per-variant register use, roughly as compiled
+# data waves per variant (launch bound / 64 - 1) and rough register use, per format;
+# 0 = not instantiated for that format
+MAXW = {"bf16": [15, 15, 15, 15, 11, 0, 15, 15, 11, 7],
+        "f32": [15, 15, 15, 15, 11, 15, 15, 15, 11, 7],
+        "e4m3": [15, 15, 11, 0, 0, 0, 15, 11, 0, 0]}
+VGPR = {"bf16": [32, 56, 80, 104, 168, 120, 48, 80, 136, 184],
+        "f32": [32, 56, 80, 104, 168, 120, 48, 80, 104, 128],
+        "e4m3": [56, 104, 144, 1, 1, 1, 96, 168, 1, 1]}
+EV = {"bf16": 8, "f32": 4, "e4m3_bf16": 16, "e4m3_e4m3": 16}
+KGAM = {"bf16": 1, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 2}
+FORMATS = list(EV)
+
+
+def _fam(fmt):
+    return "e4m3" if fmt.startswith("e4m3") else fmt
 
 
 def occupancy_model(dtype="bf16", lds_kb=160, waves_per_simd=8):
-    """Synthetic blocks_per_cu[v][w]: register file, wave slots and LDS limits."""
+    """Synthetic blocks_per_cu[v][w] of a format: register file, wave slots and LDS limits."""
+    fam = _fam(dtype)
     table = []
     for v in range(ops.NUM_VARIANTS):
         row = [0] * (ops.MAX_DATA_WAVES + 1)
-        for w in range(1, MAXW[v] + 1):
-            if v == 5 and dtype != "f32":
-                continue
+        for w in range(1, MAXW[fam][v] + 1):
             waves = w + 1
             per_simd = -(-waves // 4)
-            by_regs = min(waves_per_simd, 512 // VGPR[v]) // per_simd
-            by_lds = (lds_kb * 1024) // (VPT[v] * 64 * w * 16 + 1024)
+            by_regs = min(waves_per_simd, 512 // VGPR[fam][v]) // per_simd
+            by_lds = (lds_kb * 1024) // (VPT[v] * 64 * w * 16 * KGAM[dtype] + 1024)
             row[w] = max(0, min(by_regs, by_lds, 32 // waves))
         table.append(row)
     return table
 
 
-BPC = {"bf16": occupancy_model("bf16"), "f32": occupancy_model("f32")}
+BPC = {f: occupancy_model(f) for f in FORMATS}
 
 
 def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=None):
@@ -136,7 +173,8 @@ def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=None):
     if p["variant"] < 0:
         return
     v, w = p["variant"], p["data_waves"]
-    assert p["threads"] == 64 * (w + 1) and 1 <= w <= MAXW[v]
+    assert MAXW[_fam(dtype)][v] > 0, "variant not instantiated for this format"
+    assert p["threads"] == 64 * (w + 1) and 1 <= w <= MAXW[_fam(dtype)][v]
     assert p["slots"] == VPT[v]
     cap = bpc[v][w] * cu
     assert p["grid"] == p["n_groups"] * N
@@ -146,7 +184,7 @@ def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=None):
     assert p["n_tiles"] == -(-T // p["rows"])
     assert 1 <= p["n_groups"] <= p["n_tiles"]
     assert p["iters"] * p["n_groups"] >= p["n_tiles"] > (p["iters"] - 1) * p["n_groups"]
-    ev = 8 if dtype == "bf16" else 4
+    ev = EV[dtype]
     wvq, wvk = Hq // N // ev, Hk // N // ev
     # Q's part of a tile is padded to whole waves, then K's part follows
     need = -(-p["rows"] * wvq // 64) * 64 + p["rows"] * wvk
@@ -160,19 +198,20 @@ def plan(dtype, T, Hq, Hk, N, cu=CU, bpc=None, aligned=True):
 
 
 def test_plan_named_workloads():
-    for w in (inputs.TINY, inputs.DECODE, inputs.PREFILL, inputs.GQA):
-        p = plan(w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
+    for w in (inputs.TINY, inputs.DECODE, inputs.PREFILL, inputs.GQA,
+              *inputs.E4M3_CONFIGS.values()):
+        p = plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
         assert p["variant"] >= 0, w.name
-        check_plan(p, w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
+        check_plan(p, w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
     d = plan("bf16", 64, 4096, 4096, 4)
     assert d["rows"] == 1 and d["grid"] == 256 and d["xcd_map"] == 1
 
 
 def test_plan_every_sweep_point():
-    for w in inputs.sweep():
-        p = plan(w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
+    for w in [*inputs.sweep(), *inputs.sweep_e4m3()]:
+        p = plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
         assert p["variant"] >= 0, w.name  # every sweep shape fits a fused variant
-        check_plan(p, w.dtype, w.T, w.Hq, w.Hk, w.n_shards)
+        check_plan(p, w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
 
 
 def test_plan_refuses_grid_beyond_residency():
@@ -225,8 +264,8 @@ def test_plan_randomised_invariants():
     rnd = random.Random(1)
     for _ in range(3000):
         N = rnd.choice([1, 2, 3, 4, 5, 8, 16, 32])
-        dt = rnd.choice(["bf16", "f32"])
-        ev = 8 if dt == "bf16" else 4
+        dt = rnd.choice(FORMATS)
+        ev = EV[dt]
         Hq = N * ev * rnd.randint(1, 600)
         Hk = N * ev * rnd.randint(1, 600)
         T = rnd.choice([1, 2, 3, 7, 63, 64, 65, 1000, 4097, rnd.randint(1, 200000)])

@@ -77,3 +77,33 @@ def test_sweep_grid_and_bytes():
     assert inputs.DECODE.algorithmic_bytes() == 2_113_536
     assert inputs.GQA.algorithmic_bytes() == 201_338_880
     assert inputs.TINY.algorithmic_bytes() == 34_816
+
+
+def test_e4m3_workloads():
+    assert len(list(inputs.sweep_e4m3())) == 160
+    w = inputs.PREFILL_E4M3
+    assert w.fmt == "e4m3_bf16" and w.gamma_dtype == "bf16" and w.out_bytes == 2
+    # 1 byte read + 2 bytes written per element, gamma in bf16
+    assert w.algorithmic_bytes() == 16384 * 10240 * 3 + 10240 * 2
+    assert inputs.DECODE_E4M3.fmt == "e4m3_e4m3"
+    assert inputs.DECODE_E4M3.algorithmic_bytes() == 64 * 8192 * 2 + 8192 * 2
+    d = inputs.make_host(w.with_T(32))
+    assert d["q"].dtype == np.uint8 and d["gamma_q"].dtype == np.uint16
+    codes = d["q"]
+    assert not np.any((codes & 0x7F) == 0x7F), "no NaN codes"
+    # codes are the nearest E4M3 values of the float32 draws of the q stream
+    torch = pytest.importorskip("torch")
+    a = (np.random.default_rng(np.random.SeedSequence(w.seed).spawn(6)[0])
+         .standard_normal((32, w.Hq)) * w.sigma).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+
+
+def test_e4m3_clipping_and_transfer_round_trip():
+    torch = pytest.importorskip("torch")
+    big = np.array([1000.0, -1e6, 448.0, 449.0, 0.0], np.float32)
+    c = inputs.f32_to_e4m3_codes(big)
+    assert list(c) == [0x7E, 0xFE, 0x7E, 0x7E, 0x00]
+    t = inputs.to_device(c, "cpu", torch)
+    assert t.dtype == torch.float8_e4m3fn
+    assert np.array_equal(inputs.from_device(t), c)

@@ -13,10 +13,16 @@ Besides the headline (GB/s of algorithmic bytes), the line carries:
   roofline    -- the fused kernel against MI355X peak HBM bandwidth
   cpu_baseline-- the fp64 oracle timed on this host's cores on a sample
 
+  e4m3        -- FP8-E4M3 activations (bf16 gamma) on the prefill shape with bf16
+                 and with E4M3 outputs, each against the HBM roofline, and the
+                 decode shape in us per call
+
 Modes: ``--pmc`` runs only the kernels whose counters are collected
-(fused prefill and the copy of known size), for rocprofv3 --pmc runs.
+(fused prefill in bf16 and in E4M3->bf16, and the copy of known size), for
+rocprofv3 --pmc runs.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -30,18 +36,19 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 METRIC = "fused Q+K layerwise RMSNorm HBM GB/s (% of peak) at T=16384; decode µs at T=64"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_prefill_T16384_traffic.txt")
+TRAFFIC_SUMMARY_E4M3 = os.path.join(ROOT, "profiles", "fused_prefill_e4m3_T16384_traffic.txt")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, if it is current."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def read_traffic(path=TRAFFIC_SUMMARY):
+    """HBM bytes per launch from a committed counter summary, if it is current."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_SUMMARY):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -72,12 +79,60 @@ def device_workload(w, torch, sets=1):
     d = inputs.make_host(w)
     dev = "cuda:0"
     gq, gk = inputs.to_device(d["gamma_q"], dev, torch), inputs.to_device(d["gamma_k"], dev, torch)
+    odt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.float8_e4m3fn}[w.out]
     bufs = []
     for s in range(sets):
         q = inputs.to_device(d["q"], dev, torch)
         k = inputs.to_device(d["k"], dev, torch)
-        bufs.append((q, k, torch.empty_like(q), torch.empty_like(k)))
+        bufs.append((q, k, torch.empty(q.shape, dtype=odt, device=dev),
+                     torch.empty(k.shape, dtype=odt, device=dev)))
     return d, gq, gk, bufs
+
+
+def roofline(nbytes, ms, traffic):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+def bench_e4m3(args, torch, stream, timed):
+    """FP8-E4M3 activations: prefill with bf16 and with E4M3 outputs, decode."""
+    from layerwise_qk_norm_amd import inputs, ops
+    out = {}
+    for w in (inputs.PREFILL_E4M3, dataclasses.replace(inputs.PREFILL_E4M3, out_dtype="e4m3")):
+        _, gq, gk, bufs = device_workload(w, torch, sets=2)
+
+        def fused(i):
+            q, k, oq, ok = bufs[i % len(bufs)]
+            ops.layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps, out_q=oq, out_k=ok)
+
+        for i in range(args.warmup):
+            fused(i)
+        ms = timed(fused, args.steps, stream, torch)
+        if ops.check_fault() != ops.QKN_OK:
+            raise RuntimeError("E4M3 prefill reported an exchange timeout")
+        nbytes = w.algorithmic_bytes()
+        traffic = read_traffic(TRAFFIC_SUMMARY_E4M3) if w.out == "bf16" else None
+        out[f"prefill_to_{w.out}"] = {
+            "workload": f"T={w.T}, Q and K width {w.Hq}, E4M3 in, bf16 gamma, {w.out} out, "
+                        f"{w.n_shards} logical shards",
+            "algorithmic_bytes": nbytes, "ms": round(ms, 5),
+            "plan": ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards),
+            "roofline": roofline(nbytes, ms, traffic)}
+        del bufs
+        torch.cuda.empty_cache()
+    wd = inputs.DECODE_E4M3
+    _, dgq, dgk, dbufs = device_workload(wd, torch, sets=1)
+    q, k, oq, ok = dbufs[0]
+    ops.bench_fused(q, k, dgq, dgk, wd.n_shards, wd.eps, oq, ok, 200)
+    reps = 2000
+    c_us = timed(lambda _: ops.bench_fused(q, k, dgq, dgk, wd.n_shards, wd.eps, oq, ok, reps),
+                 1, stream, torch) * 1e3 / reps
+    if ops.check_fault() != ops.QKN_OK:
+        raise RuntimeError("E4M3 decode reported an exchange timeout")
+    out["decode"] = {"workload": "T=64, Q and K width 4096, E4M3 in and out, 4 logical shards",
+                     "device_us_per_call": round(c_us, 2)}
+    return out
 
 
 def cpu_baseline(w, d, budget_s=10.0):
@@ -151,10 +206,15 @@ def main():
         for i in range(5):
             fused(i)
             copy(i)
+        w8 = inputs.PREFILL_E4M3
+        _, gq8, gk8, b8 = device_workload(w8, torch, sets=1)
+        for i in range(5):
+            q, k, oq, ok = b8[0]
+            ops.layerwise_fwd(q, k, gq8, gk8, w8.n_shards, w8.eps, out_q=oq, out_k=ok)
         torch.cuda.synchronize()
         assert ops.check_fault() == ops.QKN_OK
-        log("pmc mode done: 5 fused prefill launches, 5 copy launches of "
-            f"{2 * w.T * (w.Hq + w.Hk) * w.elem_bytes // 2} bytes read")
+        log("pmc mode done: 5 fused bf16 prefill launches, 5 copy launches of "
+            f"{w.T * (w.Hq + w.Hk) * w.elem_bytes} bytes read, 5 fused E4M3->bf16 prefill launches")
         return
 
     for i in range(args.warmup):
@@ -210,6 +270,9 @@ def main():
     if ops.check_fault() != ops.QKN_OK:
         raise RuntimeError("decode reported an exchange timeout")
 
+    log("timing E4M3 activations ...")
+    e4m3 = bench_e4m3(args, torch, stream, timed)
+
     traffic = read_traffic()
     out = {
         "metric": METRIC,
@@ -239,6 +302,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
+        "e4m3": e4m3,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

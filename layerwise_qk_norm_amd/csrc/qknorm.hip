@@ -361,32 +361,29 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // Candidates (variant, data waves, rows, workgroups per CU). The tile must
     // fit the data threads' slots, and 2 * rows * N comm lanes must fit one
     // wave. Each candidate is scored by how far it lies, on a log scale, from
-    // about 20 KB of loads in flight per CU and about 8 waves per CU, with
-    // small preferences for more rows per tile, fuller slots and more vectors
-    // per thread. The rule and its constants were fitted to launch timings of
-    // 18 shapes on MI355X (mean 3 % from the best launch of each shape).
+    // about 32 KB of tile loads plus stores in flight per CU and about 8 waves
+    // per CU, with preferences for more rows per tile, fuller slots and more
+    // vectors per thread, and against a one-tile lag when there are peers to
+    // wait for. The rule and its constants were fitted to the timings of every
+    // candidate launch of 29 shapes of all four formats on MI355X (mean 4.6 %
+    // from the best launch of each shape).
     struct Best {
         int v = -1, w = 0, rows = 0, wpc = 0;
         double score = 0;
         int64_t wgs = 0;
     } best;
-    // With peers to wait for, the two-tile lag decouples partners; a lag-1
-    // variant is used only where no lag-2 variant holds the same slots.
-    auto has_lag2 = [&](int vpt) {
-        for (int v = 0; v < QKN_NUM_VARIANTS; ++v)
-            if (kVariants[v].lag == 2 && kVariants[v].vpt == vpt && variant_usable(dtype, v))
-                return true;
-        return false;
-    };
+    // A two-tile lag only helps when there are peers to wait for.
     auto allowed = [&](int v) {
         const Variant& k = kVariants[v];
         if (!variant_usable(dtype, v)) return false;
         if (g_opt.force_variant >= 0) return v == g_opt.force_variant;
-        if (N == 1) return k.lag == 1;
-        return k.lag == 2 || !has_lag2(k.vpt);
+        return N > 1 || k.lag == 1;
     };
     const int rows_cap = (int)std::min<int64_t>({(int64_t)qkn::kMaxRows, 32 / N, T});
+    const Fmt fm = fmt_of(dtype);
     const double batch = (double)T * (double)(wvq + wvk) * 16.0 * N;  // bytes read per call
+    const double io = 1.0 + (double)fm.out / (double)fm.in;           // (loads + stores) / loads
+    constexpr double kTarget = 32.0 * 1024;
     auto consider = [&](int v, int w, int r, int wpc) {
         const Variant& k = kVariants[v];
         const int64_t tv = tile_vectors(r);
@@ -397,15 +394,17 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         const int64_t groups = std::min<int64_t>(tiles, (int64_t)wpc * cu / N);
         if (groups < 1) return;
         const int64_t wgs = groups * N;
-        const double inflight = std::min((double)wgs * (double)(tv * 16), batch) / cu;
+        const double inflight = io * std::min((double)wgs * (double)(tv * 16), batch) / cu;
         const double waves = (double)wgs / cu * (w + 1);
         const double util = (double)tv / (double)(64 * w * k.vpt);
-        double sc = std::fabs(std::log2(std::max(inflight, 1.0) / (20.0 * 1024))) +
-                    0.5 * std::fabs(std::log2(std::max(waves, 0.1) / 8.0)) - 0.1 * r -
-                    0.5 * util - 0.2 * std::log2((double)k.vpt);
-        // a batch smaller than the in-flight target is latency-bound: every
-        // token gets its own workgroup group if the device can hold them
-        if (batch / cu < 20.0 * 1024) sc += std::log2((double)(T * N) / (double)wgs);
+        double sc = std::fabs(std::log2(std::max(inflight, 1.0) / kTarget)) +
+                    0.5 * std::fabs(std::log2(std::max(waves, 0.1) / 8.0)) - 0.2 * r -
+                    1.0 * util - 0.2 * std::log2((double)k.vpt);
+        if (N > 1 && k.lag == 1) sc += 0.5;
+        // a batch whose loads are smaller than the in-flight target is
+        // latency-bound: every token gets its own workgroup group if the device
+        // can hold them
+        if (batch / cu < kTarget) sc += std::log2((double)(T * N) / (double)wgs);
         if (best.v < 0 || sc < best.score) {
             best.v = v;
             best.w = w;
@@ -417,17 +416,23 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     };
     // Launches measured fastest on MI355X for the prefill-sized Q/K shards of
     // the letter's models (width 5120 split 1, 2, 4 or 8 ways; 5120/1024 split
-    // 4 ways), used for batches of at least 4096 tokens when nothing is forced
-    // and the device can hold them.
+    // 4 ways), for bf16 and E4M3 activations, used for batches of at least 4096
+    // tokens when nothing is forced and the device can hold them.
     struct Tuned {
         int dtype, wq, wk, n, v, w, rows, wpc;
     };
     static const Tuned kTuned[] = {
-        {QKN_BF16, 5120, 5120, 1, 4, 4, 1, 1},
-        {QKN_BF16, 2560, 2560, 2, 9, 5, 2, 1},
-        {QKN_BF16, 1280, 1280, 4, 7, 10, 4, 1},
-        {QKN_BF16, 640, 640, 8, 8, 3, 3, 2},
-        {QKN_BF16, 1280, 256, 4, 8, 2, 2, 3},
+        {QKN_FMT_BF16, 5120, 5120, 1, 4, 4, 1, 1},
+        {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 2, 1},
+        {QKN_FMT_BF16, 1280, 1280, 4, 7, 10, 4, 1},
+        {QKN_FMT_BF16, 640, 640, 8, 8, 3, 3, 2},
+        {QKN_FMT_BF16, 1280, 256, 4, 8, 2, 2, 3},
+        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 1, 5, 1, 1},
+        {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 5, 2, 1},
+        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 3, 2, 2},
+        {QKN_FMT_E4M3_BF16, 640, 640, 8, 7, 3, 4, 2},
+        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 7, 3, 4, 2},
+        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 0, 10, 2, 2},
     };
     const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0;
     if (!forced && T >= 4096) {

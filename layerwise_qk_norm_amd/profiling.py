@@ -89,10 +89,11 @@ def _per_kernel(csv_path: str):
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, out_txt: str, cmd_fetch: str,
-                      cmd_write: str, algorithmic_bytes: int):
+                      cmd_write: str, algorithmic_bytes: int, kernel: str = "fused_qknorm_kernel<qkn::Bf16",
+                      title: str = "fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)"):
     fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
     copy_name = next(n for n in fetch if "copy2_kernel" in n)
-    fused_name = next(n for n in fetch if "fused_qknorm_kernel" in n)
+    fused_name = next(n for n in fetch if kernel in n)
     kib_copy_f = statistics.mean(fetch[copy_name])
     kib_copy_w = statistics.mean(write[copy_name])
     scale_f = (COPY_BYTES / 1024) / kib_copy_f
@@ -103,7 +104,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_txt: str, cmd_fetch: s
     written = kib_w * scale_w * 1024
     traffic = fetched + written
     lines = [
-        "# HBM traffic of the fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)",
+        f"# HBM traffic of the {title}",
         f"# command (FETCH_SIZE): {cmd_fetch}",
         f"# command (WRITE_SIZE): {cmd_write}",
         f"# copy kernel of known size: {COPY_BYTES} B read and {COPY_BYTES} B written",
@@ -143,12 +144,15 @@ def main():
     f.add_argument("--cmd-fetch", required=True)
     f.add_argument("--cmd-write", required=True)
     f.add_argument("--algorithmic-bytes", type=int, default=671_109_120)
+    f.add_argument("--kernel", default="fused_qknorm_kernel<qkn::Bf16",
+                   help="substring of the kernel name to summarise")
+    f.add_argument("--title", default="fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)")
     a = ap.parse_args()
     if a.what == "trace":
         summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note, a.kernel_trace, a.window)
     else:
         summarize_traffic(a.fetch_csv, a.write_csv, a.out_txt, a.cmd_fetch, a.cmd_write,
-                          a.algorithmic_bytes)
+                          a.algorithmic_bytes, a.kernel, a.title)
 
 
 if __name__ == "__main__":

@@ -78,7 +78,9 @@ enum {
     QKN_FMT_F32 = 1,        /* f32 / f32 / f32 */
     QKN_FMT_E4M3_BF16 = 2,  /* e4m3 / bf16 / bf16 */
     QKN_FMT_E4M3_E4M3 = 3,  /* e4m3 / bf16 / e4m3 */
-    QKN_NUM_FORMATS = 4
+    QKN_FMT_LN_BF16 = 4,    /* LayerNorm, bf16 / bf16 (gamma, beta) / bf16 */
+    QKN_FMT_LN_F32 = 5,     /* LayerNorm, f32 / f32 (gamma, beta) / f32 */
+    QKN_NUM_FORMATS = 6
 };
 
 #define QKN_MAX_SHARDS 32
@@ -118,6 +120,51 @@ int qknorm_layerwise_fwd_e4m3(const void* q, const void* k, const void* gamma_q,
                               const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
                               int n_shards, float eps, void* out_q, void* out_k,
                               int out_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------ LayerNorm
+ * The same decomposition applied to LayerNorm (the reading notes' extension,
+ * Section 5e): mean and variance of the full vector follow from two additive
+ * statistics per shard, sum x and sum x^2, exchanged and combined (ascending
+ * shard order) like the RMSNorm partial while x*gamma proceeds:
+ *
+ *   mu = S1 / H,  var = max(S2 / H - mu^2, 0),  rstd = 1 / sqrt(var + eps),
+ *   y[t][j] = (x[t][j] - mu) * rstd * gamma[j] + beta[j]
+ *
+ * computed as (x*gamma)*rstd + (beta - mu*rstd*gamma) in fp32. Arguments as
+ * for the fused RMSNorm entry points, plus beta_q [Hq] and beta_k [Hk] in the
+ * suffix dtype; a null beta means no shift. Shards of one token exchange
+ * 2 x 2 x n_shards scalars, so the fused kernel holds at most 16 shards (more
+ * run the split kernels below from the same entry point). The variance is
+ * formed from the two sums in fp32: rows whose mean is large against their
+ * spread lose relative accuracy in rstd (cancellation in S2/H - mu^2).
+ */
+int qknorm_layernorm_fwd_bf16(const void* q, const void* k, const void* gamma_q,
+                              const void* gamma_k, const void* beta_q, const void* beta_k,
+                              int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
+                              void* out_q, void* out_k, hipStream_t stream);
+int qknorm_layernorm_fwd_f32(const void* q, const void* k, const void* gamma_q,
+                             const void* gamma_k, const void* beta_q, const void* beta_k,
+                             int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
+                             void* out_q, void* out_k, hipStream_t stream);
+
+/* LayerNorm split into three launches for one tensor:
+ * qknorm_shard_stats_*: sums[s * T + t] and sumsq[s * T + t], fp32 [n_shards][T]
+ *   each, over shard s's columns.
+ * qknorm_combine_stats: mean[t] and rstd[t] (fp32 [T]) from them, as above.
+ * qknorm_apply_norm_*: out = (x*gamma)*rstd + (beta - mean*rstd*gamma); beta may
+ *   be null. */
+int qknorm_shard_stats_bf16(const void* x, int64_t T, int64_t H, int n_shards, float* sums,
+                            float* sumsq, hipStream_t stream);
+int qknorm_shard_stats_f32(const void* x, int64_t T, int64_t H, int n_shards, float* sums,
+                           float* sumsq, hipStream_t stream);
+int qknorm_combine_stats(const float* sums, const float* sumsq, int64_t T, int64_t H,
+                         int n_shards, float eps, float* mean, float* rstd, hipStream_t stream);
+int qknorm_apply_norm_bf16(const void* x, const void* gamma, const void* beta,
+                           const float* mean, const float* rstd, int64_t T, int64_t H,
+                           void* out, hipStream_t stream);
+int qknorm_apply_norm_f32(const void* x, const void* gamma, const void* beta,
+                          const float* mean, const float* rstd, int64_t T, int64_t H,
+                          void* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------ split
  * The same computation for one tensor as three stream-ordered launches, with
@@ -190,7 +237,8 @@ int qknorm_release_workspace(void);
  * 16-byte vectors per data thread (5: fp32 only) and scale a tile one
  * iteration after reducing it; variants 6-9 hold 1, 2, 3, 4 and scale it two
  * iterations later, which decouples the shards of a group further. The e4m3
- * formats have variants 0, 1, 2, 6 and 7 (a 16-byte vector is 16 columns).
+ * formats have variants 0, 1, 2, 6 and 7 (a 16-byte vector is 16 columns);
+ * the LayerNorm formats have all but variant 5.
  * `dtype` is a format (QKN_FMT_*). */
 #define QKN_NUM_VARIANTS 10
 #define QKN_MAX_DATA_WAVES 15

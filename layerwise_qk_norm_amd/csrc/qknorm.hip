@@ -32,20 +32,25 @@ using qkn::FusedParams;
 // ---------------------------------------------------------------- formats
 
 // Element sizes of x, gamma and y of a format; `ev` columns per 16-byte
-// vector of x, `kgam` 16-byte words of gamma per vector.
+// vector of x, `kgam` 16-byte words of gamma per vector; `stats` statistics
+// per token and shard (1: sum of squares; 2 for LayerNorm: also the sum) and
+// `params` per-column vectors staged in LDS (gamma; LayerNorm: and beta).
 struct Fmt {
-    int in, gam, out, ev, kgam;
+    int in, gam, out, ev, kgam, stats, params;
 };
 bool fmt_valid(int f) { return f >= 0 && f < QKN_NUM_FORMATS; }
 Fmt fmt_of(int f)
 {
     switch (f) {
-    case QKN_FMT_BF16: return {2, 2, 2, 8, 1};
-    case QKN_FMT_F32: return {4, 4, 4, 4, 1};
-    case QKN_FMT_E4M3_BF16: return {1, 2, 2, 16, 2};
-    default: return {1, 2, 1, 16, 2};  // QKN_FMT_E4M3_E4M3
+    case QKN_FMT_BF16: return {2, 2, 2, 8, 1, 1, 1};
+    case QKN_FMT_F32: return {4, 4, 4, 4, 1, 1, 1};
+    case QKN_FMT_E4M3_BF16: return {1, 2, 2, 16, 2, 1, 1};
+    case QKN_FMT_E4M3_E4M3: return {1, 2, 1, 16, 2, 1, 1};
+    case QKN_FMT_LN_BF16: return {2, 2, 2, 8, 1, 2, 2};
+    default: return {4, 4, 4, 4, 1, 2, 2};  // QKN_FMT_LN_F32
     }
 }
+bool is_layernorm(int f) { return f == QKN_FMT_LN_BF16 || f == QKN_FMT_LN_F32; }
 // format of an E4M3 call with output dtype `out` (QKN_BF16 or QKN_E4M3), or -1
 int e4m3_fmt(int out)
 {
@@ -129,13 +134,33 @@ FusedFn fused_fn_e4m3(int v)
     default: return nullptr;
     }
 }
+// LayerNorm (NORM = 1) for bf16 and fp32: every variant except 5, whose gamma
+// and beta images would not fit in LDS
+template <class DT>
+FusedFn fused_fn_ln(int v)
+{
+    switch (v) {
+    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1, 1024, 1>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1, 1024, 1>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1, 1024, 1>;
+    case 3: return qkn::fused_qknorm_kernel<DT, 4, true, 1, 1024, 1>;
+    case 4: return qkn::fused_qknorm_kernel<DT, 6, true, 1, 512, 1>;
+    case 6: return qkn::fused_qknorm_kernel<DT, 1, true, 2, 1024, 1>;
+    case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024, 1>;
+    case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768, 1>;
+    case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512, 1>;
+    default: return nullptr;
+    }
+}
 FusedFn fused_fn_for(int fmt, int v)
 {
     switch (fmt) {
     case QKN_FMT_BF16: return fused_fn<Bf16>(v);
     case QKN_FMT_F32: return fused_fn<F32>(v);
     case QKN_FMT_E4M3_BF16: return fused_fn_e4m3<E4m3Bf16>(v);
-    default: return fused_fn_e4m3<E4m3E4m3>(v);
+    case QKN_FMT_E4M3_E4M3: return fused_fn_e4m3<E4m3E4m3>(v);
+    case QKN_FMT_LN_BF16: return fused_fn_ln<Bf16>(v);
+    default: return fused_fn_ln<F32>(v);
     }
 }
 bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
@@ -143,14 +168,17 @@ bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E
 // data waves a workgroup of variant v may have (launch bound / 64, minus the comm wave)
 int max_data_waves(int fmt, int v)
 {
-    const int t = is_e4m3(fmt) ? kE4m3MaxThreads[v] : kVariants[v].max_threads;
+    int t = is_e4m3(fmt) ? kE4m3MaxThreads[v] : kVariants[v].max_threads;
+    if (is_layernorm(fmt) && v == 4) t = 512;  // gamma and beta need more registers
     return t / 64 - 1;
 }
 
-// dynamic LDS of a launch: gamma in slot order (kgam 16-byte words per slot)
+// dynamic LDS of a launch: gamma (and LayerNorm's beta) in slot order, kgam
+// 16-byte words per slot each
 size_t gamma_lds_bytes(int fmt, int v, int nwd)
 {
-    return (size_t)kVariants[v].vpt * 64 * nwd * 16 * fmt_of(fmt).kgam;
+    const Fmt f = fmt_of(fmt);
+    return (size_t)kVariants[v].vpt * 64 * nwd * 16 * f.kgam * f.params;
 }
 
 // ---------------------------------------------------------------- options
@@ -379,8 +407,9 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         if (g_opt.force_variant >= 0) return v == g_opt.force_variant;
         return N > 1 || k.lag == 1;
     };
-    const int rows_cap = (int)std::min<int64_t>({(int64_t)qkn::kMaxRows, 32 / N, T});
     const Fmt fm = fmt_of(dtype);
+    // comm lanes: stats x 2 tensors x rows x N slots in one wave
+    const int rows_cap = (int)std::min<int64_t>({(int64_t)qkn::kMaxRows, 32 / (N * fm.stats), T});
     const double batch = (double)T * (double)(wvq + wvk) * 16.0 * N;  // bytes read per call
     const double io = 1.0 + (double)fm.out / (double)fm.in;           // (loads + stores) / loads
     constexpr double kTarget = 32.0 * 1024;
@@ -569,11 +598,71 @@ int launch_apply(int fmt, const void* x, const void* g, const float* rinv, int64
     return QKN_OK;
 }
 
+template <class DT>
+void launch_stats_as(bool vec, dim3 g, dim3 b, hipStream_t s, const void* x, int64_t T, int H,
+                     int N, float* sums, float* sumsq)
+{
+    if (vec) hipLaunchKernelGGL((qkn::shard_stats_kernel<DT, true>), g, b, 0, s, x, T, H, N, sums, sumsq);
+    else hipLaunchKernelGGL((qkn::shard_stats_kernel<DT, false>), g, b, 0, s, x, T, H, N, sums, sumsq);
+}
+
+int launch_stats(int fmt, const void* x, int64_t T, int64_t H, int N, float* sums, float* sumsq,
+                 hipStream_t s)
+{
+    const int64_t blocks = (T * N + 3) / 4;
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    const int W = (int)(H / N);
+    const bool vec = aligned16(x) && ((int64_t)W * fmt_of(fmt).in) % 16 == 0;
+    dim3 g((unsigned)blocks), b(256);
+    if (fmt_of(fmt).in == 2) launch_stats_as<Bf16>(vec, g, b, s, x, T, (int)H, N, sums, sumsq);
+    else launch_stats_as<F32>(vec, g, b, s, x, T, (int)H, N, sums, sumsq);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+int launch_combine_stats(const float* sums, const float* sumsq, int64_t T, int64_t H, int N,
+                         float eps, float* mean, float* rstd, hipStream_t s)
+{
+    const int64_t blocks = (T + 255) / 256;
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    hipLaunchKernelGGL(qkn::combine_stats_kernel, dim3((unsigned)blocks), dim3(256), 0, s, sums,
+                       sumsq, T, (int)H, N, eps, mean, rstd);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+template <class DT>
+void launch_norm_as(bool vec, dim3 gr, dim3 b, hipStream_t s, const void* x, const void* g,
+                    const void* bt, const float* mean, const float* rstd, int64_t T, int H, int rpb,
+                    void* y)
+{
+    if (vec) hipLaunchKernelGGL((qkn::apply_norm_kernel<DT, true>), gr, b, 0, s, x, g, bt, mean, rstd, T, H, rpb, y);
+    else hipLaunchKernelGGL((qkn::apply_norm_kernel<DT, false>), gr, b, 0, s, x, g, bt, mean, rstd, T, H, rpb, y);
+}
+
+int launch_apply_norm(int fmt, const void* x, const void* g, const void* bt, const float* mean,
+                      const float* rstd, int64_t T, int64_t H, void* y, hipStream_t s)
+{
+    const Fmt f = fmt_of(fmt);
+    const bool vec = aligned16(x) && aligned16(g) && (!bt || aligned16(bt)) && aligned16(y) &&
+                     (H * f.in) % 16 == 0;
+    const int64_t per_row = vec ? H * f.in / 16 : H;
+    const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, 2048 / per_row));
+    const int64_t blocks = (T + rpb - 1) / rpb;
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    dim3 gr((unsigned)blocks), b(256);
+    if (f.in == 2) launch_norm_as<Bf16>(vec, gr, b, s, x, g, bt, mean, rstd, T, (int)H, rpb, y);
+    else launch_norm_as<F32>(vec, gr, b, s, x, g, bt, mean, rstd, T, (int)H, rpb, y);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
 // ---------------------------------------------------------------- fused entry
 
+// bq, bk: LayerNorm's beta (either may be null); null for the RMSNorm formats
 int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const void* gk,
-                  int64_t T, int64_t Hq, int64_t Hk, int N, float eps, void* oq, void* ok,
-                  hipStream_t stream)
+                  const void* bq, const void* bk, int64_t T, int64_t Hq, int64_t Hk, int N,
+                  float eps, void* oq, void* ok, hipStream_t stream)
 {
     t_hip_error.clear();
     int rc = check_dims(T, Hq, N);
@@ -592,6 +681,11 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     if (overlaps(rok, rk) && !same(rok, rk)) return QKN_EOVERLAP;
     if (overlaps(roq, rk) || overlaps(roq, rgq) || overlaps(roq, rgk)) return QKN_EOVERLAP;
     if (overlaps(rok, rq) || overlaps(rok, rgq) || overlaps(rok, rgk)) return QKN_EOVERLAP;
+    if (bq || bk) {
+        const Range rbq = range_of(bq, bq ? Hq * f.gam : 0), rbk = range_of(bk, bk ? Hk * f.gam : 0);
+        if (overlaps(roq, rbq) || overlaps(roq, rbk) || overlaps(rok, rbq) || overlaps(rok, rbk))
+            return QKN_EOVERLAP;
+    }
 
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     QKN_HIP(hipStreamIsCapturing(stream, &cap));
@@ -606,7 +700,8 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     if ((rc = workspace_for(dev, stream, &ws))) return rc;
 
     const int aligned = aligned16(q) && aligned16(k) && aligned16(gq) && aligned16(gk) &&
-                        aligned16(oq) && aligned16(ok);
+                        aligned16(oq) && aligned16(ok) && (!bq || aligned16(bq)) &&
+                        (!bk || aligned16(bk));
     static std::map<PlanKey, qknorm_plan> cache;
     const PlanKey key{dev, dtype, N, aligned, T, Hq, Hk, g_opt_epoch};
     qknorm_plan pl;
@@ -619,6 +714,27 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
         cache.emplace(key, pl);
     }
 
+    if (pl.variant < 0 && is_layernorm(dtype)) {
+        // LayerNorm with the three split kernels, per tensor
+        const size_t need = (size_t)(2 * N + 2) * (size_t)T;
+        if ((rc = ensure_scratch(ws, need, stream))) return rc;
+        float* sums = ws->scratch;
+        float* sumsq = sums + (size_t)N * T;
+        float* mean = sumsq + (size_t)N * T;
+        float* rstd = mean + T;
+        const void* xs[2] = {q, k};
+        const void* gs[2] = {gq, gk};
+        const void* bs[2] = {bq, bk};
+        void* ys[2] = {oq, ok};
+        const int64_t Hs[2] = {Hq, Hk};
+        for (int i = 0; i < 2; ++i) {
+            if ((rc = launch_stats(dtype, xs[i], T, Hs[i], N, sums, sumsq, stream))) return rc;
+            if ((rc = launch_combine_stats(sums, sumsq, T, Hs[i], N, eps, mean, rstd, stream))) return rc;
+            if ((rc = launch_apply_norm(dtype, xs[i], gs[i], bs[i], mean, rstd, T, Hs[i], ys[i], stream)))
+                return rc;
+        }
+        return QKN_OK;
+    }
     if (pl.variant < 0) {
         // Shapes the fused kernel cannot hold in registers (or unaligned): the
         // same computation with the three split kernels, per tensor.
@@ -638,7 +754,8 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
         return QKN_OK;
     }
 
-    const size_t entries = (size_t)pl.n_groups * 2 * kVariants[pl.variant].lag * N * 2 * pl.rows;
+    const size_t entries =
+        (size_t)pl.n_groups * 2 * kVariants[pl.variant].lag * N * f.stats * 2 * pl.rows;
     if ((rc = ensure_slots(ws, entries, stream))) return rc;
     if ((uint64_t)ws->tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
         // tags would wrap: clear every slot so no stale tag can match
@@ -652,6 +769,8 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     p.x[1] = k;
     p.gamma[0] = gq;
     p.gamma[1] = gk;
+    p.beta[0] = bq;
+    p.beta[1] = bk;
     p.y[0] = oq;
     p.y[1] = ok;
     p.T = T;
@@ -725,16 +844,16 @@ int qknorm_layerwise_fwd_bf16(const void* q, const void* k, const void* gamma_q,
                               int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
                               void* out_q, void* out_k, hipStream_t stream)
 {
-    return layerwise_fwd(QKN_BF16, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps, out_q, out_k,
-                         stream);
+    return layerwise_fwd(QKN_BF16, q, k, gamma_q, gamma_k, nullptr, nullptr, T, Hq, Hk, n_shards,
+                         eps, out_q, out_k, stream);
 }
 
 int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
                              int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
                              void* out_q, void* out_k, hipStream_t stream)
 {
-    return layerwise_fwd(QKN_F32, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps, out_q, out_k,
-                         stream);
+    return layerwise_fwd(QKN_F32, q, k, gamma_q, gamma_k, nullptr, nullptr, T, Hq, Hk, n_shards,
+                         eps, out_q, out_k, stream);
 }
 
 int qknorm_layerwise_fwd_e4m3(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
@@ -743,8 +862,8 @@ int qknorm_layerwise_fwd_e4m3(const void* q, const void* k, const void* gamma_q,
 {
     const int fmt = e4m3_fmt(out_dtype);
     if (fmt < 0) return QKN_EINVAL;
-    return layerwise_fwd(fmt, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps, out_q, out_k,
-                         stream);
+    return layerwise_fwd(fmt, q, k, gamma_q, gamma_k, nullptr, nullptr, T, Hq, Hk, n_shards, eps,
+                         out_q, out_k, stream);
 }
 
 int qknorm_shard_sumsq_bf16(const void* x, int64_t T, int64_t H, int n_shards, float* partials,
@@ -797,6 +916,97 @@ int qknorm_apply_scale_e4m3(const void* x, const void* gamma, const float* rms_i
     const int fmt = e4m3_fmt(out_dtype);
     if (fmt < 0) return QKN_EINVAL;
     return apply_scale(fmt, x, gamma, rms_inv, T, H, out, stream);
+}
+
+int qknorm_layernorm_fwd_bf16(const void* q, const void* k, const void* gamma_q,
+                              const void* gamma_k, const void* beta_q, const void* beta_k,
+                              int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
+                              void* out_q, void* out_k, hipStream_t stream)
+{
+    return layerwise_fwd(QKN_FMT_LN_BF16, q, k, gamma_q, gamma_k, beta_q, beta_k, T, Hq, Hk,
+                         n_shards, eps, out_q, out_k, stream);
+}
+
+int qknorm_layernorm_fwd_f32(const void* q, const void* k, const void* gamma_q,
+                             const void* gamma_k, const void* beta_q, const void* beta_k,
+                             int64_t T, int64_t Hq, int64_t Hk, int n_shards, float eps,
+                             void* out_q, void* out_k, hipStream_t stream)
+{
+    return layerwise_fwd(QKN_FMT_LN_F32, q, k, gamma_q, gamma_k, beta_q, beta_k, T, Hq, Hk,
+                         n_shards, eps, out_q, out_k, stream);
+}
+
+static int shard_stats_entry(int fmt, const void* x, int64_t T, int64_t H, int N, float* sums,
+                             float* sumsq, hipStream_t s)
+{
+    t_hip_error.clear();
+    int rc = check_dims(T, H, N);
+    if (rc) return rc;
+    if (T == 0) return QKN_OK;
+    if (!x || !sums || !sumsq) return QKN_EINVAL;
+    const Range rx = range_of(x, T * H * fmt_of(fmt).in);
+    const Range ra = range_of(sums, (int64_t)N * T * 4), rb = range_of(sumsq, (int64_t)N * T * 4);
+    if (overlaps(ra, rx) || overlaps(rb, rx) || overlaps(ra, rb)) return QKN_EOVERLAP;
+    return launch_stats(fmt, x, T, H, N, sums, sumsq, s);
+}
+
+int qknorm_shard_stats_bf16(const void* x, int64_t T, int64_t H, int n_shards, float* sums,
+                            float* sumsq, hipStream_t stream)
+{
+    return shard_stats_entry(QKN_FMT_LN_BF16, x, T, H, n_shards, sums, sumsq, stream);
+}
+
+int qknorm_shard_stats_f32(const void* x, int64_t T, int64_t H, int n_shards, float* sums,
+                           float* sumsq, hipStream_t stream)
+{
+    return shard_stats_entry(QKN_FMT_LN_F32, x, T, H, n_shards, sums, sumsq, stream);
+}
+
+int qknorm_combine_stats(const float* sums, const float* sumsq, int64_t T, int64_t H, int n_shards,
+                         float eps, float* mean, float* rstd, hipStream_t stream)
+{
+    t_hip_error.clear();
+    int rc = check_dims(T, H, n_shards);
+    if (rc) return rc;
+    if (!eps_ok(eps)) return QKN_EINVAL;
+    if (T == 0) return QKN_OK;
+    if (!sums || !sumsq || !mean || !rstd) return QKN_EINVAL;
+    const Range ra = range_of(sums, (int64_t)n_shards * T * 4);
+    const Range rb = range_of(sumsq, (int64_t)n_shards * T * 4);
+    const Range rm = range_of(mean, T * 4), rr = range_of(rstd, T * 4);
+    if (overlaps(rm, ra) || overlaps(rm, rb) || overlaps(rr, ra) || overlaps(rr, rb) ||
+        overlaps(rm, rr))
+        return QKN_EOVERLAP;
+    return launch_combine_stats(sums, sumsq, T, H, n_shards, eps, mean, rstd, stream);
+}
+
+static int apply_norm_entry(int fmt, const void* x, const void* g, const void* b, const float* mean,
+                            const float* rstd, int64_t T, int64_t H, void* y, hipStream_t s)
+{
+    t_hip_error.clear();
+    int rc = check_dims(T, H, 1);
+    if (rc) return rc;
+    if (T == 0) return QKN_OK;
+    if (!x || !g || !mean || !rstd || !y) return QKN_EINVAL;
+    const Fmt f = fmt_of(fmt);
+    const Range ry = range_of(y, T * H * f.out), rx = range_of(x, T * H * f.in);
+    if (overlaps(ry, rx) && !same(ry, rx)) return QKN_EOVERLAP;
+    if (overlaps(ry, range_of(g, H * f.gam)) || overlaps(ry, range_of(mean, T * 4)) ||
+        overlaps(ry, range_of(rstd, T * 4)) || (b && overlaps(ry, range_of(b, H * f.gam))))
+        return QKN_EOVERLAP;
+    return launch_apply_norm(fmt, x, g, b, mean, rstd, T, H, y, s);
+}
+
+int qknorm_apply_norm_bf16(const void* x, const void* gamma, const void* beta, const float* mean,
+                           const float* rstd, int64_t T, int64_t H, void* out, hipStream_t stream)
+{
+    return apply_norm_entry(QKN_FMT_LN_BF16, x, gamma, beta, mean, rstd, T, H, out, stream);
+}
+
+int qknorm_apply_norm_f32(const void* x, const void* gamma, const void* beta, const float* mean,
+                          const float* rstd, int64_t T, int64_t H, void* out, hipStream_t stream)
+{
+    return apply_norm_entry(QKN_FMT_LN_F32, x, gamma, beta, mean, rstd, T, H, out, stream);
 }
 
 int qknorm_check_fault(hipStream_t stream)
@@ -960,8 +1170,8 @@ int qknorm_bench_fused(int dtype, const void* q, const void* k, const void* gamm
     if (!fmt_valid(dtype)) return QKN_EINVAL;
     if (repeats < 0) return QKN_EINVAL;
     for (int i = 0; i < repeats; ++i) {
-        const int rc = layerwise_fwd(dtype, q, k, gamma_q, gamma_k, T, Hq, Hk, n_shards, eps,
-                                     out_q, out_k, stream);
+        const int rc = layerwise_fwd(dtype, q, k, gamma_q, gamma_k, nullptr, nullptr, T, Hq, Hk,
+                                     n_shards, eps, out_q, out_k, stream);
         if (rc) return rc;
     }
     return QKN_OK;

@@ -235,6 +235,7 @@ constexpr int kMaxSeg = 2 * kMaxRows;
 struct FusedParams {
     const void* x[2];      // q, k            [T][H[i]]
     const void* gamma[2];  // gamma_q, gamma_k [H[i]]
+    const void* beta[2];   // LayerNorm only: beta_q, beta_k [H[i]] or null (no shift)
     void* y[2];            // out_q, out_k    [T][H[i]]
     int64_t T;
     int64_t n_tiles;
@@ -247,7 +248,7 @@ struct FusedParams {
     int32_t xcd_map;
     float eps;
     uint32_t tag_base;     // tag of a group's first tile; its tile k uses tag_base + k
-    unsigned long long* slots;  // [n_groups][2][n_shards][2*rows]
+    unsigned long long* slots;  // [n_groups][2*LAG][n_shards][stats*2*rows]
     uint32_t* fault;
     uint64_t spin_ticks;   // wall-clock ticks a comm wave may wait for one tile
     uint32_t test_flags;   // bit 0: never publish (forces the timeout path)
@@ -262,6 +263,13 @@ struct FusedParams {
 // gamma is staged once, in slot order, in LDS (dynamic shared memory of
 // VPT * 64 * nwd * 16 bytes).
 //
+// NORM = 1 computes LayerNorm instead of RMSNorm (reading notes, Section 5e):
+// each shard reduces two additive statistics per segment, sum x and sum x^2,
+// which travel as two tagged slots; the comm wave forms mu = S1/H,
+// var = max(S2/H - mu^2, 0) and rstd = 1/sqrt(var + eps); Phase C computes
+// y = u*rstd + (beta - mu*rstd*gamma) with u = x*gamma from Phase B, reading
+// gamma and beta (staged after gamma in LDS) again.
+//
 // Pipeline: a group's tiles k = 0..K-1 go through one barrier per iteration.
 // In iteration k the data waves issue the loads of tile k+1, reduce tile k
 // (Phase A), pass the barrier, scale and store tile k-LAG (Phase C), and form
@@ -272,7 +280,7 @@ struct FusedParams {
 // partners without waiting, and the exchange overlaps the loads of the next
 // tiles and the products x*gamma. u is held for LAG tiles; the slot ring is
 // 2*LAG deep; red and rinv_s are double-buffered by tile parity.
-template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT>
+template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT, int NORM = 0>
 __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
@@ -282,9 +290,11 @@ fused_qknorm_kernel(FusedParams p)
     constexpr int KG = DT::kGam;
     constexpr int KO = DT::kOut;
 
-    __shared__ float red[2][kMaxDataWaves][kMaxSeg];  // per-wave partial sums, by tile parity
-    __shared__ float rinv_s[2][kMaxSeg];              // combined reciprocal RMS, by tile parity
-    extern __shared__ u32x4 gam_lds[];                // gamma in slot order, KG words per slot
+    constexpr int NSTAT = NORM ? 2 : 1;                       // statistics per segment
+    __shared__ float red[2][kMaxDataWaves][kMaxSeg * NSTAT];  // per-wave partials, by tile parity
+    __shared__ float rinv_s[2][kMaxSeg];                      // reciprocal RMS / rstd, by parity
+    __shared__ float mu_s[2][NORM ? kMaxSeg : 1];             // LayerNorm mean, by parity
+    extern __shared__ u32x4 gam_lds[];  // gamma in slot order, KG words per slot (then beta)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -319,9 +329,12 @@ fused_qknorm_kernel(FusedParams p)
 
     if (wave == 0) {
         // ================= comm wave: acquire, combine, publish =============
-        const int kk = lane / nseg;  // shard of the slot this lane watches
-        const int sg = lane - kk * nseg;  // segment of that slot
-        const bool active = lane < N * nseg;
+        // slots of one shard: nst = NSTAT*nseg, segment statistic sg (for
+        // LayerNorm sg < nseg is sum x^2 and sg >= nseg is sum x, of segment sg - nseg)
+        const int nst = NSTAT * nseg;
+        const int kk = lane / nst;   // shard of the slot this lane watches
+        const int sg = lane - kk * nst;  // statistic of that slot
+        const bool active = lane < N * nst;
         const bool mine = active && kk == shard;
         const bool peer = active && kk != shard;
         const float Hf = (float)(sg < rows ? p.H[0] : p.H[1]);
@@ -333,7 +346,7 @@ fused_qknorm_kernel(FusedParams p)
                 // ---- Phase B comm path for tile k-LAG ---------------------------
                 const int j = k - LAG;
                 const unsigned long long* slot =
-                    p.slots + ((size_t)(group * RING + (j % RING)) * N) * nseg + lane;
+                    p.slots + ((size_t)(group * RING + (j % RING)) * N) * nst + lane;
                 const uint32_t want = p.tag_base + (uint32_t)j;
                 const float own_prev = (LAG == 2 && (j & 1)) ? own1 : own0;
                 float v = mine ? own_prev : 0.f;
@@ -359,8 +372,18 @@ fused_qknorm_kernel(FusedParams p)
                 }
                 // S = sum over shards 0..N-1 in ascending order (same on every shard)
                 float S = 0.f;
-                for (int k2 = 0; k2 < N; ++k2) S += __shfl(v, k2 * nseg + sg);
-                if (lane < nseg) rinv_s[j & 1][lane] = 1.0f / sqrtf(S / Hf + p.eps);
+                for (int k2 = 0; k2 < N; ++k2) S += __shfl(v, k2 * nst + sg);
+                if constexpr (NORM == 0) {
+                    if (lane < nseg) rinv_s[j & 1][lane] = 1.0f / sqrtf(S / Hf + p.eps);
+                } else {
+                    const float S1 = __shfl(S, (lane + nseg) & 63);  // sum x of segment `lane`
+                    if (lane < nseg) {
+                        const float mu = S1 / Hf;
+                        const float var = fmaxf(fmaf(-mu, mu, S / Hf), 0.0f);
+                        rinv_s[j & 1][lane] = 1.0f / sqrtf(var + p.eps);
+                        mu_s[j & 1][lane] = mu;
+                    }
+                }
             }
             __syncthreads();  // red[k&1] written; rinv_s[(k-LAG)&1] ready
             if (k < K && mine) {
@@ -372,7 +395,7 @@ fused_qknorm_kernel(FusedParams p)
                 if (LAG == 2 && (k & 1)) own1 = own; else own0 = own;
                 if (N > 1 && !(p.test_flags & 1u)) {
                     unsigned long long* slot =
-                        p.slots + ((size_t)(group * RING + (k % RING)) * N) * nseg + lane;
+                        p.slots + ((size_t)(group * RING + (k % RING)) * N) * nst + lane;
                     slot_publish(slot, p.tag_base + (uint32_t)k, own);
                 }
             }
@@ -430,6 +453,15 @@ fused_qknorm_kernel(FusedParams p)
             gam_lds[(i * ndt + dt) * KG + g] =
                 valid ? ld_cached(static_cast<const gam_t*>(p.gamma[t]) + col + g * (16 / (int)sizeof(gam_t)))
                       : u32x4{0, 0, 0, 0};
+        if constexpr (NORM) {
+            // beta after gamma's VPT * ndt * KG words; a null beta stages zeros
+            const gam_t* bt = static_cast<const gam_t*>(p.beta[t]);
+#pragma unroll
+            for (int g = 0; g < KG; ++g)
+                gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] =
+                    (valid && bt) ? ld_cached(bt + col + g * (16 / (int)sizeof(gam_t)))
+                                  : u32x4{0, 0, 0, 0};
+        }
     }
 
     auto tile_of = [&](int k) __attribute__((always_inline)) -> int64_t { return group + (int64_t)k * p.n_groups; };
@@ -451,10 +483,16 @@ fused_qknorm_kernel(FusedParams p)
             buf[i] = __builtin_amdgcn_raw_buffer_load_b128(tk[i] ? rk : rq, voff[i], 0, kNT);
     };
     // ---- Phase A: local sums of squares (fp32) of the tile in buf -> red[par]
+    // (LayerNorm: also the sums of x, after the sums of squares in red[par])
     auto phase_a = [&](const u32x4 (&buf)[VPT], int par) __attribute__((always_inline)) {
         float acc[kMaxSeg];
+        float acc1[NORM ? kMaxSeg : 1];
 #pragma unroll
         for (int s = 0; s < kMaxSeg; ++s) acc[s] = 0.f;
+        if constexpr (NORM) {
+#pragma unroll
+            for (int s = 0; s < kMaxSeg; ++s) acc1[s] = 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             float f[EV];
@@ -464,12 +502,23 @@ fused_qknorm_kernel(FusedParams p)
             for (int e = 0; e < EV; ++e) sq = fmaf(f[e], f[e], sq);
 #pragma unroll
             for (int s = 0; s < kMaxSeg; ++s) acc[s] += (seg[i] == s) ? sq : 0.f;
+            if constexpr (NORM) {
+                float sm = 0.f;
+#pragma unroll
+                for (int e = 0; e < EV; ++e) sm += f[e];
+#pragma unroll
+                for (int s = 0; s < kMaxSeg; ++s) acc1[s] += (seg[i] == s) ? sm : 0.f;
+            }
         }
 #pragma unroll
         for (int s = 0; s < kMaxSeg; ++s) {
             if (s < nseg) {
                 const float w = wave_sum(acc[s]);
                 if (lane == 0) red[par][dwave][s] = w;
+                if constexpr (NORM) {
+                    const float w1 = wave_sum(acc1[s]);
+                    if (lane == 0) red[par][dwave][nseg + s] = w1;
+                }
             }
         }
     };
@@ -493,8 +542,18 @@ fused_qknorm_kernel(FusedParams p)
         for (int i = 0; i < VPT; ++i) {
             const float r = rinv_s[par][seg[i]];
             float o[EV];
+            if constexpr (NORM == 0) {
 #pragma unroll
-            for (int e = 0; e < EV; ++e) o[e] = u[i][e] * r;
+                for (int e = 0; e < EV; ++e) o[e] = u[i][e] * r;
+            } else {
+                // y = u*rstd + (beta - mu*rstd*gamma)
+                const float nmr = -(mu_s[par][seg[i]] * r);
+                float g[EV], b[EV];
+                unpack_gamma(DT{}, &gam_lds[(i * ndt + dt) * KG], g);
+                unpack_gamma(DT{}, &gam_lds[(VPT * ndt + i * ndt + dt) * KG], b);
+#pragma unroll
+                for (int e = 0; e < EV; ++e) o[e] = fmaf(u[i][e], r, fmaf(nmr, g[e], b[e]));
+            }
             u32x4 w[KO];
             pack_out(DT{}, o, w);
 #pragma unroll
@@ -666,6 +725,124 @@ apply_scale_kernel(const void* x_, const void* g_, const float* rms_inv, int64_t
             for (int j = 0; j < DT::kOut; ++j) st_stream(y + base + j * (16 / (int)sizeof(out_t)), w[j]);
         } else {
             const float o = (to_f32(x[base]) * to_f32(g[c])) * r;
+            from_f32(o, y + base);
+        }
+    }
+}
+
+// LayerNorm statistics alone: sums[s*T + t] = sum of x[t][j] and sumsq[s*T + t]
+// = sum of x[t][j]^2 over shard s (fp32). One wave per (token, shard) item.
+template <class DT, bool VEC>
+__global__ void __launch_bounds__(256)
+shard_stats_kernel(const void* x_, int64_t T, int32_t H, int32_t N, float* sums, float* sumsq)
+{
+    using elem_t = typename DT::in_t;
+    constexpr int EV = DT::kVec;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= T * N) return;  // wave-uniform
+    const int64_t t = item / N;
+    const int s = (int)(item - t * N);
+    const int W = H / N;
+    const elem_t* row = static_cast<const elem_t*>(x_) + t * H + (int64_t)s * W;
+    float a1 = 0.f, a2 = 0.f;
+    if (VEC) {
+        const int Wv = W / EV;
+        for (int v = lane; v < Wv; v += 64) {
+            float f[EV];
+            unpack(DT{}, ld_stream(row + v * EV), f);
+            float sm = 0.f;
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                a2 = fmaf(f[e], f[e], a2);
+                sm += f[e];
+            }
+            a1 += sm;
+        }
+    } else {
+        for (int j = lane; j < W; j += 64) {
+            const float f = to_f32(row[j]);
+            a2 = fmaf(f, f, a2);
+            a1 += f;
+        }
+    }
+    a1 = wave_sum(a1);
+    a2 = wave_sum(a2);
+    if (lane == 0) {
+        sums[(int64_t)s * T + t] = a1;
+        sumsq[(int64_t)s * T + t] = a2;
+    }
+}
+
+// LayerNorm combine alone: mean[t] = S1/H, rstd[t] = 1/sqrt(max(S2/H - mean^2, 0) + eps)
+// with S1, S2 the shard statistics added in ascending shard order (the fused
+// kernel's expressions, so that both paths give the same factors).
+__global__ void __launch_bounds__(256)
+combine_stats_kernel(const float* sums, const float* sumsq, int64_t T, int32_t H, int32_t N,
+                     float eps, float* mean, float* rstd)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    float S1 = 0.f, S2 = 0.f;
+    for (int s = 0; s < N; ++s) {
+        S1 += sums[(int64_t)s * T + t];
+        S2 += sumsq[(int64_t)s * T + t];
+    }
+    const float Hf = (float)H;
+    const float mu = S1 / Hf;
+    const float var = fmaxf(fmaf(-mu, mu, S2 / Hf), 0.0f);
+    mean[t] = mu;
+    rstd[t] = 1.0f / sqrtf(var + eps);
+}
+
+// LayerNorm Phases B and C alone: out = (x*gamma)*rstd + (beta - mean*rstd*gamma),
+// beta null = 0. Layout as apply_scale_kernel.
+template <class DT, bool VEC>
+__global__ void __launch_bounds__(256)
+apply_norm_kernel(const void* x_, const void* g_, const void* b_, const float* mean,
+                  const float* rstd, int64_t T, int32_t H, int32_t rpb, void* y_)
+{
+    using in_t = typename DT::in_t;
+    using gam_t = typename DT::gam_t;
+    using out_t = typename DT::out_t;
+    constexpr int EV = DT::kVec;
+    const in_t* x = static_cast<const in_t*>(x_);
+    const gam_t* g = static_cast<const gam_t*>(g_);
+    const gam_t* bt = static_cast<const gam_t*>(b_);
+    out_t* y = static_cast<out_t*>(y_);
+    const int64_t r0 = (int64_t)blockIdx.x * rpb;
+    const int unit = VEC ? EV : 1;
+    const int per_row = H / unit;
+    const int total = rpb * per_row;
+    for (int v = threadIdx.x; v < total; v += 256) {
+        const int rl = v / per_row;
+        const int c = v - rl * per_row;
+        const int64_t t = r0 + rl;
+        if (t >= T) break;
+        const float r = rstd[t];
+        const float nmr = -(mean[t] * r);
+        const int64_t base = t * H + (int64_t)c * unit;
+        if (VEC) {
+            float f[EV], gg[EV], bb[EV], o[EV];
+            unpack(DT{}, ld_stream(x + base), f);
+            u32x4 gw[DT::kGam], bw[DT::kGam];
+#pragma unroll
+            for (int j = 0; j < DT::kGam; ++j) {
+                gw[j] = ld_cached(g + c * EV + j * (16 / (int)sizeof(gam_t)));
+                bw[j] = bt ? ld_cached(bt + c * EV + j * (16 / (int)sizeof(gam_t))) : u32x4{0, 0, 0, 0};
+            }
+            unpack_gamma(DT{}, gw, gg);
+            unpack_gamma(DT{}, bw, bb);
+#pragma unroll
+            for (int e = 0; e < EV; ++e) o[e] = fmaf(f[e] * gg[e], r, fmaf(nmr, gg[e], bb[e]));
+            u32x4 w[DT::kOut];
+            pack_out(DT{}, o, w);
+#pragma unroll
+            for (int j = 0; j < DT::kOut; ++j) st_stream(y + base + j * (16 / (int)sizeof(out_t)), w[j]);
+        } else {
+            const float gg = to_f32(g[c]);
+            const float bb = bt ? to_f32(bt[c]) : 0.0f;
+            const float o = fmaf(to_f32(x[base]) * gg, r, fmaf(nmr, gg, bb));
             from_f32(o, y + base);
         }
     }

@@ -5,8 +5,9 @@ arithmetic, imports neither the HIP binding nor the oracle, and serves both.
 
 Recipe (stated once, used everywhere):
 
-* Per-tensor streams come from ``numpy.random.SeedSequence(seed).spawn(6)`` in
-  the order [q, k, gamma_q, gamma_k, outlier_q, outlier_k].
+* Per-tensor streams come from ``numpy.random.SeedSequence(seed).spawn(8)`` in
+  the order [q, k, gamma_q, gamma_k, outlier_q, outlier_k, beta_q, beta_k]
+  (a child's stream does not depend on how many children are spawned).
 * Activations: ``N(0, sigma^2)`` (``standard_normal * sigma``) or Student-t
   with 3 degrees of freedom; drawn in float64 row-major, in row chunks (the
   stream is consumed in C order, so the first T' rows of a T-row draw equal a
@@ -15,6 +16,8 @@ Recipe (stated once, used everywhere):
   the first entries of a seeded permutation, shared by every token; those
   columns are multiplied by the outlier scale before rounding.
 * gamma: ``U(0.5, 1.5)`` or ``N(1, 0.1^2)``, drawn in float64.
+* LayerNorm workloads add beta ``U(-0.5, 0.5)`` in gamma's format, and may shift
+  the activations by a constant ``mu`` (mean offset) before rounding.
 * Storage: float64 -> float32 (round to nearest even), then for bf16
   float32 -> bf16 round to nearest even on the bit pattern. bf16 tensors are
   numpy ``uint16`` bit patterns. For E4M3 activations float32 -> E4M3 (OCP
@@ -53,6 +56,8 @@ class Workload:
     eps: float = EPS
     seed: int = 0
     out_dtype: str = ""  # output format; "" = the input format (E4M3: "bf16" or "e4m3")
+    norm: str = "rms"    # "rms" (RMSNorm) or "layer" (LayerNorm with beta)
+    mu: float = 0.0      # constant added to every activation draw
 
     def with_T(self, T: int) -> "Workload":
         return dataclasses.replace(self, T=T)
@@ -67,7 +72,9 @@ class Workload:
 
     @property
     def fmt(self) -> str:
-        """Kernel format name: "bf16", "f32", "e4m3_bf16" or "e4m3_e4m3"."""
+        """Kernel format name: "bf16", "f32", "e4m3_bf16", "e4m3_e4m3", "ln_bf16" or "ln_f32"."""
+        if self.norm == "layer":
+            return f"ln_{self.dtype}"
         return f"e4m3_{self.out}" if self.dtype == "e4m3" else self.dtype
 
     @property
@@ -80,9 +87,11 @@ class Workload:
         return _BYTES[self.out]
 
     def algorithmic_bytes(self) -> int:
-        """One read and one write of Q and K, plus gamma_q and gamma_k once."""
+        """One read and one write of Q and K, plus gamma (and beta) of Q and K once."""
         per_col = self.elem_bytes + self.out_bytes
-        return self.T * (self.Hq + self.Hk) * per_col + (self.Hq + self.Hk) * _BYTES[self.gamma_dtype]
+        params = 2 if self.norm == "layer" else 1
+        return (self.T * (self.Hq + self.Hk) * per_col +
+                params * (self.Hq + self.Hk) * _BYTES[self.gamma_dtype])
 
     def outlier_count(self, H: int) -> int:
         if self.outlier_frac <= 0:
@@ -108,6 +117,17 @@ GQA_E4M3 = Workload("gqa_e4m3", 8192, 5120, 1024, 4, "e4m3", outlier_frac=0.005,
                     outlier_scale=50.0, out_dtype="bf16")
 E4M3_CONFIGS = {w.name: w for w in (TINY_E4M3, DECODE_E4M3, PREFILL_E4M3, GQA_E4M3)}
 
+# LayerNorm with two additive shard statistics (reading notes, Section 5e) at the
+# same shapes, plus rows with a non-zero mean
+LN_TINY = Workload("ln_tiny", 8, 256, 256, 2, "f32", gamma_dist="normal", norm="layer")
+LN_DECODE = Workload("ln_decode", 64, 4096, 4096, 4, "bf16", outlier_frac=0.01,
+                     outlier_scale=20.0, norm="layer")
+LN_PREFILL = Workload("ln_prefill", 16384, 5120, 5120, 2, "bf16", sigma=2.0, norm="layer")
+LN_GQA = Workload("ln_gqa", 8192, 5120, 1024, 4, "bf16", outlier_frac=0.005, outlier_scale=50.0,
+                  norm="layer")
+LN_SHIFTED = Workload("ln_shifted", 1024, 4096, 4096, 4, "f32", mu=1.0, norm="layer")
+LN_CONFIGS = {w.name: w for w in (LN_TINY, LN_DECODE, LN_PREFILL, LN_GQA, LN_SHIFTED)}
+
 SWEEP_T = (4096, 4097, 16384, 65536)
 SWEEP_H = (1024, 3072, 5120, 8192, 16384)
 SWEEP_N = (1, 2, 4, 8)
@@ -119,6 +139,13 @@ def sweep() -> Iterator[Workload]:
     for T, H, N, dt, dist in itertools.product(SWEEP_T, SWEEP_H, SWEEP_N, SWEEP_DTYPE,
                                                SWEEP_DIST):
         yield Workload(f"sweep_T{T}_H{H}_N{N}_{dt}_{dist}", T, H, H, N, dt, dist=dist)
+
+
+def sweep_layernorm() -> Iterator[Workload]:
+    """LayerNorm over a reduced sweep grid: T in {4096, 16384}, H in {1024, 5120, 16384},
+    N in {1, 2, 4, 8}, bf16 and fp32, normal draws (48 points)."""
+    for T, H, N, dt in itertools.product((4096, 16384), (1024, 5120, 16384), SWEEP_N, SWEEP_DTYPE):
+        yield Workload(f"ln_sweep_T{T}_H{H}_N{N}_{dt}", T, H, H, N, dt, norm="layer")
 
 
 def sweep_e4m3() -> Iterator[Workload]:
@@ -171,7 +198,7 @@ def store(a64: np.ndarray, dtype: str) -> np.ndarray:
 # ---------------------------------------------------------------- host draws
 
 def _streams(seed: int):
-    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(6)]
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(8)]
 
 
 _NP = {"bf16": np.uint16, "f32": np.float32, "e4m3": np.uint8}
@@ -189,8 +216,14 @@ def _activations(rng, T, H, w: Workload, outlier_cols, chunk_rows: int) -> np.nd
             raise ValueError(w.dist)
         if outlier_cols is not None:
             a[:, outlier_cols] *= w.outlier_scale
+        if w.mu:
+            a += w.mu
         out[lo:hi] = store(a, w.dtype)
     return out
+
+
+def _beta(rng, H, w: Workload) -> np.ndarray:
+    return store(rng.uniform(-0.5, 0.5, H), w.gamma_dtype)
 
 
 def _gamma(rng, H, w: Workload) -> np.ndarray:
@@ -214,14 +247,18 @@ def outlier_columns(w: Workload, which: str):
 
 
 def make_host(w: Workload, chunk_rows: int = 2048) -> dict:
-    """Host arrays ``q, k, gamma_q, gamma_k`` for workload ``w``."""
-    rq, rk, rgq, rgk, _, _ = _streams(w.seed)
-    return {
+    """Host arrays ``q, k, gamma_q, gamma_k`` (and ``beta_q, beta_k`` for LayerNorm)."""
+    rq, rk, rgq, rgk, _, _, rbq, rbk = _streams(w.seed)
+    d = {
         "q": _activations(rq, w.T, w.Hq, w, outlier_columns(w, "q"), chunk_rows),
         "k": _activations(rk, w.T, w.Hk, w, outlier_columns(w, "k"), chunk_rows),
         "gamma_q": _gamma(rgq, w.Hq, w),
         "gamma_k": _gamma(rgk, w.Hk, w),
     }
+    if w.norm == "layer":
+        d["beta_q"] = _beta(rbq, w.Hq, w)
+        d["beta_k"] = _beta(rbk, w.Hk, w)
+    return d
 
 
 # ---------------------------------------------------------------- device draws
@@ -254,6 +291,8 @@ def make_device_activations(w: Workload, which: str, device, torch):
         cols = outlier_columns(w, which)
         if cols is not None:
             a[:, torch.as_tensor(cols, device=device)] *= w.outlier_scale
+        if w.mu:
+            a = a + w.mu
         if w.dtype == "e4m3":
             a = a.clamp(-E4M3_MAX, E4M3_MAX)
         out[lo:hi] = a.to(out_dtype)

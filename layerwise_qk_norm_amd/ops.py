@@ -22,7 +22,7 @@ QKN_OK, QKN_EINVAL, QKN_EOVERLAP, QKN_ENOMEM, QKN_EHIP = 0, -1, -2, -3, -4
 QKN_ERESIDENCY, QKN_ETIMEOUT, QKN_ECAPTURE = -5, -6, -7
 QKN_BF16, QKN_F32, QKN_E4M3 = 0, 1, 2
 # kernel formats (input x / gamma / output y), the ``dtype`` of the planning calls
-FORMATS = {"bf16": 0, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 3}
+FORMATS = {"bf16": 0, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 3, "ln_bf16": 4, "ln_f32": 5}
 E4M3 = torch.float8_e4m3fn
 NUM_VARIANTS = 10
 MAX_DATA_WAVES = 15
@@ -63,6 +63,13 @@ _SIGS = {
     "qknorm_apply_scale_bf16": [_P, _P, _P, _I64, _I64, _P, _P],
     "qknorm_apply_scale_f32": [_P, _P, _P, _I64, _I64, _P, _P],
     "qknorm_apply_scale_e4m3": [_P, _P, _P, _I64, _I64, _P, _I, _P],
+    "qknorm_layernorm_fwd_bf16": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
+    "qknorm_layernorm_fwd_f32": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
+    "qknorm_shard_stats_bf16": [_P, _I64, _I64, _I, _P, _P, _P],
+    "qknorm_shard_stats_f32": [_P, _I64, _I64, _I, _P, _P, _P],
+    "qknorm_combine_stats": [_P, _P, _I64, _I64, _I, _F, _P, _P, _P],
+    "qknorm_apply_norm_bf16": [_P, _P, _P, _P, _P, _I64, _I64, _P, _P],
+    "qknorm_apply_norm_f32": [_P, _P, _P, _P, _P, _I64, _I64, _P, _P],
     "qknorm_check_fault": [_P],
     "qknorm_strerror": [_I],
     "qknorm_last_hip_error": [],
@@ -222,6 +229,105 @@ def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_
             status = fn(*args, _stream(dev))
     _check(status, "qknorm_layerwise_fwd")
     return out_q, out_k
+
+
+def _ptr_or_null(t):
+    return None if t is None else t.data_ptr()
+
+
+def layernorm_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-5, beta_q=None,
+                  beta_k=None, out_q=None, out_k=None):
+    """Fused Q+K LayerNorm over the full vectors with two additive shard statistics;
+    returns ``(out_q, out_k)``. bfloat16 or float32; beta may be None (no shift)."""
+    _need(q, "q", 2)
+    dt = q.dtype
+    dev = q.device
+    code = _dtype_code(q)
+    if code == QKN_E4M3:
+        raise TypeError("LayerNorm takes bfloat16 or float32 tensors")
+    _need(k, "k", 2, dt, dev)
+    T, Hq = q.shape
+    Hk = k.shape[1]
+    if k.shape[0] != T:
+        raise ValueError("q and k must have the same number of tokens")
+    for t, name, H in ((gamma_q, "gamma_q", Hq), (gamma_k, "gamma_k", Hk),
+                       (beta_q, "beta_q", Hq), (beta_k, "beta_k", Hk)):
+        if t is None and name.startswith("beta"):
+            continue
+        _need(t, name, 1, dt, dev)
+        if t.shape[0] != H:
+            raise ValueError(f"{name} must be [{H}]")
+    out_q = torch.empty_like(q) if out_q is None else out_q
+    out_k = torch.empty_like(k) if out_k is None else out_k
+    _need(out_q, "out_q", 2, dt, dev)
+    _need(out_k, "out_k", 2, dt, dev)
+    if out_q.shape != q.shape or out_k.shape != k.shape:
+        raise ValueError("outputs must have the shapes of q and k")
+    fn = getattr(lib(), f"qknorm_layernorm_fwd_{_suffix(code)}")
+    with torch.cuda.device(dev):
+        _check(fn(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+                  _ptr_or_null(beta_q), _ptr_or_null(beta_k), T, Hq, Hk, n_shards, eps,
+                  out_q.data_ptr(), out_k.data_ptr(), _stream(dev)), "qknorm_layernorm_fwd")
+    return out_q, out_k
+
+
+def shard_stats(x, n_shards: int, sums=None, sumsq=None):
+    """Per-shard fp32 sums and sums of squares, each ``[n_shards, T]``."""
+    _need(x, "x", 2)
+    T, H = x.shape
+    code = _dtype_code(x)
+    if code == QKN_E4M3:
+        raise TypeError("LayerNorm takes bfloat16 or float32 tensors")
+    sums = torch.empty((n_shards, T), dtype=torch.float32, device=x.device) if sums is None else sums
+    sumsq = torch.empty((n_shards, T), dtype=torch.float32, device=x.device) if sumsq is None else sumsq
+    for t, name in ((sums, "sums"), (sumsq, "sumsq")):
+        _need(t, name, 2, torch.float32, x.device)
+        if tuple(t.shape) != (n_shards, T):
+            raise ValueError(f"{name} must be [n_shards, T]")
+    fn = getattr(lib(), f"qknorm_shard_stats_{_suffix(code)}")
+    with torch.cuda.device(x.device):
+        _check(fn(x.data_ptr(), T, H, n_shards, sums.data_ptr(), sumsq.data_ptr(),
+                  _stream(x.device)), "qknorm_shard_stats")
+    return sums, sumsq
+
+
+def combine_stats(sums, sumsq, H: int, eps: float = 1e-5, mean=None, rstd=None):
+    """Mean and reciprocal standard deviation per token, each ``[T]`` fp32."""
+    _need(sums, "sums", 2, torch.float32)
+    _need(sumsq, "sumsq", 2, torch.float32, sums.device)
+    n_shards, T = sums.shape
+    if tuple(sumsq.shape) != (n_shards, T):
+        raise ValueError("sums and sumsq must have the same shape")
+    mean = torch.empty((T,), dtype=torch.float32, device=sums.device) if mean is None else mean
+    rstd = torch.empty((T,), dtype=torch.float32, device=sums.device) if rstd is None else rstd
+    _need(mean, "mean", 1, torch.float32, sums.device)
+    _need(rstd, "rstd", 1, torch.float32, sums.device)
+    with torch.cuda.device(sums.device):
+        _check(lib().qknorm_combine_stats(sums.data_ptr(), sumsq.data_ptr(), T, H, n_shards, eps,
+                                          mean.data_ptr(), rstd.data_ptr(), _stream(sums.device)),
+               "qknorm_combine_stats")
+    return mean, rstd
+
+
+def apply_norm(x, gamma, beta, mean, rstd, out=None):
+    """``out = (x*gamma)*rstd + (beta - mean*rstd*gamma)`` in x's dtype (beta may be None)."""
+    _need(x, "x", 2)
+    T, H = x.shape
+    code = _dtype_code(x)
+    if code == QKN_E4M3:
+        raise TypeError("LayerNorm takes bfloat16 or float32 tensors")
+    _need(gamma, "gamma", 1, x.dtype, x.device)
+    if beta is not None:
+        _need(beta, "beta", 1, x.dtype, x.device)
+    _need(mean, "mean", 1, torch.float32, x.device)
+    _need(rstd, "rstd", 1, torch.float32, x.device)
+    out = torch.empty_like(x) if out is None else out
+    _need(out, "out", 2, x.dtype, x.device)
+    fn = getattr(lib(), f"qknorm_apply_norm_{_suffix(code)}")
+    with torch.cuda.device(x.device):
+        _check(fn(x.data_ptr(), gamma.data_ptr(), _ptr_or_null(beta), mean.data_ptr(),
+                  rstd.data_ptr(), T, H, out.data_ptr(), _stream(x.device)), "qknorm_apply_norm")
+    return out
 
 
 def shard_sumsq(x, n_shards: int, partials=None):

@@ -34,6 +34,30 @@ def decode_out(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
+def layernorm_scaled_error(got, y, x, mean, rstd, gamma, beta, eps):
+    """Elementwise |got - y| / s for LayerNorm outputs, with the operand scale
+    s_j = rstd * |gamma_j| * (|x_j| + |mean| + sigma) + |beta_j| (sigma the row's
+    standard deviation from the oracle's rstd and eps).
+
+    An output near zero comes from x_j close to the mean, where the relative
+    error of the result says nothing about the arithmetic; fp32 rounding of
+    x - mean, of the statistics and of the final fma is bounded by a few ulp of
+    this scale, and one bf16 rounding of the output by 2^-9 of it (|y_j| <= s_j).
+    """
+    got = np.asarray(got, np.float64)
+    y = np.asarray(y, np.float64)
+    xv = np.asarray(x, np.float64)
+    g = np.abs(np.asarray(gamma, np.float64))[None, :]
+    b = np.zeros_like(g) if beta is None else np.abs(np.asarray(beta, np.float64))[None, :]
+    e = float(np.float32(eps))
+    sigma = np.sqrt(np.maximum(1.0 / (rstd * rstd) - e, 0.0))
+    scale = rstd[:, None] * g * (np.abs(xv) + np.abs(mean)[:, None] + sigma[:, None]) + b
+    err = np.abs(got - y) / scale
+    err[np.isnan(got) & np.isnan(y)] = 0.0
+    err[np.isnan(got) != np.isnan(y)] = np.inf
+    return err
+
+
 def e4m3_rne(y: np.ndarray) -> np.ndarray:
     """E4M3 code (OCP OFP8 layout) nearest to each float64 value, ties to the even
     code; magnitudes of 448 and above (infinities included) saturate to the

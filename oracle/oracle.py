@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
 CPU-baseline leg of the benchmark, never by the product. It shares no code
 with the HIP library or its binding and imports nothing from them.
 
-Three independent renderings of the same definition:
+Three independent renderings of the same definitions (RMSNorm, and LayerNorm with
+its two additive shard statistics):
 
 * ``rmsnorm`` / ``shard_sumsq`` -- the plain C loops in ``qknorm_oracle.c``
   (fast enough for full-size sampled rows and for the CPU baseline);
@@ -18,7 +19,10 @@ Communication-Efficient Tensor Parallelism for Query-Key Normalization",
 Section II-A, Eq. (1); printed cleanly as Eq. (1) of the reading notes
 "SwiftQK：当归一化层成为张量并行的瓶颈", Section 2. Shard partials follow
 Algorithm 1, Phase A of the letter and Eqs. (3)-(4) of the notes' worked
-example (Section 4b).
+example (Section 4b). LayerNorm (``layernorm``, ``shard_stats``) follows the notes'
+Section 5e: mean and variance over the full vector, which shards reduce to two
+additive statistics (sum x, sum x^2); the oracle itself uses the two-pass
+definition of the variance.
 """
 from __future__ import annotations
 
@@ -63,6 +67,15 @@ def _load():
         lib.oracle_rmsnorm.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_layernorm.restype = ctypes.c_int
+        lib.oracle_layernorm.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+        lib.oracle_shard_stats.restype = ctypes.c_int
+        lib.oracle_shard_stats.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
         lib.oracle_decode_e4m3.restype = ctypes.c_int
         lib.oracle_decode_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_shard_sumsq.restype = ctypes.c_int
@@ -129,6 +142,64 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, want_y: bool = True,
     return y, S, r
 
 
+def layernorm(x: np.ndarray, gamma: np.ndarray, beta, eps: float, want_y: bool = True,
+              threads: int = 1):
+    """fp64 LayerNorm of each row of ``x`` via the C loops (two-pass definition).
+
+    ``beta`` may be None (no shift). Returns ``(y, mean, rstd)``; ``y`` is None when
+    ``want_y`` is False. Rows may be split over ``threads`` (arithmetic unchanged).
+    """
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    gamma = np.ascontiguousarray(gamma)
+    dt = _dtype_of(x)
+    if _dtype_of(gamma) != GAMMA_FORMAT[dt]:
+        raise TypeError(f"gamma must be {GAMMA_FORMAT[dt]} for {dt} inputs")
+    if beta is not None:
+        beta = np.ascontiguousarray(beta)
+        if _dtype_of(beta) != GAMMA_FORMAT[dt] or beta.shape != gamma.shape:
+            raise TypeError("beta must have the format and shape of gamma")
+    T, H = x.shape
+    if gamma.shape != (H,):
+        raise ValueError("gamma must be [H]")
+    y = np.empty((T, H), np.float64) if want_y else None
+    mu = np.empty(T, np.float64)
+    rs = np.empty(T, np.float64)
+
+    def run(lo, hi):
+        if hi <= lo:
+            return
+        rc = lib.oracle_layernorm(
+            x.ctypes.data + lo * H * x.itemsize, gamma.ctypes.data,
+            None if beta is None else beta.ctypes.data, DTYPE_CODE[dt], hi - lo, H,
+            ctypes.c_float(eps), None if y is None else y.ctypes.data + lo * H * 8,
+            mu.ctypes.data + lo * 8, rs.ctypes.data + lo * 8)
+        if rc != 0:
+            raise ValueError("oracle_layernorm rejected its arguments")
+
+    if threads <= 1 or T < 2 * threads:
+        run(0, T)
+    else:
+        edges = np.linspace(0, T, threads + 1).astype(np.int64)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda i: run(int(edges[i]), int(edges[i + 1])), range(threads)))
+    return y, mu, rs
+
+
+def shard_stats(x: np.ndarray, n_shards: int):
+    """Per-shard sums and sums of squares, each ``[n_shards][T]`` (fp64), via the C loops."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    a = np.empty((n_shards, T), np.float64)
+    b = np.empty((n_shards, T), np.float64)
+    rc = lib.oracle_shard_stats(x.ctypes.data, DTYPE_CODE[_dtype_of(x)], T, H, n_shards,
+                                a.ctypes.data, b.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_shard_stats rejected its arguments (H % N must be 0)")
+    return a, b
+
+
 def shard_sumsq(x: np.ndarray, n_shards: int) -> np.ndarray:
     """Shard-major partial sums of squares ``p[k][t]`` (fp64) via the C loops."""
     lib = _load()
@@ -190,6 +261,29 @@ def rmsnorm_np(x: np.ndarray, gamma: np.ndarray, eps: float):
     return y, S, 1.0 / denom
 
 
+def layernorm_np(x: np.ndarray, gamma: np.ndarray, beta, eps: float):
+    """NumPy float64 mirror of ``layernorm`` (numpy's mean and centred variance)."""
+    xv = decode(x)
+    g = decode(gamma)
+    b = np.zeros_like(g) if beta is None else decode(beta)
+    mu = np.mean(xv, axis=1)
+    var = np.mean((xv - mu[:, None]) ** 2, axis=1)
+    denom = np.sqrt(var + float(np.float32(eps)))
+    y = (xv - mu[:, None]) / denom[:, None] * g[None, :] + b[None, :]
+    return y, mu, 1.0 / denom
+
+
+def shard_stats_np(x: np.ndarray, n_shards: int):
+    xv = decode(x)
+    T, H = xv.shape
+    if H % n_shards:
+        raise ValueError("H % N must be 0")
+    W = H // n_shards
+    a = np.stack([np.sum(xv[:, k * W:(k + 1) * W], axis=1) for k in range(n_shards)])
+    b = np.stack([np.sum(xv[:, k * W:(k + 1) * W] ** 2, axis=1) for k in range(n_shards)])
+    return a, b
+
+
 def shard_sumsq_np(x: np.ndarray, n_shards: int) -> np.ndarray:
     xv = decode(x)
     T, H = xv.shape
@@ -220,3 +314,29 @@ def rmsnorm_exact(x: np.ndarray, gamma: np.ndarray, eps: float, digits: int = 50
         r_out.append(1 / denom)
         y_out.append([Decimal(float(xv[t, j])) / denom * Decimal(float(g[j])) for j in range(H)])
     return y_out, S_out, r_out
+
+
+def layernorm_exact(x: np.ndarray, gamma: np.ndarray, beta, eps: float, digits: int = 50):
+    """Exact mean and variance (rationals) and a ``digits``-digit decimal y, row by row.
+
+    Pure-Python loops: only for tiny inputs.
+    """
+    getcontext().prec = digits
+    xv = decode(x)
+    g = decode(gamma)
+    b = np.zeros_like(g) if beta is None else decode(beta)
+    T, H = xv.shape
+    e = Fraction(float(np.float32(eps)))
+    mu_out, var_out, y_out = [], [], []
+    for t in range(T):
+        vals = [Fraction(float(v)) for v in xv[t]]
+        mu = sum(vals, Fraction(0)) / H
+        var = sum(((v - mu) ** 2 for v in vals), Fraction(0)) / H
+        ms = var + e
+        denom = (Decimal(ms.numerator) / Decimal(ms.denominator)).sqrt()
+        mud = Decimal(mu.numerator) / Decimal(mu.denominator)
+        mu_out.append(mu)
+        var_out.append(var)
+        y_out.append([(Decimal(float(xv[t, j])) - mud) / denom * Decimal(float(g[j])) +
+                      Decimal(float(b[j])) for j in range(H)])
+    return y_out, mu_out, var_out

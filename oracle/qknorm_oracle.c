@@ -168,3 +168,78 @@ int oracle_decode_e4m3(const uint8_t* codes, int64_t n, double* out)
         out[i] = decode_e4m3(codes[i]);
     return 0;
 }
+
+/*
+ * LayerNorm of T rows of width H (the extension of the method to a norm with
+ * two additive statistics, reading notes Section 5e: mean and variance of the
+ * whole vector, from sum x and sum x^2 of every shard):
+ *
+ *   mu = (1/H) sum_j x_j,   var = (1/H) sum_j (x_j - mu)^2,
+ *   y_j = (x_j - mu) / sqrt(var + eps) * gamma_j + beta_j
+ *
+ * computed here by the definition, two passes in binary64 (mean, then the
+ * centred sum of squares), not by the sum / sum-of-squares identity.
+ *   x      [T][H]  input values (format as for oracle_rmsnorm)
+ *   gamma  [H]     scale, beta [H] shift (NULL = no shift), format of x
+ * Outputs (any may be NULL): y [T][H] unrounded, mean [T], rstd [T] = 1/sqrt(var+eps).
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_layernorm(const void* x, const void* gamma, const void* beta, int dtype, int64_t T,
+                     int64_t H, float eps, double* y, double* mean, double* rstd)
+{
+    if (!x || (y && !gamma) || T < 0 || H < 1 || !format_ok(dtype))
+        return -1;
+    const double e = (double)eps;
+    for (int64_t t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int64_t j = 0; j < H; ++j)
+            s += load(x, dtype, t * H + j);
+        const double mu = s / (double)H;
+        double c = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            const double d = load(x, dtype, t * H + j) - mu;
+            c += d * d;
+        }
+        const double denom = sqrt(c / (double)H + e);
+        if (mean)
+            mean[t] = mu;
+        if (rstd)
+            rstd[t] = 1.0 / denom;
+        if (y) {
+            for (int64_t j = 0; j < H; ++j) {
+                const double v = load(x, dtype, t * H + j);
+                const double g = load(gamma, gamma_format(dtype), j);
+                const double b = beta ? load(beta, gamma_format(dtype), j) : 0.0;
+                y[t * H + j] = (v - mu) / denom * g + b;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * The two additive statistics of every shard, shard-major:
+ *   sums[k*T + t] = sum_{j in shard k} x[t][j],  sumsq[k*T + t] = sum x[t][j]^2.
+ * Requires H % N == 0. Returns 0, or -1.
+ */
+int oracle_shard_stats(const void* x, int dtype, int64_t T, int64_t H, int n_shards,
+                       double* sums, double* sumsq)
+{
+    if (!x || !sums || !sumsq || T < 0 || H < 1 || n_shards < 1 || H % n_shards != 0 ||
+        !format_ok(dtype))
+        return -1;
+    const int64_t W = H / n_shards;
+    for (int k = 0; k < n_shards; ++k) {
+        for (int64_t t = 0; t < T; ++t) {
+            double a = 0.0, b = 0.0;
+            for (int64_t j = k * W; j < (k + 1) * W; ++j) {
+                const double v = load(x, dtype, t * H + j);
+                a += v;
+                b += v * v;
+            }
+            sums[(int64_t)k * T + t] = a;
+            sumsq[(int64_t)k * T + t] = b;
+        }
+    }
+    return 0;
+}

@@ -95,3 +95,29 @@ def run_split(x: np.ndarray, gamma: np.ndarray, n_shards: int, eps: float, out: 
     y = ops.apply_scale(xd, gd, r, out_dtype=TORCH_DTYPE[out] if out else None)
     torch.cuda.synchronize()
     return to_host(p), to_host(r), to_host(y)
+
+
+def layernorm_report(x, gamma, beta, out, eps, chunk: int = 4096, threads: int = 8) -> dict:
+    """LayerNorm output against the fp64 oracle: the largest operand-scaled error
+    (``compare.layernorm_scaled_error``) and, as context, max-abs and RMSE."""
+    worst, sum_sq, n, max_abs = 0.0, 0.0, 0, 0.0
+    for lo in range(0, x.shape[0], chunk):
+        hi = min(x.shape[0], lo + chunk)
+        y, mu, rs = oracle.layernorm(x[lo:hi], gamma, beta, eps, threads=threads)
+        got = compare.decode_out(out[lo:hi])
+        err = compare.layernorm_scaled_error(got, y, compare.decode_out(x[lo:hi]), mu, rs,
+                                             compare.decode_out(gamma),
+                                             None if beta is None else compare.decode_out(beta), eps)
+        worst = max(worst, float(err.max()) if err.size else 0.0)
+        d = np.abs(got - y)
+        max_abs = max(max_abs, float(d.max()) if d.size else 0.0)
+        sum_sq += float((d * d).sum())
+        n += d.size
+    return {"max_scaled": worst, "max_abs": max_abs, "rmse": (sum_sq / max(n, 1)) ** 0.5, "n": n}
+
+
+def assert_layernorm_parity(x, gamma, beta, out, eps, what=""):
+    r = layernorm_report(x, gamma, beta, out, eps)
+    tol = compare.TOL[dtype_name(out)]
+    assert r["max_scaled"] <= tol, f"{what}: max scaled err {r['max_scaled']:.3e} > {tol} ({r})"
+    return r

@@ -113,6 +113,32 @@ def test_e4m3_entry_points_reject_bad_arguments():
                                      ops.QKN_E4M3, None) == ops.QKN_EOVERLAP
 
 
+def test_layernorm_entry_points_reject_bad_arguments():
+    L = ops.lib()
+    q, k, gq, gk, oq, ok = FAKE
+    bq, bk = 0x90000, 0xA0000
+
+    def ln(T=4, Hq=64, Hk=64, N=2, eps=1e-6, ptrs=None, betas=(bq, bk), fn="bf16"):
+        a = ptrs or FAKE
+        return getattr(L, f"qknorm_layernorm_fwd_{fn}")(a[0], a[1], a[2], a[3], betas[0], betas[1],
+                                                        T, Hq, Hk, N, eps, a[4], a[5], None)
+    for kw in (dict(N=3), dict(T=-1), dict(eps=-1.0), dict(Hq=0), dict(N=33)):
+        assert ln(**kw) == ops.QKN_EINVAL
+        assert ln(fn="f32", **kw) == ops.QKN_EINVAL
+    assert ln(T=0, ptrs=[0] * 6, betas=(0, 0)) == ops.QKN_OK
+    assert ln(ptrs=[q, k, gq, gk, oq, bk - 16]) == ops.QKN_EOVERLAP  # out_k runs into beta_k
+    assert ln(ptrs=[q, k, gq, gk, bq, ok]) == ops.QKN_EOVERLAP       # out_q over beta_q
+    assert L.qknorm_shard_stats_bf16(q, 4, 64, 3, gq, gk, None) == ops.QKN_EINVAL
+    assert L.qknorm_shard_stats_f32(q, 4, 64, 2, gq, gq + 8, None) == ops.QKN_EOVERLAP
+    assert L.qknorm_shard_stats_f32(q, 4, 64, 2, q + 8, gk, None) == ops.QKN_EOVERLAP
+    assert L.qknorm_combine_stats(q, k, 4, 64, 2, -1.0, gq, gk, None) == ops.QKN_EINVAL
+    assert L.qknorm_combine_stats(q, k, 4, 64, 2, 1e-6, gq, gq + 4, None) == ops.QKN_EOVERLAP
+    assert L.qknorm_combine_stats(q, k, 4, 64, 2, 1e-6, q + 4, gk, None) == ops.QKN_EOVERLAP
+    assert L.qknorm_apply_norm_bf16(q, 0, bq, gq, gk, 4, 64, oq, None) == ops.QKN_EINVAL
+    assert L.qknorm_apply_norm_bf16(q, k, bq, gq, gk, 4, 64, bq - 2, None) == ops.QKN_EOVERLAP
+    assert L.qknorm_apply_norm_f32(q, k, 0, gq, gk, 0, 64, oq, None) == ops.QKN_OK
+
+
 def test_split_entry_points_reject_bad_arguments():
     L = ops.lib()
     assert L.qknorm_shard_sumsq_bf16(FAKE[0], 4, 64, 3, FAKE[1], None) == ops.QKN_EINVAL
@@ -136,13 +162,19 @@ VPT = [1, 2, 3, 4, 6, 9, 1, 2, 3, 4]
 # 0 = not instantiated for that format
 MAXW = {"bf16": [15, 15, 15, 15, 11, 0, 15, 15, 11, 7],
         "f32": [15, 15, 15, 15, 11, 15, 15, 15, 11, 7],
-        "e4m3": [15, 15, 11, 0, 0, 0, 15, 11, 0, 0]}
+        "e4m3": [15, 15, 11, 0, 0, 0, 15, 11, 0, 0],
+        "ln_bf16": [15, 15, 15, 15, 7, 0, 15, 15, 11, 7],
+        "ln_f32": [15, 15, 15, 15, 7, 0, 15, 15, 11, 7]}
 VGPR = {"bf16": [32, 56, 80, 104, 168, 120, 48, 80, 136, 184],
         "f32": [32, 56, 80, 104, 168, 120, 48, 80, 104, 128],
-        "e4m3": [56, 104, 144, 1, 1, 1, 96, 168, 1, 1]}
-EV = {"bf16": 8, "f32": 4, "e4m3_bf16": 16, "e4m3_e4m3": 16}
-KGAM = {"bf16": 1, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 2}
+        "e4m3": [56, 104, 144, 1, 1, 1, 96, 168, 1, 1],
+        "ln_bf16": [48, 73, 96, 121, 168, 1, 59, 99, 143, 184],
+        "ln_f32": [32, 58, 71, 95, 124, 1, 40, 72, 98, 139]}
+EV = {"bf16": 8, "f32": 4, "e4m3_bf16": 16, "e4m3_e4m3": 16, "ln_bf16": 8, "ln_f32": 4}
+KGAM = {"bf16": 1, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 2, "ln_bf16": 2, "ln_f32": 2}  # x params
+STATS = {"bf16": 1, "f32": 1, "e4m3_bf16": 1, "e4m3_e4m3": 1, "ln_bf16": 2, "ln_f32": 2}
 FORMATS = list(EV)
+assert set(FORMATS) == set(ops.FORMATS)
 
 
 def _fam(fmt):
@@ -180,7 +212,7 @@ def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=None):
     assert p["grid"] == p["n_groups"] * N
     assert p["grid"] <= cap, "grid must not exceed co-resident capacity"
     assert 1 <= p["rows"] <= 4
-    assert N * 2 * p["rows"] <= 64
+    assert N * 2 * p["rows"] * STATS[dtype] <= 64
     assert p["n_tiles"] == -(-T // p["rows"])
     assert 1 <= p["n_groups"] <= p["n_tiles"]
     assert p["iters"] * p["n_groups"] >= p["n_tiles"] > (p["iters"] - 1) * p["n_groups"]
@@ -199,7 +231,7 @@ def plan(dtype, T, Hq, Hk, N, cu=CU, bpc=None, aligned=True):
 
 def test_plan_named_workloads():
     for w in (inputs.TINY, inputs.DECODE, inputs.PREFILL, inputs.GQA,
-              *inputs.E4M3_CONFIGS.values()):
+              *inputs.E4M3_CONFIGS.values(), *inputs.LN_CONFIGS.values()):
         p = plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
         assert p["variant"] >= 0, w.name
         check_plan(p, w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
@@ -208,9 +240,18 @@ def test_plan_named_workloads():
 
 
 def test_plan_every_sweep_point():
-    for w in [*inputs.sweep(), *inputs.sweep_e4m3()]:
+    for w in [*inputs.sweep(), *inputs.sweep_e4m3(), *inputs.sweep_layernorm()]:
         p = plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
-        assert p["variant"] >= 0, w.name  # every sweep shape fits a fused variant
+        # every shape whose one-row tile fits some variant's slots runs fused
+        ev = EV[w.fmt]
+        wvq, wvk = w.Hq // w.n_shards // ev, w.Hk // w.n_shards // ev
+        need = -(-wvq // 64) * 64 + wvk
+        fam = _fam(w.fmt)
+        room = max(64 * MAXW[fam][v] * VPT[v] for v in range(ops.NUM_VARIANTS)
+                   if MAXW[fam][v] and (w.n_shards > 1 or v < 6))
+        assert (p["variant"] >= 0) == (need <= room), w.name
+        if w.norm == "rms":
+            assert p["variant"] >= 0, w.name  # every RMSNorm sweep shape runs fused
         check_plan(p, w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
 
 
@@ -257,6 +298,11 @@ def test_plan_many_shards_uses_narrow_tiles():
         p = plan("bf16", 4096, 4096, 4096, N)
         assert p["variant"] >= 0 and N * 2 * p["rows"] <= 64
         check_plan(p, "bf16", 4096, 4096, 4096, N)
+    # LayerNorm exchanges two statistics: 16 shards fit one comm wave, 32 do not
+    p = plan("ln_bf16", 4096, 4096, 4096, 16)
+    assert p["variant"] >= 0 and p["rows"] == 1
+    check_plan(p, "ln_bf16", 4096, 4096, 4096, 16)
+    assert plan("ln_bf16", 4096, 4096, 4096, 32)["variant"] == -1
 
 
 def test_plan_randomised_invariants():

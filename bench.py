@@ -16,10 +16,12 @@ Besides the headline (GB/s of algorithmic bytes), the line carries:
   e4m3        -- FP8-E4M3 activations (bf16 gamma) on the prefill shape with bf16
                  and with E4M3 outputs, each against the HBM roofline, and the
                  decode shape in us per call
+  layernorm   -- LayerNorm (two additive shard statistics, gamma and beta) on the
+                 prefill shape against the HBM roofline, and the decode shape
 
 Modes: ``--pmc`` runs only the kernels whose counters are collected
-(fused prefill in bf16 and in E4M3->bf16, and the copy of known size), for
-rocprofv3 --pmc runs.
+(fused prefill in bf16, in E4M3->bf16 and as LayerNorm, and the copy of known
+size), for rocprofv3 --pmc runs.
 """
 import argparse
 import dataclasses
@@ -37,6 +39,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 METRIC = "fused Q+K layerwise RMSNorm HBM GB/s (% of peak) at T=16384; decode µs at T=64"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_prefill_T16384_traffic.txt")
 TRAFFIC_SUMMARY_E4M3 = os.path.join(ROOT, "profiles", "fused_prefill_e4m3_T16384_traffic.txt")
+TRAFFIC_SUMMARY_LN = os.path.join(ROOT, "profiles", "fused_layernorm_prefill_T16384_traffic.txt")
 
 
 def log(*a):
@@ -93,6 +96,56 @@ def roofline(nbytes, ms, traffic):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+def bench_layernorm(args, torch, stream, timed):
+    """LayerNorm with two additive shard statistics on the prefill and decode shapes."""
+    from layerwise_qk_norm_amd import inputs, ops
+    out = {}
+    w = inputs.LN_PREFILL
+    d = inputs.make_host(w)
+    dev = "cuda:0"
+    par = {n: inputs.to_device(d[n], dev, torch) for n in ("gamma_q", "gamma_k", "beta_q", "beta_k")}
+    bufs = []
+    for _ in range(2):
+        q, k = inputs.to_device(d["q"], dev, torch), inputs.to_device(d["k"], dev, torch)
+        bufs.append((q, k, torch.empty_like(q), torch.empty_like(k)))
+
+    def fused(i):
+        q, k, oq, ok = bufs[i % len(bufs)]
+        ops.layernorm_fwd(q, k, par["gamma_q"], par["gamma_k"], w.n_shards, w.eps,
+                          beta_q=par["beta_q"], beta_k=par["beta_k"], out_q=oq, out_k=ok)
+
+    for i in range(args.warmup):
+        fused(i)
+    ms = timed(fused, args.steps, stream, torch)
+    if ops.check_fault() != ops.QKN_OK:
+        raise RuntimeError("LayerNorm prefill reported an exchange timeout")
+    nbytes = w.algorithmic_bytes()
+    out["prefill"] = {
+        "workload": f"T={w.T}, Q and K width {w.Hq}, bf16, gamma and beta, {w.n_shards} logical shards",
+        "algorithmic_bytes": nbytes, "ms": round(ms, 5),
+        "plan": ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards),
+        "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_LN))}
+    del bufs
+    torch.cuda.empty_cache()
+    wd = inputs.LN_DECODE
+    dd = inputs.make_host(wd)
+    t = {n: inputs.to_device(dd[n], dev, torch) for n in dd}
+    oq, ok = torch.empty_like(t["q"]), torch.empty_like(t["k"])
+
+    def dec(_):
+        ops.layernorm_fwd(t["q"], t["k"], t["gamma_q"], t["gamma_k"], wd.n_shards, wd.eps,
+                          beta_q=t["beta_q"], beta_k=t["beta_k"], out_q=oq, out_k=ok)
+
+    for i in range(50):
+        dec(i)
+    us = timed(dec, 1000, stream, torch) * 1e3
+    if ops.check_fault() != ops.QKN_OK:
+        raise RuntimeError("LayerNorm decode reported an exchange timeout")
+    out["decode"] = {"workload": "T=64, Q and K width 4096, bf16, 4 logical shards",
+                     "python_back_to_back_us_per_call": round(us, 2)}
+    return out
 
 
 def bench_e4m3(args, torch, stream, timed):
@@ -211,10 +264,18 @@ def main():
         for i in range(5):
             q, k, oq, ok = b8[0]
             ops.layerwise_fwd(q, k, gq8, gk8, w8.n_shards, w8.eps, out_q=oq, out_k=ok)
+        del b8
+        wl = inputs.LN_PREFILL
+        dl = inputs.make_host(wl)
+        tl = {n: inputs.to_device(dl[n], "cuda:0", torch) for n in dl}
+        for i in range(5):
+            ops.layernorm_fwd(tl["q"], tl["k"], tl["gamma_q"], tl["gamma_k"], wl.n_shards, wl.eps,
+                              beta_q=tl["beta_q"], beta_k=tl["beta_k"])
         torch.cuda.synchronize()
         assert ops.check_fault() == ops.QKN_OK
         log("pmc mode done: 5 fused bf16 prefill launches, 5 copy launches of "
-            f"{w.T * (w.Hq + w.Hk) * w.elem_bytes} bytes read, 5 fused E4M3->bf16 prefill launches")
+            f"{w.T * (w.Hq + w.Hk) * w.elem_bytes} bytes read, 5 fused E4M3->bf16 prefill launches, "
+            "5 fused LayerNorm prefill launches")
         return
 
     for i in range(args.warmup):
@@ -272,6 +333,8 @@ def main():
 
     log("timing E4M3 activations ...")
     e4m3 = bench_e4m3(args, torch, stream, timed)
+    log("timing LayerNorm ...")
+    layernorm = bench_layernorm(args, torch, stream, timed)
 
     traffic = read_traffic()
     out = {
@@ -303,6 +366,7 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
         "e4m3": e4m3,
+        "layernorm": layernorm,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

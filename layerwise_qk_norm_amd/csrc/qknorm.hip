@@ -445,8 +445,8 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     };
     // Launches measured fastest on MI355X for the prefill-sized Q/K shards of
     // the letter's models (width 5120 split 1, 2, 4 or 8 ways; 5120/1024 split
-    // 4 ways), for bf16 and E4M3 activations, used for batches of at least 4096
-    // tokens when nothing is forced and the device can hold them.
+    // 4 ways), for bf16 and E4M3 activations and for LayerNorm, used for batches
+    // of at least 4096 tokens when nothing is forced and the device can hold them.
     struct Tuned {
         int dtype, wq, wk, n, v, w, rows, wpc;
     };
@@ -462,6 +462,12 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_E4M3_BF16, 640, 640, 8, 7, 3, 4, 2},
         {QKN_FMT_E4M3_BF16, 1280, 256, 4, 7, 3, 4, 2},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 0, 10, 2, 2},
+        {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 2},
+        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 5, 1, 2},
+        {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 3, 1, 3},
+        {QKN_FMT_LN_BF16, 640, 640, 8, 7, 3, 2, 4},
+        {QKN_FMT_LN_BF16, 1280, 256, 4, 8, 2, 2, 3},
+        {QKN_FMT_LN_F32, 2560, 2560, 2, 9, 5, 1, 2},
     };
     const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0;
     if (!forced && T >= 4096) {

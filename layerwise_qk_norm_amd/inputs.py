@@ -18,6 +18,8 @@ Recipe (stated once, used everywhere):
 * gamma: ``U(0.5, 1.5)`` or ``N(1, 0.1^2)``, drawn in float64.
 * LayerNorm workloads add beta ``U(-0.5, 0.5)`` in gamma's format, and may shift
   the activations by a constant ``mu`` (mean offset) before rounding.
+* Headwise workloads draw gamma of length ``head_dim`` (one vector shared by
+  every head).
 * Storage: float64 -> float32 (round to nearest even), then for bf16
   float32 -> bf16 round to nearest even on the bit pattern. bf16 tensors are
   numpy ``uint16`` bit patterns. For E4M3 activations float32 -> E4M3 (OCP
@@ -56,8 +58,9 @@ class Workload:
     eps: float = EPS
     seed: int = 0
     out_dtype: str = ""  # output format; "" = the input format (E4M3: "bf16" or "e4m3")
-    norm: str = "rms"    # "rms" (RMSNorm) or "layer" (LayerNorm with beta)
+    norm: str = "rms"    # "rms" (RMSNorm), "layer" (LayerNorm with beta) or "head" (headwise)
     mu: float = 0.0      # constant added to every activation draw
+    head_dim: int = 0    # headwise: columns per head (gamma is [head_dim], shared by heads)
 
     def with_T(self, T: int) -> "Workload":
         return dataclasses.replace(self, T=T)
@@ -90,8 +93,9 @@ class Workload:
         """One read and one write of Q and K, plus gamma (and beta) of Q and K once."""
         per_col = self.elem_bytes + self.out_bytes
         params = 2 if self.norm == "layer" else 1
+        cols = 2 * self.head_dim if self.norm == "head" else self.Hq + self.Hk
         return (self.T * (self.Hq + self.Hk) * per_col +
-                params * (self.Hq + self.Hk) * _BYTES[self.gamma_dtype])
+                params * cols * _BYTES[self.gamma_dtype])
 
     def outlier_count(self, H: int) -> int:
         if self.outlier_frac <= 0:
@@ -128,6 +132,17 @@ LN_GQA = Workload("ln_gqa", 8192, 5120, 1024, 4, "bf16", outlier_frac=0.005, out
 LN_SHIFTED = Workload("ln_shifted", 1024, 4096, 4096, 4, "f32", mu=1.0, norm="layer")
 LN_CONFIGS = {w.name: w for w in (LN_TINY, LN_DECODE, LN_PREFILL, LN_GQA, LN_SHIFTED)}
 
+# headwise QK-Norm (one factor per head of 128 columns; letter, Section II-A) at the
+# same Q/K widths: 40 heads (5120), 32 heads (4096), 8 KV heads (1024)
+HW_TINY = Workload("hw_tiny", 8, 256, 256, 1, "f32", gamma_dist="normal", norm="head", head_dim=128)
+HW_DECODE = Workload("hw_decode", 64, 4096, 4096, 1, "bf16", outlier_frac=0.01, outlier_scale=20.0,
+                     norm="head", head_dim=128)
+HW_PREFILL = Workload("hw_prefill", 16384, 5120, 5120, 1, "bf16", sigma=2.0, norm="head",
+                      head_dim=128)
+HW_GQA = Workload("hw_gqa", 8192, 5120, 1024, 1, "bf16", outlier_frac=0.005, outlier_scale=50.0,
+                  norm="head", head_dim=128)
+HW_CONFIGS = {w.name: w for w in (HW_TINY, HW_DECODE, HW_PREFILL, HW_GQA)}
+
 SWEEP_T = (4096, 4097, 16384, 65536)
 SWEEP_H = (1024, 3072, 5120, 8192, 16384)
 SWEEP_N = (1, 2, 4, 8)
@@ -146,6 +161,14 @@ def sweep_layernorm() -> Iterator[Workload]:
     N in {1, 2, 4, 8}, bf16 and fp32, normal draws (48 points)."""
     for T, H, N, dt in itertools.product((4096, 16384), (1024, 5120, 16384), SWEEP_N, SWEEP_DTYPE):
         yield Workload(f"ln_sweep_T{T}_H{H}_N{N}_{dt}", T, H, H, N, dt, norm="layer")
+
+
+def sweep_headwise() -> Iterator[Workload]:
+    """Headwise RMSNorm: T in {4097, 16384}, H in {2048, 5120, 16384}, head_dim in
+    {64, 128, 256}, bf16 and fp32, normal draws (36 points)."""
+    for T, H, D, dt in itertools.product((4097, 16384), (2048, 5120, 16384), (64, 128, 256),
+                                         SWEEP_DTYPE):
+        yield Workload(f"hw_sweep_T{T}_H{H}_D{D}_{dt}", T, H, H, 1, dt, norm="head", head_dim=D)
 
 
 def sweep_e4m3() -> Iterator[Workload]:
@@ -249,11 +272,13 @@ def outlier_columns(w: Workload, which: str):
 def make_host(w: Workload, chunk_rows: int = 2048) -> dict:
     """Host arrays ``q, k, gamma_q, gamma_k`` (and ``beta_q, beta_k`` for LayerNorm)."""
     rq, rk, rgq, rgk, _, _, rbq, rbk = _streams(w.seed)
+    gq_len = w.head_dim if w.norm == "head" else w.Hq
+    gk_len = w.head_dim if w.norm == "head" else w.Hk
     d = {
         "q": _activations(rq, w.T, w.Hq, w, outlier_columns(w, "q"), chunk_rows),
         "k": _activations(rk, w.T, w.Hk, w, outlier_columns(w, "k"), chunk_rows),
-        "gamma_q": _gamma(rgq, w.Hq, w),
-        "gamma_k": _gamma(rgk, w.Hk, w),
+        "gamma_q": _gamma(rgq, gq_len, w),
+        "gamma_k": _gamma(rgk, gk_len, w),
     }
     if w.norm == "layer":
         d["beta_q"] = _beta(rbq, w.Hq, w)

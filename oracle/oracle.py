@@ -22,7 +22,8 @@ Algorithm 1, Phase A of the letter and Eqs. (3)-(4) of the notes' worked
 example (Section 4b). LayerNorm (``layernorm``, ``shard_stats``) follows the notes'
 Section 5e: mean and variance over the full vector, which shards reduce to two
 additive statistics (sum x, sum x^2); the oracle itself uses the two-pass
-definition of the variance.
+definition of the variance. Headwise RMSNorm (``headwise``) normalises each
+head of ``head_dim`` columns on its own (letter, Section II-A).
 """
 from __future__ import annotations
 
@@ -76,6 +77,10 @@ def _load():
         lib.oracle_shard_stats.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p]
+        lib.oracle_headwise.restype = ctypes.c_int
+        lib.oracle_headwise.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_decode_e4m3.restype = ctypes.c_int
         lib.oracle_decode_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_shard_sumsq.restype = ctypes.c_int
@@ -186,6 +191,43 @@ def layernorm(x: np.ndarray, gamma: np.ndarray, beta, eps: float, want_y: bool =
     return y, mu, rs
 
 
+def headwise(x: np.ndarray, gamma: np.ndarray, head_dim: int, eps: float, want_y: bool = True,
+             threads: int = 1):
+    """fp64 headwise RMSNorm via the C loops: one factor per (token, head) over the
+    head's ``head_dim`` columns; ``gamma`` is [head_dim], shared by the heads.
+    Returns ``(y, rinv)`` with ``rinv`` [T][n_heads]; ``y`` is None unless wanted."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    gamma = np.ascontiguousarray(gamma)
+    dt = _dtype_of(x)
+    if _dtype_of(gamma) != GAMMA_FORMAT[dt]:
+        raise TypeError(f"gamma must be {GAMMA_FORMAT[dt]} for {dt} inputs")
+    T, H = x.shape
+    if head_dim < 1 or H % head_dim or gamma.shape != (head_dim,):
+        raise ValueError("rows must be whole heads and gamma [head_dim]")
+    nh = H // head_dim
+    y = np.empty((T, H), np.float64) if want_y else None
+    r = np.empty((T, nh), np.float64)
+
+    def run(lo, hi):
+        if hi <= lo:
+            return
+        rc = lib.oracle_headwise(x.ctypes.data + lo * H * x.itemsize, gamma.ctypes.data,
+                                 DTYPE_CODE[dt], hi - lo, nh, head_dim, ctypes.c_float(eps),
+                                 None if y is None else y.ctypes.data + lo * H * 8,
+                                 r.ctypes.data + lo * nh * 8)
+        if rc != 0:
+            raise ValueError("oracle_headwise rejected its arguments")
+
+    if threads <= 1 or T < 2 * threads:
+        run(0, T)
+    else:
+        edges = np.linspace(0, T, threads + 1).astype(np.int64)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda i: run(int(edges[i]), int(edges[i + 1])), range(threads)))
+    return y, r
+
+
 def shard_stats(x: np.ndarray, n_shards: int):
     """Per-shard sums and sums of squares, each ``[n_shards][T]`` (fp64), via the C loops."""
     lib = _load()
@@ -271,6 +313,17 @@ def layernorm_np(x: np.ndarray, gamma: np.ndarray, beta, eps: float):
     denom = np.sqrt(var + float(np.float32(eps)))
     y = (xv - mu[:, None]) / denom[:, None] * g[None, :] + b[None, :]
     return y, mu, 1.0 / denom
+
+
+def headwise_np(x: np.ndarray, gamma: np.ndarray, head_dim: int, eps: float):
+    """NumPy float64 mirror of ``headwise`` (rows reshaped to [T, heads, head_dim])."""
+    xv = decode(x)
+    g = decode(gamma)
+    T, H = xv.shape
+    xh = xv.reshape(T, H // head_dim, head_dim)
+    denom = np.sqrt(np.mean(xh * xh, axis=2) + float(np.float32(eps)))
+    y = xh / denom[:, :, None] * g[None, None, :]
+    return y.reshape(T, H), 1.0 / denom
 
 
 def shard_stats_np(x: np.ndarray, n_shards: int):

@@ -243,3 +243,43 @@ int oracle_shard_stats(const void* x, int dtype, int64_t T, int64_t H, int n_sha
     }
     return 0;
 }
+
+/*
+ * Headwise RMSNorm: one factor per attention head instead of one per vector
+ * (letter, Section II-A: headwise QK-Norm normalises each head on its own).
+ * Row t of x holds n_heads heads of head_dim columns; head h is columns
+ * [h*D, (h+1)*D) and gamma [D] scales every head alike:
+ *
+ *   y[t][h*D + j] = x[t][h*D + j] / sqrt((1/D) sum_{i<D} x[t][h*D + i]^2 + eps) * gamma[j]
+ *
+ *   x [T][n_heads*D], gamma [D]; y [T][n_heads*D] unrounded, rinv [T][n_heads]
+ *   (either may be NULL). Returns 0, or -1 on a bad argument.
+ */
+int oracle_headwise(const void* x, const void* gamma, int dtype, int64_t T, int64_t n_heads,
+                    int64_t D, float eps, double* y, double* rinv)
+{
+    if (!x || (y && !gamma) || T < 0 || n_heads < 1 || D < 1 || !format_ok(dtype))
+        return -1;
+    const double e = (double)eps;
+    const int64_t H = n_heads * D;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < n_heads; ++h) {
+            double S = 0.0;
+            for (int64_t i = 0; i < D; ++i) {
+                const double v = load(x, dtype, t * H + h * D + i);
+                S += v * v;
+            }
+            const double denom = sqrt(S / (double)D + e);
+            if (rinv)
+                rinv[t * n_heads + h] = 1.0 / denom;
+            if (y) {
+                for (int64_t j = 0; j < D; ++j) {
+                    const double v = load(x, dtype, t * H + h * D + j);
+                    const double g = load(gamma, gamma_format(dtype), j);
+                    y[t * H + h * D + j] = v / denom * g;
+                }
+            }
+        }
+    }
+    return 0;
+}

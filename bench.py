@@ -18,6 +18,8 @@ Besides the headline (GB/s of algorithmic bytes), the line carries:
                  decode shape in us per call
   layernorm   -- LayerNorm (two additive shard statistics, gamma and beta) on the
                  prefill shape against the HBM roofline, and the decode shape
+  headwise    -- headwise QK-Norm (one factor per head of 128 columns) on the
+                 prefill shape against the HBM roofline
 
 Modes: ``--pmc`` runs only the kernels whose counters are collected
 (fused prefill in bf16, in E4M3->bf16 and as LayerNorm, and the copy of known
@@ -145,6 +147,35 @@ def bench_layernorm(args, torch, stream, timed):
         raise RuntimeError("LayerNorm decode reported an exchange timeout")
     out["decode"] = {"workload": "T=64, Q and K width 4096, bf16, 4 logical shards",
                      "python_back_to_back_us_per_call": round(us, 2)}
+    return out
+
+
+def bench_headwise(args, torch, stream, timed):
+    """Headwise QK-Norm (one factor per head of 128 columns) on the prefill shape."""
+    from layerwise_qk_norm_amd import inputs, ops
+    w = inputs.HW_PREFILL
+    d = inputs.make_host(w)
+    dev = "cuda:0"
+    gq, gk = inputs.to_device(d["gamma_q"], dev, torch), inputs.to_device(d["gamma_k"], dev, torch)
+    bufs = []
+    for _ in range(2):
+        q, k = inputs.to_device(d["q"], dev, torch), inputs.to_device(d["k"], dev, torch)
+        bufs.append((q, k, torch.empty_like(q), torch.empty_like(k)))
+
+    def fused(i):
+        q, k, oq, ok = bufs[i % len(bufs)]
+        ops.headwise_fwd(q, k, gq, gk, w.head_dim, w.eps, out_q=oq, out_k=ok)
+
+    for i in range(args.warmup):
+        fused(i)
+    ms = timed(fused, args.steps, stream, torch)
+    nbytes = w.algorithmic_bytes()
+    out = {"prefill": {
+        "workload": f"T={w.T}, Q and K width {w.Hq} ({w.Hq // w.head_dim} heads of {w.head_dim}), bf16",
+        "algorithmic_bytes": nbytes, "ms": round(ms, 5),
+        "roofline": roofline(nbytes, ms, None)}}
+    del bufs
+    torch.cuda.empty_cache()
     return out
 
 
@@ -335,6 +366,8 @@ def main():
     e4m3 = bench_e4m3(args, torch, stream, timed)
     log("timing LayerNorm ...")
     layernorm = bench_layernorm(args, torch, stream, timed)
+    log("timing headwise ...")
+    headwise = bench_headwise(args, torch, stream, timed)
 
     traffic = read_traffic()
     out = {
@@ -367,6 +400,7 @@ def main():
                      "traffic": traffic},
         "e4m3": e4m3,
         "layernorm": layernorm,
+        "headwise": headwise,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

@@ -166,6 +166,31 @@ int qknorm_apply_norm_f32(const void* x, const void* gamma, const void* beta,
                           const float* mean, const float* rstd, int64_t T, int64_t H,
                           void* out, hipStream_t stream);
 
+/* ------------------------------------------------------------------ headwise
+ * Headwise QK-Norm ("SwiftQK", Section II-A): one factor per attention head
+ * instead of one per full vector. Row t of q holds heads_q heads of head_dim
+ * columns (head h = columns [h*head_dim, (h+1)*head_dim)), and likewise k;
+ * gamma_q and gamma_k are [head_dim], each shared by all heads of its tensor:
+ *
+ *   y[t][h*D + j] = x[t][h*D + j] / sqrt((1/D) sum_{i<D} x[t][h*D+i]^2 + eps) * gamma[j]
+ *
+ * When tensor parallelism splits the heads (not the columns of a head) across
+ * ranks, no shard exchange is needed: this is the method's degenerate case,
+ * one streaming pass with the reduction inside each head's lanes, and it takes
+ * no shard count. Conventions as above (in place allowed, T == 0 no-op). The
+ * 128-bit path needs 16-byte aligned pointers and a head of 1, 2, 4, ... or 64
+ * 16-byte vectors (bf16 head_dim 8..512, f32 4..256); other shapes are still
+ * correct (one wave per head).
+ */
+int qknorm_headwise_fwd_bf16(const void* q, const void* k, const void* gamma_q,
+                             const void* gamma_k, int64_t T, int64_t heads_q, int64_t heads_k,
+                             int64_t head_dim, float eps, void* out_q, void* out_k,
+                             hipStream_t stream);
+int qknorm_headwise_fwd_f32(const void* q, const void* k, const void* gamma_q,
+                            const void* gamma_k, int64_t T, int64_t heads_q, int64_t heads_k,
+                            int64_t head_dim, float eps, void* out_q, void* out_k,
+                            hipStream_t stream);
+
 /* ------------------------------------------------------------------ split
  * The same computation for one tensor as three stream-ordered launches, with
  * the intermediate statistics in caller-owned device buffers (the unfused

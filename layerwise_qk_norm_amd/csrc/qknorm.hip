@@ -663,6 +663,77 @@ int launch_apply_norm(int fmt, const void* x, const void* g, const void* bt, con
     return QKN_OK;
 }
 
+// ---------------------------------------------------------------- headwise
+
+template <class DT>
+void launch_headwise_as(int vh, dim3 g, hipStream_t s, const qkn::HeadwiseParams& p)
+{
+    switch (vh) {
+    case 1: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 1>), g, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 2>), g, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 4>), g, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 8>), g, dim3(256), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 16>), g, dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 32>), g, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 64>), g, dim3(256), 0, s, p); break;
+    }
+}
+
+int headwise_fwd(int fmt, const void* q, const void* k, const void* gq, const void* gk, int64_t T,
+                 int64_t hq, int64_t hk, int64_t D, float eps, void* oq, void* ok,
+                 hipStream_t stream)
+{
+    t_hip_error.clear();
+    if (T < 0 || hq < 1 || hk < 1 || D < 1 || hq * D > (int64_t(1) << 28) ||
+        hk * D > (int64_t(1) << 28) || !eps_ok(eps))
+        return QKN_EINVAL;
+    if (T == 0) return QKN_OK;
+    if (!q || !k || !gq || !gk || !oq || !ok) return QKN_EINVAL;
+    const Fmt f = fmt_of(fmt);
+    const int64_t Hq = hq * D, Hk = hk * D;
+    const Range rq = range_of(q, T * Hq * f.in), rk = range_of(k, T * Hk * f.in);
+    const Range rgq = range_of(gq, D * f.gam), rgk = range_of(gk, D * f.gam);
+    const Range roq = range_of(oq, T * Hq * f.out), rok = range_of(ok, T * Hk * f.out);
+    if (overlaps(roq, rok)) return QKN_EOVERLAP;
+    if (overlaps(roq, rq) && !same(roq, rq)) return QKN_EOVERLAP;
+    if (overlaps(rok, rk) && !same(rok, rk)) return QKN_EOVERLAP;
+    if (overlaps(roq, rk) || overlaps(roq, rgq) || overlaps(roq, rgk)) return QKN_EOVERLAP;
+    if (overlaps(rok, rq) || overlaps(rok, rgq) || overlaps(rok, rgk)) return QKN_EOVERLAP;
+    qkn::HeadwiseParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x[0] = q;
+    p.x[1] = k;
+    p.gamma[0] = gq;
+    p.gamma[1] = gk;
+    p.y[0] = oq;
+    p.y[1] = ok;
+    p.D = (int32_t)D;
+    p.heads[0] = (int32_t)hq;
+    p.heads[1] = (int32_t)hk;
+    p.T = T;
+    p.eps = eps;
+    // 128-bit path: whole 16-byte vectors per head, a power of two of them (<= 64)
+    const int64_t vh = D * f.in % 16 == 0 ? D * f.in / 16 : 0;
+    const bool vec = vh >= 1 && vh <= 64 && (vh & (vh - 1)) == 0 && aligned16(q) && aligned16(k) &&
+                     aligned16(gq) && aligned16(gk) && aligned16(oq) && aligned16(ok);
+    if (vec) {
+        p.nv[0] = T * Hq * f.in / 16;
+        p.nv[1] = T * Hk * f.in / 16;
+        p.blocks_q = (p.nv[0] + 255) / 256;
+        const int64_t blocks = p.blocks_q + (p.nv[1] + 255) / 256;
+        if (blocks > 0x7fffffff) return QKN_EINVAL;
+        if (f.in == 2) launch_headwise_as<Bf16>((int)vh, dim3((unsigned)blocks), stream, p);
+        else launch_headwise_as<F32>((int)vh, dim3((unsigned)blocks), stream, p);
+    } else {
+        const int64_t blocks = (T * (hq + hk) + 3) / 4;
+        if (blocks > 0x7fffffff) return QKN_EINVAL;
+        if (f.in == 2) hipLaunchKernelGGL((qkn::headwise_scalar_kernel<Bf16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((qkn::headwise_scalar_kernel<F32>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    }
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
 // ---------------------------------------------------------------- fused entry
 
 // bq, bk: LayerNorm's beta (either may be null); null for the RMSNorm formats
@@ -1013,6 +1084,22 @@ int qknorm_apply_norm_f32(const void* x, const void* gamma, const void* beta, co
                           const float* rstd, int64_t T, int64_t H, void* out, hipStream_t stream)
 {
     return apply_norm_entry(QKN_FMT_LN_F32, x, gamma, beta, mean, rstd, T, H, out, stream);
+}
+
+int qknorm_headwise_fwd_bf16(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
+                             int64_t T, int64_t heads_q, int64_t heads_k, int64_t head_dim,
+                             float eps, void* out_q, void* out_k, hipStream_t stream)
+{
+    return headwise_fwd(QKN_FMT_BF16, q, k, gamma_q, gamma_k, T, heads_q, heads_k, head_dim, eps,
+                        out_q, out_k, stream);
+}
+
+int qknorm_headwise_fwd_f32(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
+                            int64_t T, int64_t heads_q, int64_t heads_k, int64_t head_dim,
+                            float eps, void* out_q, void* out_k, hipStream_t stream)
+{
+    return headwise_fwd(QKN_FMT_F32, q, k, gamma_q, gamma_k, T, heads_q, heads_k, head_dim, eps,
+                        out_q, out_k, stream);
 }
 
 int qknorm_check_fault(hipStream_t stream)

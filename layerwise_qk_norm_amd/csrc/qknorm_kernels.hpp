@@ -848,6 +848,122 @@ apply_norm_kernel(const void* x_, const void* g_, const void* b_, const float* m
     }
 }
 
+// ================================================================ headwise
+
+// Headwise QK-Norm: one factor per (token, head) over the head's D columns,
+// gamma [D] shared by every head ("SwiftQK", Section II-A: headwise QK-Norm
+// normalises each head on its own). When heads are not split across shards no
+// exchange is needed, so this is one streaming pass.
+struct HeadwiseParams {
+    const void* x[2];      // q [T][Hq], k [T][Hk]
+    const void* gamma[2];  // [D] each
+    void* y[2];
+    int64_t nv[2];         // 16-byte vectors of q and of k
+    int64_t blocks_q;      // workgroups [0, blocks_q) cover q, the rest cover k
+    int32_t D;             // head_dim
+    int32_t heads[2];      // scalar kernel only: heads per row of q and of k
+    int64_t T;             // scalar kernel only
+    float eps;
+};
+
+// Sum over aligned groups of G lanes (G a power of two <= 64), left in every
+// lane of the group, bit-identical across the group (each step adds a pair of
+// values that both lanes of the pair hold).
+template <int G>
+__device__ __forceinline__ float group_sum(float v)
+{
+#define QKN_DPP(ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false))
+    if constexpr (G >= 2) v += QKN_DPP(0xB1);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v += QKN_DPP(0x4E);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += QKN_DPP(0x141);  // row_half_mirror
+    if constexpr (G >= 16) v += QKN_DPP(0x140); // row_mirror
+#undef QKN_DPP
+    if constexpr (G >= 32) v += __shfl_xor(v, 16);
+    if constexpr (G >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// 128-bit path: a head is VH consecutive 16-byte vectors (VH a power of two
+// <= 64, so heads never straddle a wave and workgroups of 256 vectors hold
+// whole heads); one vector per thread. Each workgroup reads and writes through
+// a descriptor of its own 4 KiB, so lanes past the end load 0 and store
+// nothing while still taking part in the group reduction.
+template <class DT, int VH>
+__global__ void __launch_bounds__(256)
+headwise_kernel(HeadwiseParams p)
+{
+    constexpr int EV = DT::kVec;
+    using gam_t = typename DT::gam_t;
+    constexpr int ES = (int)sizeof(typename DT::in_t);
+    constexpr int OS = (int)sizeof(typename DT::out_t);
+    const bool in_q = (int64_t)blockIdx.x < p.blocks_q;
+    const int t = in_q ? 0 : 1;
+    const int64_t v0 = ((int64_t)blockIdx.x - (in_q ? 0 : p.blocks_q)) * 256;
+    const int64_t left = p.nv[t] - v0;
+    const int nvec = (int)(left < 256 ? left : 256);
+    const char* xb = static_cast<const char*>(p.x[t]) + v0 * 16;
+    char* yb = static_cast<char*>(p.y[t]) + v0 * (16 / ES) * OS;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(xb), (short)0, nvec * 16, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc(yb, (short)0, nvec * 16 / ES * OS, 0x00020000);
+    const int c = (threadIdx.x & (VH - 1)) * EV;  // column within the head
+    const u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(rx, threadIdx.x * 16, 0, kNT);
+    u32x4 gw[DT::kGam];
+#pragma unroll
+    for (int j = 0; j < DT::kGam; ++j)
+        gw[j] = ld_cached(static_cast<const gam_t*>(p.gamma[t]) + c + j * (16 / (int)sizeof(gam_t)));
+    float f[EV], g[EV];
+    unpack(DT{}, xv, f);
+    unpack_gamma(DT{}, gw, g);
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) sq = fmaf(f[e], f[e], sq);
+    const float S = group_sum<VH>(sq);
+    const float r = 1.0f / sqrtf(S / (float)p.D + p.eps);
+    float o[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) o[e] = (f[e] * g[e]) * r;
+    u32x4 w[DT::kOut];
+    pack_out(DT{}, o, w);
+#pragma unroll
+    for (int j = 0; j < DT::kOut; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(w[j], ry, threadIdx.x * 16 / ES * OS + 16 * j, 0, kNT);
+}
+
+// Any layout: one wave per (token, head), q's items first; elementwise loads.
+template <class DT>
+__global__ void __launch_bounds__(256)
+headwise_scalar_kernel(HeadwiseParams p)
+{
+    using in_t = typename DT::in_t;
+    using gam_t = typename DT::gam_t;
+    using out_t = typename DT::out_t;
+    const int lane = threadIdx.x & 63;
+    int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t items_q = p.T * p.heads[0];
+    int t = 0;
+    if (item >= items_q) {
+        item -= items_q;
+        t = 1;
+        if (item >= p.T * p.heads[1]) return;  // wave-uniform
+    }
+    const int64_t row = item / p.heads[t];
+    const int64_t h = item - row * p.heads[t];
+    const int64_t base = row * (int64_t)p.heads[t] * p.D + h * p.D;
+    const in_t* x = static_cast<const in_t*>(p.x[t]) + base;
+    const gam_t* g = static_cast<const gam_t*>(p.gamma[t]);
+    out_t* y = static_cast<out_t*>(p.y[t]) + base;
+    float acc = 0.f;
+    for (int j = lane; j < p.D; j += 64) {
+        const float f = to_f32(x[j]);
+        acc = fmaf(f, f, acc);
+    }
+    const float r = 1.0f / sqrtf(wave_sum(acc) / (float)p.D + p.eps);
+    for (int j = lane; j < p.D; j += 64) from_f32((to_f32(x[j]) * to_f32(g[j])) * r, y + j);
+}
+
 // ================================================================ copy ceiling
 
 // One 16-byte nontemporal vector per thread through a descriptor covering

@@ -70,6 +70,8 @@ _SIGS = {
     "qknorm_combine_stats": [_P, _P, _I64, _I64, _I, _F, _P, _P, _P],
     "qknorm_apply_norm_bf16": [_P, _P, _P, _P, _P, _I64, _I64, _P, _P],
     "qknorm_apply_norm_f32": [_P, _P, _P, _P, _P, _I64, _I64, _P, _P],
+    "qknorm_headwise_fwd_bf16": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _P],
+    "qknorm_headwise_fwd_f32": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _P],
     "qknorm_check_fault": [_P],
     "qknorm_strerror": [_I],
     "qknorm_last_hip_error": [],
@@ -268,6 +270,41 @@ def layernorm_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-5, beta
         _check(fn(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
                   _ptr_or_null(beta_q), _ptr_or_null(beta_k), T, Hq, Hk, n_shards, eps,
                   out_q.data_ptr(), out_k.data_ptr(), _stream(dev)), "qknorm_layernorm_fwd")
+    return out_q, out_k
+
+
+def headwise_fwd(q, k, gamma_q, gamma_k, head_dim: int, eps: float = 1e-6, out_q=None,
+                 out_k=None):
+    """Headwise RMSNorm of q and k (one factor per head of ``head_dim`` columns;
+    gamma_q and gamma_k are [head_dim]); returns ``(out_q, out_k)``."""
+    _need(q, "q", 2)
+    dt = q.dtype
+    dev = q.device
+    code = _dtype_code(q)
+    if code == QKN_E4M3:
+        raise TypeError("headwise takes bfloat16 or float32 tensors")
+    _need(k, "k", 2, dt, dev)
+    _need(gamma_q, "gamma_q", 1, dt, dev)
+    _need(gamma_k, "gamma_k", 1, dt, dev)
+    T, Hq = q.shape
+    Hk = k.shape[1]
+    if k.shape[0] != T:
+        raise ValueError("q and k must have the same number of tokens")
+    if head_dim < 1 or Hq % head_dim or Hk % head_dim:
+        raise ValueError("q and k rows must be whole heads of head_dim columns")
+    if gamma_q.shape[0] != head_dim or gamma_k.shape[0] != head_dim:
+        raise ValueError("gamma_q and gamma_k must be [head_dim]")
+    out_q = torch.empty_like(q) if out_q is None else out_q
+    out_k = torch.empty_like(k) if out_k is None else out_k
+    _need(out_q, "out_q", 2, dt, dev)
+    _need(out_k, "out_k", 2, dt, dev)
+    if out_q.shape != q.shape or out_k.shape != k.shape:
+        raise ValueError("outputs must have the shapes of q and k")
+    fn = getattr(lib(), f"qknorm_headwise_fwd_{_suffix(code)}")
+    with torch.cuda.device(dev):
+        _check(fn(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), T,
+                  Hq // head_dim, Hk // head_dim, head_dim, eps, out_q.data_ptr(),
+                  out_k.data_ptr(), _stream(dev)), "qknorm_headwise_fwd")
     return out_q, out_k
 
 

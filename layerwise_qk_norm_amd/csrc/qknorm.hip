@@ -763,6 +763,27 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
         if (overlaps(roq, rbq) || overlaps(roq, rbk) || overlaps(rok, rbq) || overlaps(rok, rbk))
             return QKN_EOVERLAP;
     }
+    // The fused kernel addresses each tensor with 32-bit offsets into one buffer
+    // descriptor: every tensor of a launch stays 64 KiB below 2^31 bytes, so
+    // an unused lane's offset (2^31 + the tile's row offset + the store's word
+    // offset) still fits in 32 bits. Longer batches run as consecutive launches
+    // over token ranges (rows are independent, so the result is the same).
+    // H <= 2^28 keeps tmax >= 1.
+    const int64_t row_bytes = std::max(Hq, Hk) * std::max(f.in, f.out);
+    const int64_t tmax = ((int64_t(1) << 31) - (int64_t(1) << 16)) / row_bytes;
+    if (T > tmax) {
+        for (int64_t t0 = 0; t0 < T; t0 += tmax) {
+            const int64_t tc = std::min(tmax, T - t0);
+            auto at = [&](const void* b, int64_t H, int e) {
+                return static_cast<const void*>(static_cast<const char*>(b) + t0 * H * e);
+            };
+            rc = layerwise_fwd(dtype, at(q, Hq, f.in), at(k, Hk, f.in), gq, gk, bq, bk, tc, Hq, Hk,
+                               N, eps, const_cast<void*>(at(oq, Hq, f.out)),
+                               const_cast<void*>(at(ok, Hk, f.out)), stream);
+            if (rc) return rc;
+        }
+        return QKN_OK;
+    }
 
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     QKN_HIP(hipStreamIsCapturing(stream, &cap));

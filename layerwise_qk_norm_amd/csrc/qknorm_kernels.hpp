@@ -205,25 +205,27 @@ __device__ __forceinline__ unsigned long long slot_read(const unsigned long long
 
 // ---------------------------------------------------------------- reductions
 
-// Sum over a full wave64 (EXEC must be all ones). Rows of 16 lanes reduce with
-// DPP (xor 1, xor 2, half-mirror, mirror), leaving the row sum in every lane
-// of the row; the four row sums are then added in lane order 0, 16, 32, 48.
-// Fixed order, so results are bitwise reproducible.
+// Sum over a full wave64 (EXEC must be all ones), returned as a wave-uniform
+// value. Rows of 16 lanes reduce with DPP (xor 1, xor 2, half-mirror, mirror),
+// leaving each row's sum in every lane of the row; row_bcast:15 then adds row
+// 0's sum into row 1 and row 2's into row 3, and row_bcast:31 adds rows 0+1
+// into rows 2 and 3, so lane 63 ends with (r3 + r2) + (r1 + r0). Fixed order,
+// so results are bitwise reproducible.
 __device__ __forceinline__ float wave_sum(float v)
 {
 #define QKN_DPP(ctrl) \
     __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false))
-    v += QKN_DPP(0xB1);   // quad_perm [1,0,3,2]
-    v += QKN_DPP(0x4E);   // quad_perm [2,3,0,1]
-    v += QKN_DPP(0x141);  // row_half_mirror
-    v += QKN_DPP(0x140);  // row_mirror
+#define QKN_DPP_ROWS(ctrl, rows) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rows, 0xF, false))
+    v += QKN_DPP(0xB1);           // quad_perm [1,0,3,2]
+    v += QKN_DPP(0x4E);           // quad_perm [2,3,0,1]
+    v += QKN_DPP(0x141);          // row_half_mirror
+    v += QKN_DPP(0x140);          // row_mirror
+    v += QKN_DPP_ROWS(0x142, 0xA);  // row_bcast:15 into rows 1 and 3 (rows 0, 2 add 0)
+    v += QKN_DPP_ROWS(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+#undef QKN_DPP_ROWS
 #undef QKN_DPP
-    const int b = __builtin_bit_cast(int, v);
-    float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-    float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-    float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-    float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-    return ((r0 + r1) + r2) + r3;
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // ================================================================ fused kernel
@@ -404,19 +406,22 @@ fused_qknorm_kernel(FusedParams p)
     }
 
     // ===================== data waves ========================================
-    // Memory access goes through per-tile buffer descriptors: a lane whose slot
-    // is unused, or whose row lies past T, carries an offset beyond the
-    // descriptor's range, so its load returns 0 and its store is dropped by the
-    // hardware. Every load and store is therefore unconditional, which keeps
-    // vmcnt accounting exact: the prefetched tile can be consumed while the
-    // previous tile's stores are still in flight.
+    // Memory access goes through one buffer descriptor per tensor, built once:
+    // a lane's byte offset is its slot offset within the tile plus the tile's
+    // row offset. A lane whose slot is unused carries 0x80000000, and a row past
+    // T lies past T*H elements, so either offset is beyond the descriptor's range
+    // (the host keeps every tensor of a launch below 2^31 bytes): its load
+    // returns 0 and its store is dropped by the hardware. Every load and store
+    // is therefore unconditional, which keeps vmcnt accounting exact: the
+    // prefetched tile can be consumed while the previous tile's stores are still
+    // in flight.
     const int dwave = wave - 1;
     const int ndt = 64 * nwd;  // data threads
     const int dt = tid - 64;
     const int VQ = rows * p.Wv[0];
     const int VQp = (VQ + 63) & ~63;  // K starts on a wave boundary
     const int V = VQp + rows * p.Wv[1];
-    constexpr uint32_t kOOB = 0x7ffffff0u;
+    constexpr uint32_t kOOB = 0x80000000u;
     constexpr int ES = (int)sizeof(in_t);
     constexpr int OS = (int)sizeof(typename DT::out_t);
 
@@ -447,7 +452,9 @@ fused_qknorm_kernel(FusedParams p)
         tk[i] = t != 0;
         voff[i] = valid ? (uint32_t)((r * p.H[t] + col) * ES) : kOOB;
         ooff[i] = ES == OS ? voff[i] : (valid ? (uint32_t)((r * p.H[t] + col) * OS) : kOOB);
-        seg[i] = valid ? t * rows + r : 0;
+        // unused slots take their tensor's last segment, which keeps segments
+        // non-decreasing along (slot, lane) (their squares are 0)
+        seg[i] = valid ? t * rows + r : t * rows + rows - 1;
 #pragma unroll
         for (int g = 0; g < KG; ++g)
             gam_lds[(i * ndt + dt) * KG + g] =
@@ -465,61 +472,72 @@ fused_qknorm_kernel(FusedParams p)
     }
 
     auto tile_of = [&](int k) __attribute__((always_inline)) -> int64_t { return group + (int64_t)k * p.n_groups; };
-    // descriptor of a tile's rows of one tensor, elements of `eb` bytes
-    auto rsrc = [&](const void* base, int t, int64_t t0, int eb) __attribute__((always_inline)) {
-        // rows of this tile that exist; 0 past the end (then every access is out of range)
-        const int64_t left = p.T - t0;
-        const int vr = left <= 0 ? 0 : (left < rows ? (int)left : rows);
-        const char* b = static_cast<const char*>(base) + t0 * p.H[t] * eb;
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, vr * p.H[t] * eb,
-                                                 0x00020000);
+    // whole-tensor descriptors, elements of `eb` bytes
+    auto rsrc = [&](const void* base, int t, int eb) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                                 (int)(p.T * p.H[t] * eb), 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t dxq = rsrc(p.x[0], 0, ES), dxk = rsrc(p.x[1], 1, ES);
+    const __amdgpu_buffer_rsrc_t dyq = rsrc(p.y[0], 0, OS), dyk = rsrc(p.y[1], 1, OS);
+    // byte offset of a tile's first row in tensor t; a tile past the end is
+    // placed at row T, where every access is out of range
+    auto row_off = [&](int64_t tile, int t, int eb) __attribute__((always_inline)) -> uint32_t {
+        int64_t t0 = tile * rows;
+        t0 = t0 < p.T ? t0 : p.T;
+        return (uint32_t)(t0 * p.H[t] * eb);
     };
     auto load_tile = [&](int64_t tile, u32x4 (&buf)[VPT]) __attribute__((always_inline)) {
-        const int64_t t0 = tile * rows;
-        const __amdgpu_buffer_rsrc_t rq = rsrc(p.x[0], 0, t0, ES);
-        const __amdgpu_buffer_rsrc_t rk = rsrc(p.x[1], 1, t0, ES);
+        const uint32_t oq = row_off(tile, 0, ES), ok = row_off(tile, 1, ES);
 #pragma unroll
         for (int i = 0; i < VPT; ++i)
-            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(tk[i] ? rk : rq, voff[i], 0, kNT);
+            buf[i] = __builtin_amdgcn_raw_buffer_load_b128(tk[i] ? dxk : dxq, voff[i] + (tk[i] ? ok : oq),
+                                                           0, kNT);
     };
     // ---- Phase A: local sums of squares (fp32) of the tile in buf -> red[par]
-    // (LayerNorm: also the sums of x, after the sums of squares in red[par])
+    // (LayerNorm: also the sums of x, after the sums of squares in red[par]).
+    // Along this wave's (slot, lane) order the segments never decrease (slot
+    // i+1 starts ndt >= 64 vectors after slot i, lanes are consecutive), and a
+    // slot's lanes span segments seg(lane 0)..seg(lane 63), usually one. Each
+    // slot is reduced over the wave once per segment it spans; runs of one
+    // segment add up in a wave-uniform register and lane 0 writes every
+    // finished segment (segments the wave does not touch stay 0).
     auto phase_a = [&](const u32x4 (&buf)[VPT], int par) __attribute__((always_inline)) {
-        float acc[kMaxSeg];
-        float acc1[NORM ? kMaxSeg : 1];
-#pragma unroll
-        for (int s = 0; s < kMaxSeg; ++s) acc[s] = 0.f;
-        if constexpr (NORM) {
-#pragma unroll
-            for (int s = 0; s < kMaxSeg; ++s) acc1[s] = 0.f;
-        }
+        if (lane < NSTAT * nseg) red[par][dwave][lane] = 0.f;
+        int cur = __builtin_amdgcn_readfirstlane(seg[0]);
+        float run = 0.f, run1 = 0.f;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             float f[EV];
             unpack(DT{}, buf[i], f);
-            float sq = 0.f;
+            float sq = 0.f, sm = 0.f;
 #pragma unroll
             for (int e = 0; e < EV; ++e) sq = fmaf(f[e], f[e], sq);
-#pragma unroll
-            for (int s = 0; s < kMaxSeg; ++s) acc[s] += (seg[i] == s) ? sq : 0.f;
             if constexpr (NORM) {
-                float sm = 0.f;
 #pragma unroll
                 for (int e = 0; e < EV; ++e) sm += f[e];
-#pragma unroll
-                for (int s = 0; s < kMaxSeg; ++s) acc1[s] += (seg[i] == s) ? sm : 0.f;
+            }
+            const int s0 = __builtin_amdgcn_readfirstlane(seg[i]);
+            const int s1 = __builtin_amdgcn_readlane(seg[i], 63);
+            for (int s = s0; s <= s1; ++s) {
+                const bool mine_s = s0 == s1 || seg[i] == s;
+                const float w = wave_sum(mine_s ? sq : 0.f);
+                const float w1 = NORM ? wave_sum(mine_s ? sm : 0.f) : 0.f;
+                if (s != cur) {
+                    if (lane == 0) {
+                        red[par][dwave][cur] = run;
+                        if constexpr (NORM) red[par][dwave][nseg + cur] = run1;
+                    }
+                    run = 0.f;
+                    run1 = 0.f;
+                    cur = s;
+                }
+                run += w;
+                run1 += w1;
             }
         }
-#pragma unroll
-        for (int s = 0; s < kMaxSeg; ++s) {
-            if (s < nseg) {
-                const float w = wave_sum(acc[s]);
-                if (lane == 0) red[par][dwave][s] = w;
-                if constexpr (NORM) {
-                    const float w1 = wave_sum(acc1[s]);
-                    if (lane == 0) red[par][dwave][nseg + s] = w1;
-                }
-            }
+        if (lane == 0) {
+            red[par][dwave][cur] = run;
+            if constexpr (NORM) red[par][dwave][nseg + cur] = run1;
         }
     };
     // ---- Phase B (compute path): u = x * gamma, independent of the exchange
@@ -535,9 +553,7 @@ fused_qknorm_kernel(FusedParams p)
     };
     // ---- Phase C: y = u * rinv, one rounding to the output format, stored
     auto phase_c = [&](const float (&u)[VPT][EV], int64_t tile, int par) __attribute__((always_inline)) {
-        const int64_t t0 = tile * rows;
-        const __amdgpu_buffer_rsrc_t oq = rsrc(p.y[0], 0, t0, OS);
-        const __amdgpu_buffer_rsrc_t ok = rsrc(p.y[1], 1, t0, OS);
+        const uint32_t oq = row_off(tile, 0, OS), ok = row_off(tile, 1, OS);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const float r = rinv_s[par][seg[i]];
@@ -558,7 +574,8 @@ fused_qknorm_kernel(FusedParams p)
             pack_out(DT{}, o, w);
 #pragma unroll
             for (int j = 0; j < KO; ++j)
-                __builtin_amdgcn_raw_buffer_store_b128(w[j], tk[i] ? ok : oq, ooff[i] + 16 * j, 0, kNT);
+                __builtin_amdgcn_raw_buffer_store_b128(w[j], tk[i] ? dyk : dyq,
+                                                       ooff[i] + (tk[i] ? ok : oq) + 16 * j, 0, kNT);
         }
     };
 

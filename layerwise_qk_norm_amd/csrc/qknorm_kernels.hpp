@@ -427,33 +427,66 @@ fused_qknorm_kernel(FusedParams p)
 
     // Static per-slot layout (identical for every tile). tensor is uniform per
     // (wave, slot) because Q's part is padded to whole waves.
+    // Two output words per vector (E4M3 in, bf16 out: 32 output bytes per
+    // 16-byte input vector). Before storing, v_permlane32_swap exchanges the
+    // upper half-wave's first words with the lower half-wave's second words,
+    // so the first store covers the slot's vectors 0..31 and the second its
+    // vectors 32..63, each as whole lines (lanes 0-31 write first halves,
+    // lanes 32-63 second halves).
+    constexpr bool kPair = KO == 2;
     uint32_t voff[VPT];  // input byte offset from the tile's first row, or kOOB
     uint32_t ooff[VPT];  // output byte offset (equal to voff when ES == OS)
+    uint32_t poff[kPair ? VPT : 1][2];  // kPair: the lane's offsets for its two stores
     int seg[VPT];        // segment: tensor * rows + row
     bool tk[VPT];        // slot belongs to K (wave-uniform)
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int vbase = i * ndt + dwave * 64;
-        const int v = vbase + lane;
         const int t = vbase >= VQp ? 1 : 0;
         int r, c;
         bool valid;
-        if (t == 0) {
-            valid = v < VQ;
-            r = v / p.Wv[0];
-            c = v - r * p.Wv[0];
+        if constexpr (!kPair) {
+            const int v = vbase + lane;
+            if (t == 0) {
+                valid = v < VQ;
+                r = v / p.Wv[0];
+                c = v - r * p.Wv[0];
+            } else {
+                valid = v < V;
+                const int u = v - VQp;
+                r = u / p.Wv[1];
+                c = u - r * p.Wv[1];
+            }
         } else {
-            valid = v < V;
-            const int u = v - VQp;
-            r = u / p.Wv[1];
-            c = u - r * p.Wv[1];
+            // (valid, row, column vector) of the slot's vector vbase + m
+            auto locate = [&](int m, int& rr, int& cc) __attribute__((always_inline)) -> bool {
+                const int v = vbase + m;
+                if (t == 0) {
+                    rr = v / p.Wv[0];
+                    cc = v - rr * p.Wv[0];
+                    return v < VQ;
+                }
+                const int u = v - VQp;
+                rr = u / p.Wv[1];
+                cc = u - rr * p.Wv[1];
+                return v < V;
+            };
+            valid = locate(lane, r, c);
+            // store h covers vector 32h + (lane & 31); lanes 32-63 write its second half
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                int r2, c2;
+                const bool ok = locate(32 * h + (lane & 31), r2, c2);
+                poff[i][h] = ok ? (uint32_t)((r2 * p.H[t] + (shard * p.Wv[t] + c2) * EV) * OS + 16 * (lane >> 5))
+                                : kOOB;
+            }
         }
         const int col = (shard * p.Wv[t] + c) * EV;
         tk[i] = t != 0;
         voff[i] = valid ? (uint32_t)((r * p.H[t] + col) * ES) : kOOB;
         ooff[i] = ES == OS ? voff[i] : (valid ? (uint32_t)((r * p.H[t] + col) * OS) : kOOB);
         // unused slots take their tensor's last segment, which keeps segments
-        // non-decreasing along (slot, lane) (their squares are 0)
+        // non-decreasing along (slot, vector) (their squares are 0)
         seg[i] = valid ? t * rows + r : t * rows + rows - 1;
 #pragma unroll
         for (int g = 0; g < KG; ++g)
@@ -495,9 +528,10 @@ fused_qknorm_kernel(FusedParams p)
     };
     // ---- Phase A: local sums of squares (fp32) of the tile in buf -> red[par]
     // (LayerNorm: also the sums of x, after the sums of squares in red[par]).
-    // Along this wave's (slot, lane) order the segments never decrease (slot
-    // i+1 starts ndt >= 64 vectors after slot i, lanes are consecutive), and a
-    // slot's lanes span segments seg(lane 0)..seg(lane 63), usually one. Each
+    // Along this wave's (slot, vector) order the segments never decrease
+    // (slot i+1 starts ndt >= 64 vectors after slot i), and a slot's vectors
+    // span segments seg(first vector)..seg(last vector), usually one; lane 0
+    // holds the first vector and lane 63 the last. Each
     // slot is reduced over the wave once per segment it spans; runs of one
     // segment add up in a wave-uniform register and lane 0 writes every
     // finished segment (segments the wave does not touch stay 0).
@@ -572,10 +606,26 @@ fused_qknorm_kernel(FusedParams p)
             }
             u32x4 w[KO];
             pack_out(DT{}, o, w);
+            if constexpr (kPair) {
+                // s0: lanes 0-31 keep their first half, lanes 32-63 receive the
+                // second half of lane - 32; s1: lanes 0-31 receive the first
+                // half of lane + 32, lanes 32-63 keep their second half
+                u32x4 s0, s1;
 #pragma unroll
-            for (int j = 0; j < KO; ++j)
-                __builtin_amdgcn_raw_buffer_store_b128(w[j], tk[i] ? dyk : dyq,
-                                                       ooff[i] + (tk[i] ? ok : oq) + 16 * j, 0, kNT);
+                for (int d = 0; d < 4; ++d) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(w[0][d], w[1][d], false, false);
+                    s0[d] = sw[0];
+                    s1[d] = sw[1];
+                }
+                const uint32_t base = tk[i] ? ok : oq;
+                __builtin_amdgcn_raw_buffer_store_b128(s0, tk[i] ? dyk : dyq, poff[i][0] + base, 0, kNT);
+                __builtin_amdgcn_raw_buffer_store_b128(s1, tk[i] ? dyk : dyq, poff[i][1] + base, 0, kNT);
+            } else {
+#pragma unroll
+                for (int j = 0; j < KO; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(w[j], tk[i] ? dyk : dyq,
+                                                           ooff[i] + (tk[i] ? ok : oq) + 16 * j, 0, kNT);
+            }
         }
     };
 

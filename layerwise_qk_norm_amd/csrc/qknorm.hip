@@ -451,20 +451,23 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         int dtype, wq, wk, n, v, w, rows, wpc;
     };
     static const Tuned kTuned[] = {
-        {QKN_FMT_BF16, 5120, 5120, 1, 4, 4, 1, 1},
+        {QKN_FMT_BF16, 5120, 5120, 1, 3, 5, 1, 1},
         {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 2, 1},
-        {QKN_FMT_BF16, 1280, 1280, 4, 7, 10, 4, 1},
-        {QKN_FMT_BF16, 640, 640, 8, 8, 3, 3, 2},
-        {QKN_FMT_BF16, 1280, 256, 4, 8, 2, 2, 3},
-        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 1, 5, 1, 1},
-        {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 5, 2, 1},
-        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 3, 2, 2},
-        {QKN_FMT_E4M3_BF16, 640, 640, 8, 7, 3, 4, 2},
-        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 7, 3, 4, 2},
-        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 0, 10, 2, 2},
-        {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 2},
-        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 5, 1, 2},
-        {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 3, 1, 3},
+        {QKN_FMT_BF16, 1280, 1280, 4, 9, 5, 4, 1},
+        {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2},
+        {QKN_FMT_BF16, 1280, 256, 4, 9, 3, 4, 2},
+        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1},
+        {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1},
+        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1},
+        {QKN_FMT_E4M3_BF16, 640, 640, 8, 6, 4, 3, 4},
+        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 6, 6, 4, 2},
+        {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1},
+        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 1, 10, 4, 1},
+        {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 6, 10, 4, 1},
+        {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4},
+        {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1},
+        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1},
+        {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 10, 4, 1},
         {QKN_FMT_LN_BF16, 640, 640, 8, 7, 3, 2, 4},
         {QKN_FMT_LN_BF16, 1280, 256, 4, 8, 2, 2, 3},
         {QKN_FMT_LN_F32, 2560, 2560, 2, 9, 5, 1, 2},

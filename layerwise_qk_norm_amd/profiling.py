@@ -4,6 +4,9 @@
   [--kernel-trace TRACE_CSV --window KERNEL:START:COUNT]`` writes the per-kernel duration
   table of a ``--kernel-trace --stats`` run and, with a window, the average over one
   run of consecutive dispatches (the benchmark's timed steps, after its warmup).
+``python -m layerwise_qk_norm_amd.profiling sq OUT_TXT CSV... --cmd "..."`` writes the
+  instruction-issue counters (SQ_*) of the fused prefill kernel next to the copy
+  kernel's, averaged per dispatch, from one or more ``--pmc`` runs.
 ``python -m layerwise_qk_norm_amd.profiling traffic FETCH_CSV WRITE_CSV OUT_TXT --cmd-fetch
   "..." --cmd-write "..."`` writes HBM bytes per launch of the fused prefill kernel
   from two ``--pmc`` runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch). Each counter
@@ -126,6 +129,45 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_txt: str, cmd_fetch: s
     open(out_txt, "w").write("\n".join(lines) + "\n")
 
 
+def _counters(csv_path: str):
+    """{kernel: {counter: [value per dispatch]}} of one --pmc run."""
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        out.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    return out
+
+
+def summarize_sq(csvs, out_txt: str, cmds, kernel: str, title: str):
+    """Instruction-issue counters (per dispatch, averaged) of one kernel and of the
+    copy kernel of the same run, from one or more --pmc runs."""
+    fused, copy = {}, {}
+    for path in csvs:
+        per = _counters(path)
+        fname = next(n for n in per if kernel in n)
+        cname = next(n for n in per if "copy2_kernel" in n)
+        for c, v in per[fname].items():
+            fused[c] = statistics.mean(v)
+        for c, v in per[cname].items():
+            copy[c] = statistics.mean(v)
+    lines = [f"# SQ instruction counters of the {title}, averaged per dispatch"]
+    lines += [f"# command: {c}" for c in cmds]
+    lines += [f"kernel_source_sha: {kernel_source_sha()}", f"kernel: {short(fname)}",
+              f"{'counter':24s} {'fused':>16s} {'copy':>16s}"]
+    for c in sorted(fused):
+        lines.append(f"{c:24s} {fused[c]:16.0f} {copy.get(c, float('nan')):16.0f}")
+    waves = fused.get("SQ_WAVES")
+    if waves and "SQ_INSTS_VALU" in fused:
+        lines.append(f"valu_insts_per_wave: {fused['SQ_INSTS_VALU'] / waves:.0f}")
+    if "SQ_ACTIVE_INST_VALU" in fused and "SQ_WAVE_CYCLES" in fused:
+        lines.append("valu_active_over_wave_cycles: "
+                     f"{fused['SQ_ACTIVE_INST_VALU'] / fused['SQ_WAVE_CYCLES']:.3f}")
+    if "SQ_WAIT_INST_ANY" in fused and "SQ_WAVE_CYCLES" in fused:
+        lines.append("wait_inst_any_over_wave_cycles: "
+                     f"{fused['SQ_WAIT_INST_ANY'] / fused['SQ_WAVE_CYCLES']:.3f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -147,8 +189,16 @@ def main():
     f.add_argument("--kernel", default="fused_qknorm_kernel<qkn::Bf16",
                    help="substring of the kernel name to summarise")
     f.add_argument("--title", default="fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)")
+    q = sub.add_parser("sq")
+    q.add_argument("out_txt")
+    q.add_argument("csvs", nargs="+")
+    q.add_argument("--cmd", action="append", required=True)
+    q.add_argument("--kernel", default="fused_qknorm_kernel<qkn::Bf16, 4, true, 2, 512, 0>")
+    q.add_argument("--title", default="fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)")
     a = ap.parse_args()
-    if a.what == "trace":
+    if a.what == "sq":
+        summarize_sq(a.csvs, a.out_txt, a.cmd, a.kernel, a.title)
+    elif a.what == "trace":
         summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note, a.kernel_trace, a.window)
     else:
         summarize_traffic(a.fetch_csv, a.write_csv, a.out_txt, a.cmd_fetch, a.cmd_write,

@@ -294,6 +294,9 @@ enum {
     QKN_OPT_MAX_GROUPS = 6,     /* 0 = no cap, else cap on workgroup groups */
     QKN_OPT_FORCE_SPLIT = 7,    /* 1 = fused entry points run the split kernels */
     QKN_OPT_DATA_WAVES = 9,     /* 0 = planner's choice, else data waves per workgroup */
+    QKN_OPT_SPLIT_VECTORS = 10, /* 0 = library's choice, else 1, 2, 4 or 8: 16-byte vectors
+                                   each thread of the split kernels' 16-byte paths loads
+                                   at once (the apply kernels take at most 4) */
     QKN_OPT_TEST_SKIP_PUBLISH = 8 /* test hook: 1 = fused workgroups never publish
                                      their partial, so every exchange with n_shards
                                      > 1 ends at the spin limit (kernel still exits) */

@@ -207,6 +207,7 @@ struct Options {
     int64_t max_groups = 0;
     int64_t force_split = 0;
     int64_t test_skip_publish = 0;
+    int64_t split_vectors = 0;
 };
 Options g_opt;
 
@@ -539,12 +540,35 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
 
 // ---------------------------------------------------------------- split launches
 
+// 16-byte loads each lane of a split reduction issues at once: enough to cover
+// a shard row of `row_bytes` in one pass (a wave loads 1 KiB per vector), at
+// most 8; QKN_OPT_SPLIT_VECTORS overrides.
+int reduce_vectors(int64_t row_bytes)
+{
+    if (g_opt.split_vectors > 0) return (int)g_opt.split_vectors;
+    const int64_t need = (row_bytes + 1023) / 1024;
+    return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+}
+
+template <class DT, bool STATS>
+void launch_reduce_vec(int u, dim3 g, hipStream_t s, const void* x, int64_t T, int H, int N,
+                       float* sums, float* sumsq)
+{
+    switch (u) {
+    case 1: hipLaunchKernelGGL((qkn::shard_reduce_vec_kernel<DT, 1, STATS>), g, dim3(256), 0, s, x, T, H, N, sums, sumsq); break;
+    case 2: hipLaunchKernelGGL((qkn::shard_reduce_vec_kernel<DT, 2, STATS>), g, dim3(256), 0, s, x, T, H, N, sums, sumsq); break;
+    case 4: hipLaunchKernelGGL((qkn::shard_reduce_vec_kernel<DT, 4, STATS>), g, dim3(256), 0, s, x, T, H, N, sums, sumsq); break;
+    default: hipLaunchKernelGGL((qkn::shard_reduce_vec_kernel<DT, 8, STATS>), g, dim3(256), 0, s, x, T, H, N, sums, sumsq); break;
+    }
+}
+
 template <class DT>
 void launch_sumsq_as(bool vec, dim3 g, dim3 b, hipStream_t s, const void* x, int64_t T, int H, int N,
                      float* partials)
 {
-    if (vec) hipLaunchKernelGGL((qkn::shard_sumsq_kernel<DT, true>), g, b, 0, s, x, T, H, N, partials);
-    else hipLaunchKernelGGL((qkn::shard_sumsq_kernel<DT, false>), g, b, 0, s, x, T, H, N, partials);
+    if (vec) launch_reduce_vec<DT, false>(reduce_vectors((int64_t)(H / N) * sizeof(typename DT::in_t)), g,
+                                          s, x, T, H, N, nullptr, partials);
+    else hipLaunchKernelGGL((qkn::shard_sumsq_kernel<DT>), g, b, 0, s, x, T, H, N, partials);
 }
 
 // fmt: any format whose input is x's format (only the input format matters)
@@ -577,12 +601,35 @@ int launch_combine(const float* partials, int64_t T, int64_t H, int N, float eps
     return QKN_OK;
 }
 
+// 16-byte input vectors per thread of the one-pass apply kernels.
+int apply_vectors() { return g_opt.split_vectors > 0 ? (int)std::min<int64_t>(g_opt.split_vectors, 4) : 2; }
+
+// The one-pass apply kernels over T rows of `per_row` input vectors; LN
+// selects the LayerNorm form (s0 = mean, s1 = rstd), else s0 = rms_inv.
+template <class DT, bool LN>
+int launch_apply_vec(hipStream_t s, const void* x, const void* g, const void* bt, const float* s0,
+                     const float* s1, int64_t T, int64_t per_row, void* y)
+{
+    const int u = apply_vectors();
+    const int64_t nvec = T * per_row;
+    const int64_t blocks = (nvec + 256 * u - 1) / (256 * u);
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    const dim3 gr((unsigned)blocks), b(256);
+    const double inv = 1.0 / (double)per_row;
+    switch (u) {
+    case 1: hipLaunchKernelGGL((qkn::apply_vec_kernel<DT, 1, LN>), gr, b, 0, s, x, g, bt, s0, s1, nvec, (int)per_row, inv, y); break;
+    case 2: hipLaunchKernelGGL((qkn::apply_vec_kernel<DT, 2, LN>), gr, b, 0, s, x, g, bt, s0, s1, nvec, (int)per_row, inv, y); break;
+    default: hipLaunchKernelGGL((qkn::apply_vec_kernel<DT, 4, LN>), gr, b, 0, s, x, g, bt, s0, s1, nvec, (int)per_row, inv, y); break;
+    }
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
 template <class DT>
-void launch_apply_as(bool vec, dim3 gr, dim3 b, hipStream_t s, const void* x, const void* g,
+void launch_apply_as(dim3 gr, dim3 b, hipStream_t s, const void* x, const void* g,
                      const float* rinv, int64_t T, int H, int rpb, void* y)
 {
-    if (vec) hipLaunchKernelGGL((qkn::apply_scale_kernel<DT, true>), gr, b, 0, s, x, g, rinv, T, H, rpb, y);
-    else hipLaunchKernelGGL((qkn::apply_scale_kernel<DT, false>), gr, b, 0, s, x, g, rinv, T, H, rpb, y);
+    hipLaunchKernelGGL((qkn::apply_scale_kernel<DT>), gr, b, 0, s, x, g, rinv, T, H, rpb, y);
 }
 
 int launch_apply(int fmt, const void* x, const void* g, const float* rinv, int64_t T, int64_t H,
@@ -592,16 +639,25 @@ int launch_apply(int fmt, const void* x, const void* g, const float* rinv, int64
     // 16-byte paths need every row of x to be whole vectors (then gamma's and
     // y's rows are whole 16-byte words too: their elements are at least as wide)
     const bool vec = aligned16(x) && aligned16(g) && aligned16(y) && (H * f.in) % 16 == 0;
-    const int64_t per_row = vec ? H * f.in / 16 : H;
+    if (vec) {
+        const int64_t pr = H * f.in / 16;
+        switch (fmt) {
+        case QKN_FMT_BF16: return launch_apply_vec<Bf16, false>(s, x, g, nullptr, rinv, nullptr, T, pr, y);
+        case QKN_FMT_F32: return launch_apply_vec<F32, false>(s, x, g, nullptr, rinv, nullptr, T, pr, y);
+        case QKN_FMT_E4M3_BF16: return launch_apply_vec<E4m3Bf16, false>(s, x, g, nullptr, rinv, nullptr, T, pr, y);
+        default: return launch_apply_vec<E4m3E4m3, false>(s, x, g, nullptr, rinv, nullptr, T, pr, y);
+        }
+    }
+    const int64_t per_row = H;
     const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, 2048 / per_row));
     const int64_t blocks = (T + rpb - 1) / rpb;
     if (blocks > 0x7fffffff) return QKN_EINVAL;
     dim3 gr((unsigned)blocks), b(256);
     switch (fmt) {
-    case QKN_FMT_BF16: launch_apply_as<Bf16>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
-    case QKN_FMT_F32: launch_apply_as<F32>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
-    case QKN_FMT_E4M3_BF16: launch_apply_as<E4m3Bf16>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
-    default: launch_apply_as<E4m3E4m3>(vec, gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
+    case QKN_FMT_BF16: launch_apply_as<Bf16>(gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
+    case QKN_FMT_F32: launch_apply_as<F32>(gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
+    case QKN_FMT_E4M3_BF16: launch_apply_as<E4m3Bf16>(gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
+    default: launch_apply_as<E4m3E4m3>(gr, b, s, x, g, rinv, T, (int)H, rpb, y); break;
     }
     QKN_HIP(hipGetLastError());
     return QKN_OK;
@@ -611,8 +667,9 @@ template <class DT>
 void launch_stats_as(bool vec, dim3 g, dim3 b, hipStream_t s, const void* x, int64_t T, int H,
                      int N, float* sums, float* sumsq)
 {
-    if (vec) hipLaunchKernelGGL((qkn::shard_stats_kernel<DT, true>), g, b, 0, s, x, T, H, N, sums, sumsq);
-    else hipLaunchKernelGGL((qkn::shard_stats_kernel<DT, false>), g, b, 0, s, x, T, H, N, sums, sumsq);
+    if (vec) launch_reduce_vec<DT, true>(reduce_vectors((int64_t)(H / N) * sizeof(typename DT::in_t)), g, s,
+                                         x, T, H, N, sums, sumsq);
+    else hipLaunchKernelGGL((qkn::shard_stats_kernel<DT>), g, b, 0, s, x, T, H, N, sums, sumsq);
 }
 
 int launch_stats(int fmt, const void* x, int64_t T, int64_t H, int N, float* sums, float* sumsq,
@@ -641,12 +698,10 @@ int launch_combine_stats(const float* sums, const float* sumsq, int64_t T, int64
 }
 
 template <class DT>
-void launch_norm_as(bool vec, dim3 gr, dim3 b, hipStream_t s, const void* x, const void* g,
-                    const void* bt, const float* mean, const float* rstd, int64_t T, int H, int rpb,
-                    void* y)
+void launch_norm_as(dim3 gr, dim3 b, hipStream_t s, const void* x, const void* g, const void* bt,
+                    const float* mean, const float* rstd, int64_t T, int H, int rpb, void* y)
 {
-    if (vec) hipLaunchKernelGGL((qkn::apply_norm_kernel<DT, true>), gr, b, 0, s, x, g, bt, mean, rstd, T, H, rpb, y);
-    else hipLaunchKernelGGL((qkn::apply_norm_kernel<DT, false>), gr, b, 0, s, x, g, bt, mean, rstd, T, H, rpb, y);
+    hipLaunchKernelGGL((qkn::apply_norm_kernel<DT>), gr, b, 0, s, x, g, bt, mean, rstd, T, H, rpb, y);
 }
 
 int launch_apply_norm(int fmt, const void* x, const void* g, const void* bt, const float* mean,
@@ -655,13 +710,18 @@ int launch_apply_norm(int fmt, const void* x, const void* g, const void* bt, con
     const Fmt f = fmt_of(fmt);
     const bool vec = aligned16(x) && aligned16(g) && (!bt || aligned16(bt)) && aligned16(y) &&
                      (H * f.in) % 16 == 0;
-    const int64_t per_row = vec ? H * f.in / 16 : H;
+    if (vec) {
+        const int64_t pr = H * f.in / 16;
+        if (f.in == 2) return launch_apply_vec<Bf16, true>(s, x, g, bt, mean, rstd, T, pr, y);
+        return launch_apply_vec<F32, true>(s, x, g, bt, mean, rstd, T, pr, y);
+    }
+    const int64_t per_row = H;
     const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, 2048 / per_row));
     const int64_t blocks = (T + rpb - 1) / rpb;
     if (blocks > 0x7fffffff) return QKN_EINVAL;
     dim3 gr((unsigned)blocks), b(256);
-    if (f.in == 2) launch_norm_as<Bf16>(vec, gr, b, s, x, g, bt, mean, rstd, T, (int)H, rpb, y);
-    else launch_norm_as<F32>(vec, gr, b, s, x, g, bt, mean, rstd, T, (int)H, rpb, y);
+    if (f.in == 2) launch_norm_as<Bf16>(gr, b, s, x, g, bt, mean, rstd, T, (int)H, rpb, y);
+    else launch_norm_as<F32>(gr, b, s, x, g, bt, mean, rstd, T, (int)H, rpb, y);
     QKN_HIP(hipGetLastError());
     return QKN_OK;
 }
@@ -1239,6 +1299,9 @@ int qknorm_set_option(int key, int64_t value)
     case QKN_OPT_MAX_GROUPS: if (value < 0) return QKN_EINVAL; g_opt.max_groups = value; return QKN_OK;
     case QKN_OPT_FORCE_SPLIT: g_opt.force_split = value ? 1 : 0; return QKN_OK;
     case QKN_OPT_TEST_SKIP_PUBLISH: g_opt.test_skip_publish = value ? 1 : 0; return QKN_OK;
+    case QKN_OPT_SPLIT_VECTORS:
+        if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8) return QKN_EINVAL;
+        g_opt.split_vectors = value; return QKN_OK;
     default: return QKN_EINVAL;
     }
 }
@@ -1255,6 +1318,7 @@ int64_t qknorm_get_option(int key)
     case QKN_OPT_MAX_GROUPS: return g_opt.max_groups;
     case QKN_OPT_FORCE_SPLIT: return g_opt.force_split;
     case QKN_OPT_TEST_SKIP_PUBLISH: return g_opt.test_skip_publish;
+    case QKN_OPT_SPLIT_VECTORS: return g_opt.split_vectors;
     default: return INT64_MIN;
     }
 }

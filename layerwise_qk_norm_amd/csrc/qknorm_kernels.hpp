@@ -163,22 +163,15 @@ __device__ __forceinline__ void from_f32(float v, uint8_t* p)
 
 // ---------------------------------------------------------------- memory
 
-// Streaming 16-byte accesses: inputs are read once and outputs written once,
-// so both are marked nontemporal.
-__device__ __forceinline__ u32x4 ld_stream(const void* p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void st_stream(void* p, const u32x4& v)
-{
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
+// 16-byte load of a small operand that many workgroups reread (gamma, beta):
+// left to the caches.
 __device__ __forceinline__ u32x4 ld_cached(const void* p)
 {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Cache policy bits of buffer instructions on gfx950: nontemporal.
+// Cache policy bits of buffer instructions on gfx950: nontemporal. Inputs are
+// read once and outputs written once, so every streaming access carries it.
 constexpr int kNT = 2;
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
@@ -707,12 +700,12 @@ fused_qknorm_kernel(FusedParams p)
 
 // Phase A alone: partials[s*T + t] = sum of x[t][j]^2 over shard s (fp32).
 // One wave per (token, shard) item, items token-major; 4 waves per workgroup.
-template <class DT, bool VEC>
+// Element by element: the path for rows that are not whole 16-byte vectors.
+template <class DT>
 __global__ void __launch_bounds__(256)
 shard_sumsq_kernel(const void* x_, int64_t T, int32_t H, int32_t N, float* partials)
 {
     using elem_t = typename DT::in_t;
-    constexpr int EV = DT::kVec;
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= T * N) return;  // wave-uniform
@@ -721,19 +714,9 @@ shard_sumsq_kernel(const void* x_, int64_t T, int32_t H, int32_t N, float* parti
     const int W = H / N;
     const elem_t* row = static_cast<const elem_t*>(x_) + t * H + (int64_t)s * W;
     float acc = 0.f;
-    if (VEC) {
-        const int Wv = W / EV;
-        for (int v = lane; v < Wv; v += 64) {
-            float f[EV];
-            unpack(DT{}, ld_stream(row + v * EV), f);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) acc = fmaf(f[e], f[e], acc);
-        }
-    } else {
-        for (int j = lane; j < W; j += 64) {
-            const float f = to_f32(row[j]);
-            acc = fmaf(f, f, acc);
-        }
+    for (int j = lane; j < W; j += 64) {
+        const float f = to_f32(row[j]);
+        acc = fmaf(f, f, acc);
     }
     acc = wave_sum(acc);
     if (lane == 0) partials[(int64_t)s * T + t] = acc;
@@ -752,9 +735,10 @@ combine_scale_kernel(const float* partials, int64_t T, int32_t H, int32_t N, flo
     rms_inv[t] = 1.0f / sqrtf(S / (float)H + eps);
 }
 
-// Phases B (x*gamma) and C alone: out = x * gamma * rms_inv. A workgroup
-// covers `rpb` consecutive rows; its threads walk the rows' vectors linearly.
-template <class DT, bool VEC>
+// Phases B (x*gamma) and C alone: out = x * gamma * rms_inv, element by
+// element. A workgroup covers `rpb` consecutive rows; its threads walk the
+// rows' elements linearly.
+template <class DT>
 __global__ void __launch_bounds__(256)
 apply_scale_kernel(const void* x_, const void* g_, const float* rms_inv, int64_t T, int32_t H,
                    int32_t rpb, void* y_)
@@ -762,49 +746,30 @@ apply_scale_kernel(const void* x_, const void* g_, const float* rms_inv, int64_t
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     using out_t = typename DT::out_t;
-    constexpr int EV = DT::kVec;
     const in_t* x = static_cast<const in_t*>(x_);
     const gam_t* g = static_cast<const gam_t*>(g_);
     out_t* y = static_cast<out_t*>(y_);
     const int64_t r0 = (int64_t)blockIdx.x * rpb;
-    const int unit = VEC ? EV : 1;
-    const int per_row = H / unit;
-    const int total = rpb * per_row;
+    const int total = rpb * H;
     for (int v = threadIdx.x; v < total; v += 256) {
-        const int rl = v / per_row;
-        const int c = v - rl * per_row;
+        const int rl = v / H;
+        const int c = v - rl * H;
         const int64_t t = r0 + rl;
         if (t >= T) break;
-        const float r = rms_inv[t];
-        const int64_t base = t * H + (int64_t)c * unit;
-        if (VEC) {
-            float f[EV], gg[EV], o[EV];
-            unpack(DT{}, ld_stream(x + base), f);
-            u32x4 gw[DT::kGam];
-#pragma unroll
-            for (int j = 0; j < DT::kGam; ++j) gw[j] = ld_cached(g + c * EV + j * (16 / (int)sizeof(gam_t)));
-            unpack_gamma(DT{}, gw, gg);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) o[e] = (f[e] * gg[e]) * r;
-            u32x4 w[DT::kOut];
-            pack_out(DT{}, o, w);
-#pragma unroll
-            for (int j = 0; j < DT::kOut; ++j) st_stream(y + base + j * (16 / (int)sizeof(out_t)), w[j]);
-        } else {
-            const float o = (to_f32(x[base]) * to_f32(g[c])) * r;
-            from_f32(o, y + base);
-        }
+        const int64_t base = t * H + c;
+        const float o = (to_f32(x[base]) * to_f32(g[c])) * rms_inv[t];
+        from_f32(o, y + base);
     }
 }
 
 // LayerNorm statistics alone: sums[s*T + t] = sum of x[t][j] and sumsq[s*T + t]
-// = sum of x[t][j]^2 over shard s (fp32). One wave per (token, shard) item.
-template <class DT, bool VEC>
+// = sum of x[t][j]^2 over shard s (fp32). One wave per (token, shard) item,
+// element by element (rows that are not whole 16-byte vectors).
+template <class DT>
 __global__ void __launch_bounds__(256)
 shard_stats_kernel(const void* x_, int64_t T, int32_t H, int32_t N, float* sums, float* sumsq)
 {
     using elem_t = typename DT::in_t;
-    constexpr int EV = DT::kVec;
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= T * N) return;  // wave-uniform
@@ -813,25 +778,10 @@ shard_stats_kernel(const void* x_, int64_t T, int32_t H, int32_t N, float* sums,
     const int W = H / N;
     const elem_t* row = static_cast<const elem_t*>(x_) + t * H + (int64_t)s * W;
     float a1 = 0.f, a2 = 0.f;
-    if (VEC) {
-        const int Wv = W / EV;
-        for (int v = lane; v < Wv; v += 64) {
-            float f[EV];
-            unpack(DT{}, ld_stream(row + v * EV), f);
-            float sm = 0.f;
-#pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                a2 = fmaf(f[e], f[e], a2);
-                sm += f[e];
-            }
-            a1 += sm;
-        }
-    } else {
-        for (int j = lane; j < W; j += 64) {
-            const float f = to_f32(row[j]);
-            a2 = fmaf(f, f, a2);
-            a1 += f;
-        }
+    for (int j = lane; j < W; j += 64) {
+        const float f = to_f32(row[j]);
+        a2 = fmaf(f, f, a2);
+        a1 += f;
     }
     a1 = wave_sum(a1);
     a2 = wave_sum(a2);
@@ -863,8 +813,8 @@ combine_stats_kernel(const float* sums, const float* sumsq, int64_t T, int32_t H
 }
 
 // LayerNorm Phases B and C alone: out = (x*gamma)*rstd + (beta - mean*rstd*gamma),
-// beta null = 0. Layout as apply_scale_kernel.
-template <class DT, bool VEC>
+// beta null = 0, element by element. Layout as apply_scale_kernel.
+template <class DT>
 __global__ void __launch_bounds__(256)
 apply_norm_kernel(const void* x_, const void* g_, const void* b_, const float* mean,
                   const float* rstd, int64_t T, int32_t H, int32_t rpb, void* y_)
@@ -872,46 +822,144 @@ apply_norm_kernel(const void* x_, const void* g_, const void* b_, const float* m
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     using out_t = typename DT::out_t;
-    constexpr int EV = DT::kVec;
     const in_t* x = static_cast<const in_t*>(x_);
     const gam_t* g = static_cast<const gam_t*>(g_);
     const gam_t* bt = static_cast<const gam_t*>(b_);
     out_t* y = static_cast<out_t*>(y_);
     const int64_t r0 = (int64_t)blockIdx.x * rpb;
-    const int unit = VEC ? EV : 1;
-    const int per_row = H / unit;
-    const int total = rpb * per_row;
+    const int total = rpb * H;
     for (int v = threadIdx.x; v < total; v += 256) {
-        const int rl = v / per_row;
-        const int c = v - rl * per_row;
+        const int rl = v / H;
+        const int c = v - rl * H;
         const int64_t t = r0 + rl;
         if (t >= T) break;
         const float r = rstd[t];
         const float nmr = -(mean[t] * r);
-        const int64_t base = t * H + (int64_t)c * unit;
-        if (VEC) {
-            float f[EV], gg[EV], bb[EV], o[EV];
-            unpack(DT{}, ld_stream(x + base), f);
-            u32x4 gw[DT::kGam], bw[DT::kGam];
+        const int64_t base = t * H + c;
+        const float gg = to_f32(g[c]);
+        const float bb = bt ? to_f32(bt[c]) : 0.0f;
+        const float o = fmaf(to_f32(x[base]) * gg, r, fmaf(nmr, gg, bb));
+        from_f32(o, y + base);
+    }
+}
+
+// ---------------------------------------------------------------- split kernels, 16-byte paths
+
+// Phase A alone (and the LayerNorm statistics when STATS): one wave per
+// (token, shard) item, items token-major, 4 waves per workgroup. Each lane
+// issues U 16-byte loads before it uses any of them. The shard row is reached
+// through a descriptor whose size is the row's byte count, so vectors past the
+// row's end read as zero and add nothing. Requires the row to be whole vectors.
+template <class DT, int U, bool STATS>
+__global__ void __launch_bounds__(256)
+shard_reduce_vec_kernel(const void* x_, int64_t T, int32_t H, int32_t N, float* sums, float* sumsq)
+{
+    using elem_t = typename DT::in_t;
+    constexpr int EV = DT::kVec;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= T * N) return;  // wave-uniform
+    const int64_t t = item / N;
+    const int s = (int)(item - t * N);
+    const int W = H / N;
+    const int Wb = W * (int)sizeof(elem_t);
+    const elem_t* row = static_cast<const elem_t*>(x_) + t * H + (int64_t)s * W;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<elem_t*>(row), (short)0, Wb, 0x00020000);
+    float a1 = 0.f, a2 = 0.f;
+    for (int c = 0; c < Wb; c += 64 * 16 * U) {
+        u32x4 v[U];
 #pragma unroll
-            for (int j = 0; j < DT::kGam; ++j) {
-                gw[j] = ld_cached(g + c * EV + j * (16 / (int)sizeof(gam_t)));
-                bw[j] = bt ? ld_cached(bt + c * EV + j * (16 / (int)sizeof(gam_t))) : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < U; ++j)
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, c + (j * 64 + lane) * 16, 0, kNT);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float f[EV];
+            unpack(DT{}, v[j], f);
+            float sm = 0.f;
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                a2 = fmaf(f[e], f[e], a2);
+                if (STATS) sm += f[e];
             }
-            unpack_gamma(DT{}, gw, gg);
-            unpack_gamma(DT{}, bw, bb);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) o[e] = fmaf(f[e] * gg[e], r, fmaf(nmr, gg[e], bb[e]));
-            u32x4 w[DT::kOut];
-            pack_out(DT{}, o, w);
-#pragma unroll
-            for (int j = 0; j < DT::kOut; ++j) st_stream(y + base + j * (16 / (int)sizeof(out_t)), w[j]);
-        } else {
-            const float gg = to_f32(g[c]);
-            const float bb = bt ? to_f32(bt[c]) : 0.0f;
-            const float o = fmaf(to_f32(x[base]) * gg, r, fmaf(nmr, gg, bb));
-            from_f32(o, y + base);
+            if (STATS) a1 += sm;
         }
+    }
+    a2 = wave_sum(a2);
+    if (STATS) a1 = wave_sum(a1);
+    if (lane == 0) {
+        sumsq[(int64_t)s * T + t] = a2;
+        if (STATS) sums[(int64_t)s * T + t] = a1;
+    }
+}
+
+// Phases B and C alone (RMSNorm: out = (x*gamma)*s0[t]; LayerNorm when LN:
+// out = (x*gamma)*s1[t] + (beta - s0[t]*s1[t]*gamma) with s0 = mean, s1 = rstd,
+// beta null = 0). One pass with no loop: workgroup b covers the 256*U
+// consecutive input vectors from b*256*U of the row-major tensor (nvec in all),
+// thread i the vectors b*256*U + i + 256*j. Vector v lies in row v / per_row,
+// found from a double-precision product and corrected by one step. Each thread
+// issues all its loads before its first use; descriptors sized to the tensor
+// turn the vectors past its end into zero loads and dropped stores.
+template <class DT, int U, bool LN>
+__global__ void __launch_bounds__(256)
+apply_vec_kernel(const void* x_, const void* g_, const void* b_, const float* s0, const float* s1,
+                 int64_t nvec, int32_t per_row, double inv_per_row, void* y_)
+{
+    using gam_t = typename DT::gam_t;
+    constexpr int EV = DT::kVec;
+    constexpr int KO = DT::kOut;
+    constexpr int KG = DT::kGam;
+    const gam_t* g = static_cast<const gam_t*>(g_);
+    const gam_t* bt = static_cast<const gam_t*>(b_);
+    const int64_t v0 = (int64_t)blockIdx.x * 256 * U;
+    const int64_t left = nvec - v0;
+    const int nv = (int)(left < 256 * U ? left : 256 * U);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(x_) + v0 * 16), (short)0, nv * 16, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(y_) + v0 * 16 * KO, (short)0, nv * 16 * KO, 0x00020000);
+    u32x4 xv[U], gv[U][KG], bv[U][KG];
+    float r[U], m[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) xv[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (threadIdx.x + 256 * j) * 16, 0, kNT);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        // clamp so that lanes past the end still address row data (their
+        // results are dropped by the store descriptor)
+        int64_t v = v0 + threadIdx.x + 256 * j;
+        v = v < nvec ? v : nvec - 1;
+        int64_t t = (int64_t)((double)v * inv_per_row);
+        int64_t c = v - t * per_row;
+        if (c < 0) { --t; c += per_row; } else if (c >= per_row) { ++t; c -= per_row; }
+#pragma unroll
+        for (int h = 0; h < KG; ++h) {
+            gv[j][h] = ld_cached(g + c * EV + h * (16 / (int)sizeof(gam_t)));
+            if (LN) bv[j][h] = bt ? ld_cached(bt + c * EV + h * (16 / (int)sizeof(gam_t))) : u32x4{0, 0, 0, 0};
+        }
+        r[j] = LN ? s1[t] : s0[t];
+        m[j] = LN ? s0[t] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        float f[EV], gg[EV], o[EV];
+        unpack(DT{}, xv[j], f);
+        unpack_gamma(DT{}, gv[j], gg);
+        if (LN) {
+            float bb[EV];
+            unpack_gamma(DT{}, bv[j], bb);
+            const float nmr = -(m[j] * r[j]);
+#pragma unroll
+            for (int e = 0; e < EV; ++e) o[e] = fmaf(f[e] * gg[e], r[j], fmaf(nmr, gg[e], bb[e]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < EV; ++e) o[e] = (f[e] * gg[e]) * r[j];
+        }
+        u32x4 w[KO];
+        pack_out(DT{}, o, w);
+#pragma unroll
+        for (int h = 0; h < KO; ++h)
+            __builtin_amdgcn_raw_buffer_store_b128(w[h], ry, ((threadIdx.x + 256 * j) * KO + h) * 16, 0, kNT);
     }
 }
 

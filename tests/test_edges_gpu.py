@@ -6,7 +6,7 @@ import torch
 from layerwise_qk_norm_amd import inputs, ops
 from oracle import compare, oracle
 
-from _gpu import assert_parity, needs_gpu, run_fused, run_split, to_dev, to_host
+from _gpu import assert_layernorm_parity, assert_parity, needs_gpu, run_fused, run_split, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -221,3 +221,44 @@ def test_bench_helpers_compute_the_same():
     oa, ob = torch.zeros_like(a), torch.zeros_like(b)
     ops.bench_copy(a, b, oa, ob)
     assert torch.equal(oa, a) and torch.equal(ob, b)
+
+
+
+@pytest.mark.parametrize("case", [("bf16", 37, 1000, 1), ("bf16", 19, 5120, 2), ("f32", 23, 1000, 4), ("f32", 23, 1160, 2),
+                                  ("e4m3", 29, 2080, 2)])
+def test_split_vector_widths(case):
+    # The split kernels' 16-byte paths at every vector count per thread. Rows of
+    # 125 / 640 / 250 / 290 / 130 vectors do not divide a workgroup's span of vectors,
+    # so workgroups straddle rows and the last one is partial. Every width adds
+    # each lane's vectors in the same order and scales elementwise alike, so the
+    # results are bitwise equal; the library's default is also held to the oracle.
+    dtype, T, H, N = case
+    w = inputs.Workload("sv", T, H, H, N, dtype, out_dtype="bf16" if dtype == "e4m3" else "")
+    d = inputs.make_host(w)
+    base = run_split(d["q"], d["gamma_q"], N, w.eps, w.out_dtype)
+    assert_parity(d["q"], d["gamma_q"], base[2], w.eps, "split")
+    pe = oracle.shard_sumsq(d["q"], N)
+    assert np.max(np.abs(base[0] - pe) / pe) <= compare.TOL_STAT
+    for v in (1, 2, 4, 8):
+        ops.set_option("split_vectors", v)
+        got = run_split(d["q"], d["gamma_q"], N, w.eps, w.out_dtype)
+        for a, b in zip(base, got):
+            assert np.array_equal(a, b), (case, v)
+    ops.set_option("split_vectors", 0)
+    if dtype == "e4m3":
+        return
+    x, g = to_dev(d["q"]), to_dev(d["gamma_q"])
+    beta = to_dev(d["gamma_k"])  # any vector of the format serves as beta here
+    ref = None
+    for v in (0, 1, 2, 4, 8):
+        ops.set_option("split_vectors", v)
+        s1, s2 = ops.shard_stats(x, N)
+        mean, rstd = ops.combine_stats(s1, s2, H, w.eps)
+        y = ops.apply_norm(x, g, beta, mean, rstd)
+        torch.cuda.synchronize()
+        got = [to_host(t) for t in (s1, s2, mean, rstd, y)]
+        if ref is None:
+            ref = got
+            assert_layernorm_parity(d["q"], d["gamma_q"], d["gamma_k"], got[4], w.eps, "split LN")
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b), (case, v)

@@ -22,8 +22,8 @@ Besides the headline (GB/s of algorithmic bytes), the line carries:
                  prefill shape against the HBM roofline
 
 Modes: ``--pmc`` runs only the kernels whose counters are collected
-(fused prefill in bf16, in E4M3->bf16 and as LayerNorm, and the copy of known
-size), for rocprofv3 --pmc runs.
+(fused prefill in bf16, in E4M3->bf16, in E4M3->E4M3 and as LayerNorm, headwise
+prefill, and the copy of known size), for rocprofv3 --pmc runs.
 """
 import argparse
 import dataclasses
@@ -42,6 +42,8 @@ METRIC = "fused Q+K layerwise RMSNorm HBM GB/s (% of peak) at T=16384; decode µ
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_prefill_T16384_traffic.txt")
 TRAFFIC_SUMMARY_E4M3 = os.path.join(ROOT, "profiles", "fused_prefill_e4m3_T16384_traffic.txt")
 TRAFFIC_SUMMARY_LN = os.path.join(ROOT, "profiles", "fused_layernorm_prefill_T16384_traffic.txt")
+TRAFFIC_SUMMARY_E4M3_E4M3 = os.path.join(ROOT, "profiles", "fused_prefill_e4m3_to_e4m3_T16384_traffic.txt")
+TRAFFIC_SUMMARY_HW = os.path.join(ROOT, "profiles", "headwise_prefill_T16384_traffic.txt")
 
 
 def log(*a):
@@ -173,7 +175,7 @@ def bench_headwise(args, torch, stream, timed):
     out = {"prefill": {
         "workload": f"T={w.T}, Q and K width {w.Hq} ({w.Hq // w.head_dim} heads of {w.head_dim}), bf16",
         "algorithmic_bytes": nbytes, "ms": round(ms, 5),
-        "roofline": roofline(nbytes, ms, None)}}
+        "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_HW))}}
     del bufs
     torch.cuda.empty_cache()
     return out
@@ -196,7 +198,7 @@ def bench_e4m3(args, torch, stream, timed):
         if ops.check_fault() != ops.QKN_OK:
             raise RuntimeError("E4M3 prefill reported an exchange timeout")
         nbytes = w.algorithmic_bytes()
-        traffic = read_traffic(TRAFFIC_SUMMARY_E4M3) if w.out == "bf16" else None
+        traffic = read_traffic(TRAFFIC_SUMMARY_E4M3 if w.out == "bf16" else TRAFFIC_SUMMARY_E4M3_E4M3)
         out[f"prefill_to_{w.out}"] = {
             "workload": f"T={w.T}, Q and K width {w.Hq}, E4M3 in, bf16 gamma, {w.out} out, "
                         f"{w.n_shards} logical shards",
@@ -290,23 +292,29 @@ def main():
         for i in range(5):
             fused(i)
             copy(i)
-        w8 = inputs.PREFILL_E4M3
-        _, gq8, gk8, b8 = device_workload(w8, torch, sets=1)
-        for i in range(5):
-            q, k, oq, ok = b8[0]
-            ops.layerwise_fwd(q, k, gq8, gk8, w8.n_shards, w8.eps, out_q=oq, out_k=ok)
-        del b8
+        for w8 in (inputs.PREFILL_E4M3, dataclasses.replace(inputs.PREFILL_E4M3, out_dtype="e4m3")):
+            _, gq8, gk8, b8 = device_workload(w8, torch, sets=1)
+            for i in range(5):
+                q, k, oq, ok = b8[0]
+                ops.layerwise_fwd(q, k, gq8, gk8, w8.n_shards, w8.eps, out_q=oq, out_k=ok)
+            del b8
         wl = inputs.LN_PREFILL
         dl = inputs.make_host(wl)
         tl = {n: inputs.to_device(dl[n], "cuda:0", torch) for n in dl}
         for i in range(5):
             ops.layernorm_fwd(tl["q"], tl["k"], tl["gamma_q"], tl["gamma_k"], wl.n_shards, wl.eps,
                               beta_q=tl["beta_q"], beta_k=tl["beta_k"])
+        del tl
+        wh = inputs.HW_PREFILL
+        dh = inputs.make_host(wh)
+        th = {n: inputs.to_device(dh[n], "cuda:0", torch) for n in ("q", "k", "gamma_q", "gamma_k")}
+        for i in range(5):
+            ops.headwise_fwd(th["q"], th["k"], th["gamma_q"], th["gamma_k"], wh.head_dim, wh.eps)
         torch.cuda.synchronize()
         assert ops.check_fault() == ops.QKN_OK
         log("pmc mode done: 5 fused bf16 prefill launches, 5 copy launches of "
-            f"{w.T * (w.Hq + w.Hk) * w.elem_bytes} bytes read, 5 fused E4M3->bf16 prefill launches, "
-            "5 fused LayerNorm prefill launches")
+            f"{w.T * (w.Hq + w.Hk) * w.elem_bytes} bytes read, 5 fused E4M3->bf16 and 5 E4M3->E4M3 "
+            "prefill launches, 5 fused LayerNorm prefill launches, 5 headwise prefill launches")
         return
 
     for i in range(args.warmup):

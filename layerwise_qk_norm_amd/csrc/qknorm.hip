@@ -414,6 +414,11 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     const double batch = (double)T * (double)(wvq + wvk) * 16.0 * N;  // bytes read per call
     const double io = 1.0 + (double)fm.out / (double)fm.in;           // (loads + stores) / loads
     constexpr double kTarget = 32.0 * 1024;
+    // A batch whose loads are smaller than the in-flight target is latency-bound:
+    // a call takes one pass of a tile through a workgroup, so fewer vectors per
+    // thread (the tile spread over more waves) shorten it, where in streaming
+    // batches more vectors per thread help.
+    const bool latency_bound = batch / cu < kTarget;
     auto consider = [&](int v, int w, int r, int wpc) {
         const Variant& k = kVariants[v];
         const int64_t tv = tile_vectors(r);
@@ -429,12 +434,11 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         const double util = (double)tv / (double)(64 * w * k.vpt);
         double sc = std::fabs(std::log2(std::max(inflight, 1.0) / kTarget)) +
                     0.5 * std::fabs(std::log2(std::max(waves, 0.1) / 8.0)) - 0.2 * r -
-                    1.0 * util - 0.2 * std::log2((double)k.vpt);
+                    1.0 * util + (latency_bound ? 0.6 : -0.2) * std::log2((double)k.vpt);
         if (N > 1 && k.lag == 1) sc += 0.5;
-        // a batch whose loads are smaller than the in-flight target is
-        // latency-bound: every token gets its own workgroup group if the device
-        // can hold them
-        if (batch / cu < kTarget) sc += std::log2((double)(T * N) / (double)wgs);
+        // latency-bound: every token also gets its own workgroup group if the
+        // device can hold them
+        if (latency_bound) sc += std::log2((double)(T * N) / (double)wgs);
         if (best.v < 0 || sc < best.score) {
             best.v = v;
             best.w = w;

@@ -255,6 +255,19 @@ def test_plan_every_sweep_point():
         check_plan(p, w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
 
 
+def test_plan_latency_bound_batches_take_one_vector_per_thread():
+    # Batches whose loads are below 32 KB per CU run one tile pass per call, so the
+    # planner spreads a tile over as many waves as it needs at one 16-byte vector
+    # per thread (measured on MI355X: 3.7 us per single-token call against 4.8 us
+    # with four vectors per thread on one wave). Streaming batches keep wider slots.
+    for dt in ("bf16", "e4m3_bf16", "ln_bf16"):
+        for T, H, N in ((1, 4096, 4), (2, 5120, 2), (64, 4096, 4), (128, 4096, 2), (256, 2048, 2)):
+            p = plan(dt, T, H, H, N)
+            check_plan(p, dt, T, H, H, N)
+            assert p["slots"] == 1 and p["rows"] == 1, (dt, T, H, N, p)
+    assert plan("bf16", 16384, 5120, 5120, 2)["slots"] > 1
+
+
 def test_plan_refuses_grid_beyond_residency():
     one = [[1] * (ops.MAX_DATA_WAVES + 1) for _ in range(ops.NUM_VARIANTS)]
     with pytest.raises(ops.QKNormError) as e:

@@ -468,7 +468,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_E4M3_BF16, 1280, 256, 4, 6, 6, 4, 2},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1},
-        {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 6, 10, 4, 1},
+        {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3},
         {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4},
         {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1},
         {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1},

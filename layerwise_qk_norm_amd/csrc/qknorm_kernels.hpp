@@ -107,11 +107,14 @@ __device__ __forceinline__ void unpack(E4m3Bf16, const u32x4& v, float* f) { unp
 __device__ __forceinline__ void unpack(E4m3E4m3, const u32x4& v, float* f) { unpack_e4m3(v, f); }
 
 // fp32 -> E4M3: round to nearest even by the hardware converter, after
-// saturating magnitudes above 448 (infinities included) to +-448; NaN stays
-// NaN (the comparison is false for it).
+// saturating magnitudes above 448 (infinities included) to +-448. The converter
+// itself turns magnitudes of 480 and more into NaN, so the clamp is needed. It
+// uses the NaN-propagating maximum and minimum of IEEE 754-2019 (one
+// v_maximum3_f32 and one v_minimum3_f32 on gfx950, no lane mask), so NaN stays
+// NaN and -0 stays -0.
 __device__ __forceinline__ float sat_e4m3(float v)
 {
-    return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+    return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
 }
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
 {

@@ -172,7 +172,7 @@ def format_of(x_dtype, out_dtype) -> int:
 def _need(t: torch.Tensor, name: str, ndim: int, dtype=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
@@ -188,15 +188,56 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_q=None,
-                  out_k=None, out_dtype=None):
-    """Fused Q+K layerwise RMSNorm; returns ``(out_q, out_k)``.
+# The current stream's handle as an int, without building a torch Stream object
+# (about a microsecond per call less); the public API when this build lacks it.
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_GET_DEVICE = getattr(torch._C, "_cuda_getDevice", None)
 
-    q and k are bfloat16, float32 or float8_e4m3fn (E4M3). gamma has the dtype of
-    q, except bfloat16 for E4M3 inputs. Outputs have the dtype of q, except for
-    E4M3 inputs: bfloat16 by default, float8_e4m3fn when ``out_dtype`` (or the
-    given outputs) say so.
+
+def _raw_stream(index: int) -> int:
+    return _RAW_STREAM(index) if _RAW_STREAM is not None else torch.cuda.current_stream(index).cuda_stream
+
+
+def _current_device() -> int:
+    return _GET_DEVICE() if _GET_DEVICE is not None else torch.cuda.current_device()
+
+
+def _issue(fn, args, index: int, what: str):
+    """Calls a C entry point on the current stream of device ``index``, with that
+    device current (the library plans and keeps its workspace per current device)."""
+    if _current_device() == index:
+        status = fn(*args, _raw_stream(index))
+    else:
+        with torch.cuda.device(index):
+            status = fn(*args, _raw_stream(index))
+    if status != QKN_OK:
+        raise QKNormError(status, what)
+
+
+class Prepared:
+    """A validated call, issued again by calling the object: ``outs = prepared()``.
+
+    Validation (dtypes, shapes, contiguity, devices) runs once, when the object is
+    made; each call then only passes the stored pointers and the current stream to
+    the library, which still validates sizes, overlap and residency. Meant for
+    loops that reuse the same tensors (decode steps, graph-free serving loops).
+    The contents of the tensors may change between calls; their shapes and
+    storage must not (no ``resize_``, ``set_`` or reallocation), and the object
+    keeps them alive. Returns the output tensors.
     """
+
+    __slots__ = ("_fn", "_args", "_index", "_what", "_outs", "_keep")
+
+    def __init__(self, fn, args, index, what, outs, keep):
+        self._fn, self._args, self._index, self._what = fn, args, index, what
+        self._outs, self._keep = outs, keep
+
+    def __call__(self):
+        _issue(self._fn, self._args, self._index, self._what)
+        return self._outs
+
+
+def _layerwise_call(q, k, gamma_q, gamma_k, n_shards, eps, out_q, out_k, out_dtype):
     _need(q, "q", 2)
     dt = q.dtype
     dev = q.device
@@ -225,23 +266,34 @@ def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_
         args = args + (_dtype_code(out_q),)
     else:
         fn = L.qknorm_layerwise_fwd_bf16 if code == QKN_BF16 else L.qknorm_layerwise_fwd_f32
-    if dev.index == torch.cuda.current_device():
-        status = fn(*args, torch.cuda.current_stream(dev).cuda_stream)
-    else:
-        with torch.cuda.device(dev):
-            status = fn(*args, _stream(dev))
-    _check(status, "qknorm_layerwise_fwd")
-    return out_q, out_k
+    return Prepared(fn, args, dev.index, "qknorm_layerwise_fwd", (out_q, out_k),
+                    (q, k, gamma_q, gamma_k))
+
+
+def layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_q=None,
+                  out_k=None, out_dtype=None):
+    """Fused Q+K layerwise RMSNorm; returns ``(out_q, out_k)``.
+
+    q and k are bfloat16, float32 or float8_e4m3fn (E4M3). gamma has the dtype of
+    q, except bfloat16 for E4M3 inputs. Outputs have the dtype of q, except for
+    E4M3 inputs: bfloat16 by default, float8_e4m3fn when ``out_dtype`` (or the
+    given outputs) say so.
+    """
+    return _layerwise_call(q, k, gamma_q, gamma_k, n_shards, eps, out_q, out_k, out_dtype)()
+
+
+def prepare_layerwise_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-6, out_q=None,
+                          out_k=None, out_dtype=None) -> Prepared:
+    """``layerwise_fwd`` validated once: the returned object issues the call each
+    time it is called (see ``Prepared``)."""
+    return _layerwise_call(q, k, gamma_q, gamma_k, n_shards, eps, out_q, out_k, out_dtype)
 
 
 def _ptr_or_null(t):
     return None if t is None else t.data_ptr()
 
 
-def layernorm_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-5, beta_q=None,
-                  beta_k=None, out_q=None, out_k=None):
-    """Fused Q+K LayerNorm over the full vectors with two additive shard statistics;
-    returns ``(out_q, out_k)``. bfloat16 or float32; beta may be None (no shift)."""
+def _layernorm_call(q, k, gamma_q, gamma_k, n_shards, eps, beta_q, beta_k, out_q, out_k):
     _need(q, "q", 2)
     dt = q.dtype
     dev = q.device
@@ -267,17 +319,27 @@ def layernorm_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-5, beta
     if out_q.shape != q.shape or out_k.shape != k.shape:
         raise ValueError("outputs must have the shapes of q and k")
     fn = getattr(lib(), f"qknorm_layernorm_fwd_{_suffix(code)}")
-    with torch.cuda.device(dev):
-        _check(fn(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
-                  _ptr_or_null(beta_q), _ptr_or_null(beta_k), T, Hq, Hk, n_shards, eps,
-                  out_q.data_ptr(), out_k.data_ptr(), _stream(dev)), "qknorm_layernorm_fwd")
-    return out_q, out_k
+    args = (q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+            _ptr_or_null(beta_q), _ptr_or_null(beta_k), T, Hq, Hk, n_shards, eps,
+            out_q.data_ptr(), out_k.data_ptr())
+    return Prepared(fn, args, dev.index, "qknorm_layernorm_fwd", (out_q, out_k),
+                    (q, k, gamma_q, gamma_k, beta_q, beta_k))
 
 
-def headwise_fwd(q, k, gamma_q, gamma_k, head_dim: int, eps: float = 1e-6, out_q=None,
-                 out_k=None):
-    """Headwise RMSNorm of q and k (one factor per head of ``head_dim`` columns;
-    gamma_q and gamma_k are [head_dim]); returns ``(out_q, out_k)``."""
+def layernorm_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-5, beta_q=None,
+                  beta_k=None, out_q=None, out_k=None):
+    """Fused Q+K LayerNorm over the full vectors with two additive shard statistics;
+    returns ``(out_q, out_k)``. bfloat16 or float32; beta may be None (no shift)."""
+    return _layernorm_call(q, k, gamma_q, gamma_k, n_shards, eps, beta_q, beta_k, out_q, out_k)()
+
+
+def prepare_layernorm_fwd(q, k, gamma_q, gamma_k, n_shards: int, eps: float = 1e-5, beta_q=None,
+                          beta_k=None, out_q=None, out_k=None) -> Prepared:
+    """``layernorm_fwd`` validated once (see ``Prepared``)."""
+    return _layernorm_call(q, k, gamma_q, gamma_k, n_shards, eps, beta_q, beta_k, out_q, out_k)
+
+
+def _headwise_call(q, k, gamma_q, gamma_k, head_dim, eps, out_q, out_k):
     _need(q, "q", 2)
     dt = q.dtype
     dev = q.device
@@ -302,11 +364,23 @@ def headwise_fwd(q, k, gamma_q, gamma_k, head_dim: int, eps: float = 1e-6, out_q
     if out_q.shape != q.shape or out_k.shape != k.shape:
         raise ValueError("outputs must have the shapes of q and k")
     fn = getattr(lib(), f"qknorm_headwise_fwd_{_suffix(code)}")
-    with torch.cuda.device(dev):
-        _check(fn(q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), T,
-                  Hq // head_dim, Hk // head_dim, head_dim, eps, out_q.data_ptr(),
-                  out_k.data_ptr(), _stream(dev)), "qknorm_headwise_fwd")
-    return out_q, out_k
+    args = (q.data_ptr(), k.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), T,
+            Hq // head_dim, Hk // head_dim, head_dim, eps, out_q.data_ptr(), out_k.data_ptr())
+    return Prepared(fn, args, dev.index, "qknorm_headwise_fwd", (out_q, out_k),
+                    (q, k, gamma_q, gamma_k))
+
+
+def headwise_fwd(q, k, gamma_q, gamma_k, head_dim: int, eps: float = 1e-6, out_q=None,
+                 out_k=None):
+    """Headwise RMSNorm of q and k (one factor per head of ``head_dim`` columns;
+    gamma_q and gamma_k are [head_dim]); returns ``(out_q, out_k)``."""
+    return _headwise_call(q, k, gamma_q, gamma_k, head_dim, eps, out_q, out_k)()
+
+
+def prepare_headwise_fwd(q, k, gamma_q, gamma_k, head_dim: int, eps: float = 1e-6, out_q=None,
+                         out_k=None) -> Prepared:
+    """``headwise_fwd`` validated once (see ``Prepared``)."""
+    return _headwise_call(q, k, gamma_q, gamma_k, head_dim, eps, out_q, out_k)
 
 
 def shard_stats(x, n_shards: int, sums=None, sumsq=None):

@@ -262,3 +262,65 @@ def test_split_vector_widths(case):
             assert_layernorm_parity(d["q"], d["gamma_q"], d["gamma_k"], got[4], w.eps, "split LN")
         for a, b in zip(ref, got):
             assert np.array_equal(a, b), (case, v)
+
+
+def _eq(a, b):
+    return all(np.array_equal(to_host(x), to_host(y)) for x, y in zip(a, b))
+
+
+def test_prepared_calls_match_direct_calls():
+    # A prepared call validates once and then issues the same C call; its outputs
+    # must equal the direct call's bit for bit, on every call, and follow changes
+    # of the inputs' contents between calls.
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    q, k, gq, gk = (to_dev(d[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
+    ref = ops.layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps)
+    call = ops.prepare_layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps)
+    for _ in range(3):
+        assert _eq(call(), ref)
+    q.copy_(k)
+    got = call()
+    assert _eq(got, ops.layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps))
+    assert_parity(d["k"], d["gamma_q"], to_host(got[0]), w.eps, "prepared, new contents")
+    # given outputs are written in place and returned
+    oq, ok = torch.empty_like(q), torch.empty_like(k)
+    c2 = ops.prepare_layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps, out_q=oq, out_k=ok)
+    outs = c2()
+    assert outs[0] is oq and outs[1] is ok and _eq(outs, got)
+    # E4M3 inputs with E4M3 outputs
+    w8 = inputs.E4M3_CONFIGS["decode_e4m3"]
+    d8 = inputs.make_host(w8)
+    q8, k8, g8q, g8k = (to_dev(d8[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
+    e4 = torch.float8_e4m3fn
+    c8 = ops.prepare_layerwise_fwd(q8, k8, g8q, g8k, w8.n_shards, w8.eps, out_dtype=e4)
+    assert _eq(c8(), ops.layerwise_fwd(q8, k8, g8q, g8k, w8.n_shards, w8.eps, out_dtype=e4))
+    # LayerNorm with beta, and headwise
+    wl = inputs.LN_DECODE
+    dl = inputs.make_host(wl)
+    tl = {n: to_dev(dl[n]) for n in ("q", "k", "gamma_q", "gamma_k", "beta_q", "beta_k")}
+    cl = ops.prepare_layernorm_fwd(tl["q"], tl["k"], tl["gamma_q"], tl["gamma_k"], wl.n_shards,
+                                   wl.eps, beta_q=tl["beta_q"], beta_k=tl["beta_k"])
+    assert _eq(cl(), ops.layernorm_fwd(tl["q"], tl["k"], tl["gamma_q"], tl["gamma_k"], wl.n_shards,
+                                       wl.eps, beta_q=tl["beta_q"], beta_k=tl["beta_k"]))
+    wh = inputs.HW_DECODE
+    dh = inputs.make_host(wh)
+    th = {n: to_dev(dh[n]) for n in ("q", "k", "gamma_q", "gamma_k")}
+    ch = ops.prepare_headwise_fwd(th["q"], th["k"], th["gamma_q"], th["gamma_k"], wh.head_dim, wh.eps)
+    assert _eq(ch(), ops.headwise_fwd(th["q"], th["k"], th["gamma_q"], th["gamma_k"], wh.head_dim,
+                                      wh.eps))
+
+
+def test_prepared_call_validates_once_and_reports_errors():
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    q, k, gq, gk = (to_dev(d[n]) for n in ("q", "k", "gamma_q", "gamma_k"))
+    with pytest.raises(ValueError):
+        ops.prepare_layerwise_fwd(q, k[:3], gq, gk, w.n_shards)
+    with pytest.raises(TypeError):
+        ops.prepare_layerwise_fwd(q, k.float(), gq, gk, w.n_shards)
+    # the library's own checks still run on every call
+    bad = ops.prepare_layerwise_fwd(q, k, gq, gk, 3)  # 4096 is not a multiple of 3
+    with pytest.raises(ops.QKNormError) as e:
+        bad()
+    assert e.value.status == ops.QKN_EINVAL

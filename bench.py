@@ -12,6 +12,7 @@ Besides the headline (GB/s of algorithmic bytes), the line carries:
   split       -- the three-kernel split path on the same workload
   roofline    -- the fused kernel against MI355X peak HBM bandwidth
   cpu_baseline-- the fp64 oracle timed on this host's cores on a sample
+  cpu_host    -- the host CPU model and the oracle's rate on one core
 
   e4m3        -- FP8-E4M3 activations (bf16 gamma) on the prefill shape with bf16
                  and with E4M3 outputs, each against the HBM roofline, and the
@@ -259,6 +260,32 @@ def cpu_baseline(w, d, budget_s=10.0):
                       f"loops, rows split over {threads} threads), {sec:.2f} s"}
 
 
+def cpu_host(w, d, budget_s=2.5):
+    """The host the baseline ran on: CPU model, usable cores, and the oracle's rate on
+    one core (rows from the front of the prefill batch for about budget_s)."""
+    from oracle import oracle
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rows, sec = 64, 0.0
+    while True:
+        t0 = time.perf_counter()
+        for n in ("q", "k"):
+            oracle.rmsnorm(d[n][:rows], d["gamma_" + n], w.eps, threads=1)
+        sec = time.perf_counter() - t0
+        if sec >= 0.25 * budget_s or rows >= w.T:
+            break
+        rows = min(w.T, rows * 4)
+    return {"model": model, "os_cpu_count": os.cpu_count(),
+            "single_core_GBs": round(w.with_T(rows).algorithmic_bytes() / sec / 1e9, 4),
+            "single_core_sample": f"first {rows} of {w.T} tokens, Q and K, {sec:.2f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -433,6 +460,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(w, d)
+        out["cpu_host"] = cpu_host(w, d)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

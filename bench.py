@@ -21,6 +21,8 @@ Besides the headline (GB/s of algorithmic bytes), the line carries:
                  prefill shape against the HBM roofline, and the decode shape
   headwise    -- headwise QK-Norm (one factor per head of 128 columns) on the
                  prefill shape against the HBM roofline
+  gqa         -- the GQA-shaped workload (Q width 5120, K width 1024, 4 shards)
+                 against the HBM roofline
 
 Modes: ``--pmc`` runs only the kernels whose counters are collected
 (fused prefill in bf16, in E4M3->bf16, in E4M3->E4M3 and as LayerNorm, headwise
@@ -158,6 +160,33 @@ def bench_layernorm(args, torch, stream, timed):
     out["decode"] = {"workload": "T=64, Q and K width 4096, bf16, 4 logical shards",
                      "python_back_to_back_us_per_call": round(us, 2),
                      "prepared_back_to_back_us_per_call": round(us_prep, 2)}
+    return out
+
+
+def bench_gqa(args, torch, stream, timed):
+    """The GQA-shaped workload (T=8192, Q width 5120, K width 1024, 4 logical shards).
+    One call moves 201 MB, less than the 256 MB Infinity Cache, so three buffer sets
+    rotate (604 MB) and every call streams from HBM."""
+    from layerwise_qk_norm_amd import inputs, ops
+    w = inputs.GQA
+    _, gq, gk, bufs = device_workload(w, torch, sets=3)
+
+    def fused(i):
+        q, k, oq, ok = bufs[i % len(bufs)]
+        ops.layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps, out_q=oq, out_k=ok)
+
+    for i in range(args.warmup):
+        fused(i)
+    ms = timed(fused, args.steps, stream, torch)
+    if ops.check_fault() != ops.QKN_OK:
+        raise RuntimeError("GQA workload reported an exchange timeout")
+    nbytes = w.algorithmic_bytes()
+    out = {"workload": f"T={w.T}, Q width {w.Hq}, K width {w.Hk}, bf16, {w.n_shards} logical shards",
+           "algorithmic_bytes": nbytes, "ms": round(ms, 5),
+           "plan": ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards),
+           "roofline": roofline(nbytes, ms, None)}
+    del bufs
+    torch.cuda.empty_cache()
     return out
 
 
@@ -422,6 +451,8 @@ def main():
     layernorm = bench_layernorm(args, torch, stream, timed)
     log("timing headwise ...")
     headwise = bench_headwise(args, torch, stream, timed)
+    log("timing the GQA workload ...")
+    gqa = bench_gqa(args, torch, stream, timed)
 
     traffic = read_traffic()
     out = {
@@ -456,6 +487,7 @@ def main():
         "e4m3": e4m3,
         "layernorm": layernorm,
         "headwise": headwise,
+        "gqa": gqa,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

@@ -264,6 +264,14 @@ int qknorm_release_workspace(void);
  * iterations later, which decouples the shards of a group further. The e4m3
  * formats have variants 0, 1, 2, 6 and 7 (a 16-byte vector is 16 columns);
  * the LayerNorm formats have all but variant 5.
+ * A tile is `rows` tokens of Q and of K (mixed layout), or, for RMSNorm in bf16
+ * or fp32 with Hq == Hk, `rows` rows of one tensor (single-tensor layout, st =
+ * 1: the first ceil(T/rows) tiles hold Q's rows, the rest K's, so that every
+ * access of an iteration falls in one tensor; up to 8 rows). The measured
+ * launches of the prefill-sized shards use the single-tensor layout; the
+ * scoring rule plans mixed tiles unless QKN_OPT_TILE_LAYOUT asks otherwise.
+ * Here the single-tensor kernels are taken to occupy the device like the mixed
+ * ones (the real path queries both).
  * `dtype` is a format (QKN_FMT_*). */
 #define QKN_NUM_VARIANTS 10
 #define QKN_MAX_DATA_WAVES 15
@@ -272,12 +280,13 @@ typedef struct qknorm_plan {
     int threads;        /* workgroup size: 64 x (data_waves + 1) */
     int data_waves;     /* data waves per workgroup (one more wave exchanges) */
     int slots;          /* 16-byte vectors per data thread */
-    int rows;           /* tokens per tile */
-    int64_t n_tiles;    /* ceil(T / rows) */
+    int rows;           /* tokens per tile (single-tensor layout: rows of one tensor) */
+    int64_t n_tiles;    /* ceil(T / rows); twice that in the single-tensor layout */
     int n_groups;       /* workgroup groups; each group = n_shards workgroups */
     int grid;           /* n_groups * n_shards */
     int xcd_map;        /* 1: members of a group share blockIdx % 8 */
     int iters;          /* tiles per group (ceil(n_tiles / n_groups)) */
+    int st;             /* 1: single-tensor tiles; 0: mixed Q+K tiles */
 } qknorm_plan;
 int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
                       int cu_count, const int* blocks_per_cu, int aligned,
@@ -288,7 +297,8 @@ int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards
 enum {
     QKN_OPT_SPIN_LIMIT_NS = 1,  /* exchange spin budget in ns (default 1e9) */
     QKN_OPT_FORCE_VARIANT = 2,  /* -1 = planner's choice, else a variant id */
-    QKN_OPT_ROWS = 3,           /* 0 = planner's choice, else rows per tile (<= 4) */
+    QKN_OPT_ROWS = 3,           /* 0 = planner's choice, else rows per tile (<= 4; single-tensor
+                                   tiles <= 8) */
     QKN_OPT_XCD_MAP = 4,        /* -1 = auto, 0 = off, 1 = on when possible */
     QKN_OPT_COOPERATIVE = 5,    /* 1 = hipLaunchCooperativeKernel, 0 = plain */
     QKN_OPT_MAX_GROUPS = 6,     /* 0 = no cap, else cap on workgroup groups */
@@ -297,6 +307,8 @@ enum {
     QKN_OPT_SPLIT_VECTORS = 10, /* 0 = library's choice, else 1, 2, 4 or 8: 16-byte vectors
                                    each thread of the split kernels' 16-byte paths loads
                                    at once (the apply kernels take at most 4) */
+    QKN_OPT_TILE_LAYOUT = 11,   /* 0 = planner's choice, 1 = mixed Q+K tiles only,
+                                   2 = single-tensor tiles wherever allowed */
     QKN_OPT_TEST_SKIP_PUBLISH = 8 /* test hook: 1 = fused workgroups never publish
                                      their partial, so every exchange with n_shards
                                      > 1 ends at the spin limit (kernel still exits) */

@@ -163,6 +163,32 @@ FusedFn fused_fn_for(int fmt, int v)
     default: return fused_fn_ln<F32>(v);
     }
 }
+// Single-tensor tiles (RMSNorm in bf16 or fp32 with Hq == Hk): the variants with
+// 1-4 vectors per thread, with a one- or two-tile lag.
+template <class DT>
+FusedFn fused_fn_st(int v)
+{
+    switch (v) {
+    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1, 1024, 0, true>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1, 1024, 0, true>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1, 1024, 0, true>;
+    case 3: return qkn::fused_qknorm_kernel<DT, 4, true, 1, 1024, 0, true>;
+    case 6: return qkn::fused_qknorm_kernel<DT, 1, true, 2, 1024, 0, true>;
+    case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024, 0, true>;
+    case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768, 0, true>;
+    case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512, 0, true>;
+    default: return nullptr;
+    }
+}
+bool st_format(int fmt) { return fmt == QKN_FMT_BF16 || fmt == QKN_FMT_F32; }
+// kernel of a format, variant and tile layout (st: single-tensor tiles)
+FusedFn fused_fn_layout(int fmt, int v, bool st)
+{
+    if (!st) return fused_fn_for(fmt, v);
+    if (fmt == QKN_FMT_BF16) return fused_fn_st<Bf16>(v);
+    if (fmt == QKN_FMT_F32) return fused_fn_st<F32>(v);
+    return nullptr;
+}
 bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
 // data waves a workgroup of variant v may have (launch bound / 64, minus the comm wave)
@@ -175,10 +201,11 @@ int max_data_waves(int fmt, int v)
 
 // dynamic LDS of a launch: gamma (and LayerNorm's beta) in slot order, kgam
 // 16-byte words per slot each
-size_t gamma_lds_bytes(int fmt, int v, int nwd)
+size_t gamma_lds_bytes(int fmt, int v, int nwd, bool st = false)
 {
     const Fmt f = fmt_of(fmt);
-    return (size_t)kVariants[v].vpt * 64 * nwd * 16 * f.kgam * f.params;
+    // single-tensor tiles hold gamma_q's and gamma_k's images
+    return (size_t)kVariants[v].vpt * 64 * nwd * 16 * f.kgam * f.params * (st ? 2 : 1);
 }
 
 // ---------------------------------------------------------------- options
@@ -208,6 +235,7 @@ struct Options {
     int64_t force_split = 0;
     int64_t test_skip_publish = 0;
     int64_t split_vectors = 0;
+    int64_t tile_layout = 0;
 };
 Options g_opt;
 
@@ -233,6 +261,8 @@ struct DevInfo {
     int wall_khz = 0;
     bool occ_done[QKN_NUM_FORMATS] = {};
     int occ[QKN_NUM_FORMATS][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
+    // single-tensor-tile kernels of the bf16 and fp32 formats
+    int occ_st[2][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
 };
 
 std::mutex g_mu;
@@ -247,22 +277,27 @@ int device_info(int dev, int dtype, DevInfo** out)
         if (d.wall_khz <= 0) d.wall_khz = 100000;
     }
     if (!d.occ_done[dtype]) {
-        for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
-            FusedFn fn = fused_fn_for(dtype, v);
-            const bool usable = fn != nullptr;
-            if (usable) {
-                const size_t max_lds = gamma_lds_bytes(dtype, v, max_data_waves(dtype, v));
-                QKN_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            (int)max_lds));
-            }
-            for (int w = 0; w <= QKN_MAX_DATA_WAVES; ++w) {
-                int n = 0;
-                if (usable && w >= 1 && w <= max_data_waves(dtype, v)) {
-                    QKN_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &n, reinterpret_cast<const void*>(fn), 64 * (w + 1), gamma_lds_bytes(dtype, v, w)));
+        for (int layout = 0; layout < (st_format(dtype) ? 2 : 1); ++layout) {
+            const bool st = layout == 1;
+            for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
+                FusedFn fn = fused_fn_layout(dtype, v, st);
+                const bool usable = fn != nullptr;
+                if (usable) {
+                    const size_t max_lds = gamma_lds_bytes(dtype, v, max_data_waves(dtype, v), st);
+                    QKN_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                (int)max_lds));
                 }
-                d.occ[dtype][v][w] = n;
+                for (int w = 0; w <= QKN_MAX_DATA_WAVES; ++w) {
+                    int n = 0;
+                    if (usable && w >= 1 && w <= max_data_waves(dtype, v)) {
+                        QKN_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &n, reinterpret_cast<const void*>(fn), 64 * (w + 1),
+                            gamma_lds_bytes(dtype, v, w, st)));
+                    }
+                    if (st) d.occ_st[dtype][v][w] = n;
+                    else d.occ[dtype][v][w] = n;
+                }
             }
         }
         d.occ_done[dtype] = true;
@@ -368,8 +403,10 @@ int current_device(int* dev)
 
 // bpc[v * (QKN_MAX_DATA_WAVES + 1) + w]: co-resident workgroups per CU of
 // variant v with w data waves (0 = not launchable).
+// bpc: occupancy of the mixed-tile kernels; bpc_st: of the single-tensor-tile
+// kernels (same layout), or null for none.
 int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int* bpc,
-         int aligned, qknorm_plan* out)
+         const int* bpc_st, int aligned, qknorm_plan* out)
 {
     std::memset(out, 0, sizeof *out);
     out->variant = -1;
@@ -384,8 +421,15 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     const int64_t Wq = Hq / N, Wk = Hk / N;
     if (!aligned || Wq % ev || Wk % ev || g_opt.force_split) return QKN_OK;  // split kernels
     const int64_t wvq = Wq / ev, wvk = Wk / ev;
-    // vectors a tile of r rows occupies: Q's part padded to whole waves, then K's
-    auto tile_vectors = [&](int64_t r) { return ((r * wvq + 63) / 64) * 64 + r * wvk; };
+    // Tile layouts. Mixed: a tile is r tokens of Q and of K, Q's part padded to
+    // whole waves, then K's. Single-tensor (RMSNorm in bf16 or fp32 with
+    // Hq == Hk): a tile is r rows of one tensor, Q's tiles first, so there are
+    // twice as many tiles and a tile's segments are its rows.
+    const bool st_ok = st_format(dtype) && Hq == Hk && bpc_st != nullptr && g_opt.tile_layout != 1;
+    auto tile_vectors = [&](int64_t r, bool st) {
+        return st ? r * wvq : ((r * wvq + 63) / 64) * 64 + r * wvk;
+    };
+    auto tiles_of = [&](int64_t r, bool st) { return (st ? 2 : 1) * ((T + r - 1) / r); };
 
     // Candidates (variant, data waves, rows, workgroups per CU). The tile must
     // fit the data threads' slots, and 2 * rows * N comm lanes must fit one
@@ -398,6 +442,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // from the best launch of each shape).
     struct Best {
         int v = -1, w = 0, rows = 0, wpc = 0;
+        bool st = false;
         double score = 0;
         int64_t wgs = 0;
     } best;
@@ -409,8 +454,10 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         return N > 1 || k.lag == 1;
     };
     const Fmt fm = fmt_of(dtype);
-    // comm lanes: stats x 2 tensors x rows x N slots in one wave
+    // comm lanes: stats x segments x N slots in one wave (segments: 2 per token
+    // for mixed tiles, 1 per row for single-tensor tiles)
     const int rows_cap = (int)std::min<int64_t>({(int64_t)qkn::kMaxRows, 32 / (N * fm.stats), T});
+    const int rows_cap_st = (int)std::min<int64_t>({(int64_t)qkn::kMaxSeg, 64 / (N * fm.stats), T});
     const double batch = (double)T * (double)(wvq + wvk) * 16.0 * N;  // bytes read per call
     const double io = 1.0 + (double)fm.out / (double)fm.in;           // (loads + stores) / loads
     constexpr double kTarget = 32.0 * 1024;
@@ -419,13 +466,14 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // thread (the tile spread over more waves) shorten it, where in streaming
     // batches more vectors per thread help.
     const bool latency_bound = batch / cu < kTarget;
-    auto consider = [&](int v, int w, int r, int wpc) {
+    auto consider = [&](int v, int w, int r, int wpc, bool st) {
         const Variant& k = kVariants[v];
-        const int64_t tv = tile_vectors(r);
+        if (st && (!st_ok || r > rows_cap_st || !fused_fn_layout(dtype, v, true))) return;
+        const int64_t tv = tile_vectors(r, st);
         if (w < 1 || w > max_data_waves(dtype, v) || (int64_t)64 * w * k.vpt < tv) return;
-        const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
+        const int b = (st ? bpc_st : bpc)[v * (QKN_MAX_DATA_WAVES + 1) + w];
         if (b <= 0 || wpc > b || (int64_t)b * cu < N) return;
-        const int64_t tiles = (T + r - 1) / r;
+        const int64_t tiles = tiles_of(r, st);
         const int64_t groups = std::min<int64_t>(tiles, (int64_t)wpc * cu / N);
         if (groups < 1) return;
         const int64_t wgs = groups * N;
@@ -444,6 +492,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
             best.w = w;
             best.rows = r;
             best.wpc = wpc;
+            best.st = st;
             best.score = sc;
             best.wgs = wgs;
         }
@@ -451,56 +500,70 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // Launches measured fastest on MI355X for the prefill-sized Q/K shards of
     // the letter's models (width 5120 split 1, 2, 4 or 8 ways; 5120/1024 split
     // 4 ways), for bf16 and E4M3 activations and for LayerNorm, used for batches
-    // of at least 4096 tokens when nothing is forced and the device can hold them.
+    // of at least 4096 tokens when nothing is forced and the device can hold
+    // them; the first fitting entry of a shape is taken.
     struct Tuned {
-        int dtype, wq, wk, n, v, w, rows, wpc;
+        int dtype, wq, wk, n, v, w, rows, wpc, st;
     };
     static const Tuned kTuned[] = {
-        {QKN_FMT_BF16, 5120, 5120, 1, 3, 5, 1, 1},
-        {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 2, 1},
-        {QKN_FMT_BF16, 1280, 1280, 4, 9, 5, 4, 1},
-        {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2},
-        {QKN_FMT_BF16, 1280, 256, 4, 9, 3, 4, 2},
-        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1},
-        {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1},
-        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1},
-        {QKN_FMT_E4M3_BF16, 640, 640, 8, 6, 4, 3, 3},
-        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 6, 6, 4, 2},
-        {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1},
-        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1},
-        {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3},
-        {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4},
-        {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1},
-        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1},
-        {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 10, 4, 1},
-        {QKN_FMT_LN_BF16, 640, 640, 8, 7, 3, 2, 4},
-        {QKN_FMT_LN_BF16, 1280, 256, 4, 8, 2, 2, 3},
-        {QKN_FMT_LN_F32, 2560, 2560, 2, 9, 5, 1, 2},
+        // single-tensor tiles first; the mixed-tile entries after them serve when
+        // QKN_OPT_TILE_LAYOUT asks for mixed tiles
+        {QKN_FMT_BF16, 5120, 5120, 1, 9, 5, 2, 1, 1},
+        {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 4, 1, 1},
+        {QKN_FMT_BF16, 1280, 1280, 4, 7, 10, 8, 1, 1},
+        {QKN_FMT_BF16, 640, 640, 8, 9, 3, 8, 2, 1},
+        {QKN_FMT_BF16, 5120, 5120, 1, 3, 5, 1, 1, 0},
+        {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 2, 1, 0},
+        {QKN_FMT_BF16, 1280, 1280, 4, 9, 5, 4, 1, 0},
+        {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2, 0},
+        {QKN_FMT_BF16, 1280, 256, 4, 9, 3, 4, 2, 0},
+        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1, 0},
+        {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
+        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},
+        {QKN_FMT_E4M3_BF16, 640, 640, 8, 6, 4, 3, 3, 0},
+        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 6, 6, 4, 2, 0},
+        {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1, 0},
+        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1, 0},
+        {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3, 0},
+        {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4, 0},
+        {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1, 0},
+        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1, 0},
+        {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 10, 4, 1, 0},
+        {QKN_FMT_LN_BF16, 640, 640, 8, 7, 3, 2, 4, 0},
+        {QKN_FMT_LN_BF16, 1280, 256, 4, 8, 2, 2, 3, 0},
+        {QKN_FMT_LN_F32, 2560, 2560, 2, 9, 5, 1, 2, 0},
     };
-    const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0;
+    const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0 ||
+                        g_opt.tile_layout == 2;
     if (!forced && T >= 4096) {
         for (const Tuned& t : kTuned) {
-            if (t.dtype == dtype && t.wq == Wq && t.wk == Wk && t.n == N && t.rows <= rows_cap)
-                consider(t.v, t.w, t.rows, t.wpc);
+            if (t.dtype == dtype && t.wq == Wq && t.wk == Wk && t.n == N &&
+                t.rows <= (t.st ? rows_cap_st : rows_cap))
+                consider(t.v, t.w, t.rows, t.wpc, t.st != 0);
+            if (best.v >= 0) break;  // the first entry that fits the device
         }
     }
+    // the search below uses mixed tiles, or single-tensor tiles where
+    // QKN_OPT_TILE_LAYOUT asks for them and the shape allows them
+    const bool st_search = g_opt.tile_layout == 2 && st_ok;
     if (best.v < 0) {
         for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
             if (!allowed(v)) continue;
             const Variant& k = kVariants[v];
-            for (int r = 1; r <= rows_cap; ++r) {
+            if (st_search && !fused_fn_layout(dtype, v, true)) continue;
+            for (int r = 1; r <= (st_search ? rows_cap_st : rows_cap); ++r) {
                 if (g_opt.rows > 0 && r != g_opt.rows) continue;
-                const int64_t tv = tile_vectors(r);
+                const int64_t tv = tile_vectors(r, st_search);
                 int w = (int)((tv + 64 * k.vpt - 1) / (64 * k.vpt));
                 if (g_opt.force_data_waves > 0) {
                     if (g_opt.force_data_waves < w) continue;
                     w = (int)g_opt.force_data_waves;
                 }
                 if (w < 1 || w > max_data_waves(dtype, v)) continue;
-                const int b = bpc[v * (QKN_MAX_DATA_WAVES + 1) + w];
-                const int64_t tiles = (T + r - 1) / r;
+                const int b = (st_search ? bpc_st : bpc)[v * (QKN_MAX_DATA_WAVES + 1) + w];
+                const int64_t tiles = tiles_of(r, st_search);
                 for (int wpc = 1; wpc <= b; ++wpc) {
-                    consider(v, w, r, wpc);
+                    consider(v, w, r, wpc, st_search);
                     if ((int64_t)wpc * cu / N >= tiles) break;  // more would idle
                 }
             }
@@ -512,7 +575,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
             const Variant& k = kVariants[v];
             if (!variant_usable(dtype, v)) continue;
-            const int w = (int)((tile_vectors(1) + 64 * k.vpt - 1) / (64 * k.vpt));
+            const int w = (int)((tile_vectors(1, false) + 64 * k.vpt - 1) / (64 * k.vpt));
             if (w >= 1 && w <= max_data_waves(dtype, v) && bpc[v * (QKN_MAX_DATA_WAVES + 1) + w] > 0 &&
                 (int64_t)bpc[v * (QKN_MAX_DATA_WAVES + 1) + w] * cu < N)
                 return QKN_ERESIDENCY;
@@ -520,7 +583,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         return QKN_OK;
     }
     const int rows = best.rows;
-    const int64_t n_tiles = (T + rows - 1) / rows;
+    const int64_t n_tiles = tiles_of(rows, best.st);
     int64_t groups = best.wgs / N;
     if (g_opt.max_groups > 0) groups = std::min<int64_t>(groups, g_opt.max_groups);
     int xcd = 0;
@@ -539,6 +602,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     out->grid = (int)(groups * N);
     out->xcd_map = xcd;
     out->iters = (int)((n_tiles + groups - 1) / groups);
+    out->st = best.st ? 1 : 0;
     return QKN_OK;
 }
 
@@ -874,7 +938,8 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     if (hit != cache.end()) {
         pl = hit->second;
     } else {
-        if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, &di->occ[dtype][0][0], aligned, &pl))) return rc;
+        const int* occ_st = st_format(dtype) ? &di->occ_st[dtype][0][0] : nullptr;
+        if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, &di->occ[dtype][0][0], occ_st, aligned, &pl))) return rc;
         if (cache.size() > 4096) cache.clear();
         cache.emplace(key, pl);
     }
@@ -956,10 +1021,12 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     const double ticks = (double)g_opt.spin_ns * 1e-9 * (double)di->wall_khz * 1e3;
     p.spin_ticks = ticks < 1.0 ? 1 : (uint64_t)ticks;
     p.test_flags = g_opt.test_skip_publish ? 1u : 0u;
+    p.nq = pl.st ? (T + pl.rows - 1) / pl.rows : 0;
     ws->tag_base += (uint32_t)pl.iters;
 
-    FusedFn fn = fused_fn_for(dtype, pl.variant);
-    const size_t lds = gamma_lds_bytes(dtype, pl.variant, pl.data_waves);
+    FusedFn fn = fused_fn_layout(dtype, pl.variant, pl.st != 0);
+    if (!fn) return QKN_EINVAL;
+    const size_t lds = gamma_lds_bytes(dtype, pl.variant, pl.data_waves, pl.st != 0);
     if (g_opt.cooperative) {
         void* args[] = {&p};
         QKN_HIP(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(pl.grid),
@@ -1238,8 +1305,11 @@ int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_sh
     DevInfo* di = nullptr;
     if ((rc = device_info(dev, dtype, &di))) return rc;
     qknorm_plan pl;
-    if ((rc = plan(dtype, 1 << 20, Hq, Hk, n_shards, di->cu, &di->occ[dtype][0][0], 1, &pl))) return rc;
-    *out = pl.variant < 0 ? 0 : di->occ[dtype][pl.variant][pl.data_waves] * di->cu;
+    const int* occ_st = st_format(dtype) ? &di->occ_st[dtype][0][0] : nullptr;
+    if ((rc = plan(dtype, 1 << 20, Hq, Hk, n_shards, di->cu, &di->occ[dtype][0][0], occ_st, 1, &pl))) return rc;
+    *out = pl.variant < 0 ? 0
+                          : (pl.st ? di->occ_st[dtype][pl.variant][pl.data_waves]
+                                   : di->occ[dtype][pl.variant][pl.data_waves]) * di->cu;
     return QKN_OK;
 }
 
@@ -1280,7 +1350,10 @@ int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards
                       const int* blocks_per_cu, int aligned, qknorm_plan* out)
 {
     if (!out) return QKN_EINVAL;
-    return plan(dtype, T, Hq, Hk, n_shards, cu_count, blocks_per_cu, aligned, out);
+    // single-tensor-tile kernels occupy the device like the mixed-tile ones of
+    // the same variant (same registers per wave; twice the LDS, never the limit
+    // for the launches planned); the caller's table serves for both
+    return plan(dtype, T, Hq, Hk, n_shards, cu_count, blocks_per_cu, blocks_per_cu, aligned, out);
 }
 
 int qknorm_set_option(int key, int64_t value)
@@ -1293,7 +1366,7 @@ int qknorm_set_option(int key, int64_t value)
         if (value < -1 || value >= QKN_NUM_VARIANTS) return QKN_EINVAL;
         g_opt.force_variant = value; return QKN_OK;
     case QKN_OPT_ROWS:
-        if (value < 0 || value > qkn::kMaxRows) return QKN_EINVAL;
+        if (value < 0 || value > qkn::kMaxSeg) return QKN_EINVAL;
         g_opt.rows = value; return QKN_OK;
     case QKN_OPT_DATA_WAVES:
         if (value < 0 || value > QKN_MAX_DATA_WAVES) return QKN_EINVAL;
@@ -1306,6 +1379,9 @@ int qknorm_set_option(int key, int64_t value)
     case QKN_OPT_SPLIT_VECTORS:
         if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8) return QKN_EINVAL;
         g_opt.split_vectors = value; return QKN_OK;
+    case QKN_OPT_TILE_LAYOUT:
+        if (value < 0 || value > 2) return QKN_EINVAL;
+        g_opt.tile_layout = value; return QKN_OK;
     default: return QKN_EINVAL;
     }
 }
@@ -1323,6 +1399,7 @@ int64_t qknorm_get_option(int key)
     case QKN_OPT_FORCE_SPLIT: return g_opt.force_split;
     case QKN_OPT_TEST_SKIP_PUBLISH: return g_opt.test_skip_publish;
     case QKN_OPT_SPLIT_VECTORS: return g_opt.split_vectors;
+    case QKN_OPT_TILE_LAYOUT: return g_opt.tile_layout;
     default: return INT64_MIN;
     }
 }

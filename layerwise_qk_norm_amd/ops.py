@@ -29,7 +29,7 @@ MAX_DATA_WAVES = 15
 MAX_SHARDS = 32
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
        "max_groups": 6, "force_split": 7, "test_skip_publish": 8, "data_waves": 9,
-       "split_vectors": 10}
+       "split_vectors": 10, "tile_layout": 11}
 
 
 class QKNormError(RuntimeError):
@@ -46,7 +46,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("threads", ctypes.c_int),
                 ("data_waves", ctypes.c_int), ("slots", ctypes.c_int),
                 ("rows", ctypes.c_int), ("n_tiles", ctypes.c_int64), ("n_groups", ctypes.c_int),
-                ("grid", ctypes.c_int), ("xcd_map", ctypes.c_int), ("iters", ctypes.c_int)]
+                ("grid", ctypes.c_int), ("xcd_map", ctypes.c_int), ("iters", ctypes.c_int),
+                ("st", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

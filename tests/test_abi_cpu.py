@@ -211,15 +211,24 @@ def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=None):
     cap = bpc[v][w] * cu
     assert p["grid"] == p["n_groups"] * N
     assert p["grid"] <= cap, "grid must not exceed co-resident capacity"
-    assert 1 <= p["rows"] <= 4
-    assert N * 2 * p["rows"] * STATS[dtype] <= 64
-    assert p["n_tiles"] == -(-T // p["rows"])
-    assert 1 <= p["n_groups"] <= p["n_tiles"]
-    assert p["iters"] * p["n_groups"] >= p["n_tiles"] > (p["iters"] - 1) * p["n_groups"]
     ev = EV[dtype]
     wvq, wvk = Hq // N // ev, Hk // N // ev
-    # Q's part of a tile is padded to whole waves, then K's part follows
-    need = -(-p["rows"] * wvq // 64) * 64 + p["rows"] * wvk
+    if p["st"]:
+        # single-tensor tiles: RMSNorm in bf16/fp32 with Hq == Hk, rows of one tensor,
+        # Q's tiles then K's, one segment per row
+        assert dtype in ("bf16", "f32") and Hq == Hk and v not in (4, 5)
+        assert 1 <= p["rows"] <= 8
+        assert N * p["rows"] * STATS[dtype] <= 64
+        assert p["n_tiles"] == 2 * -(-T // p["rows"])
+        need = p["rows"] * wvq
+    else:
+        assert 1 <= p["rows"] <= 4
+        assert N * 2 * p["rows"] * STATS[dtype] <= 64
+        assert p["n_tiles"] == -(-T // p["rows"])
+        # Q's part of a tile is padded to whole waves, then K's part follows
+        need = -(-p["rows"] * wvq // 64) * 64 + p["rows"] * wvk
+    assert 1 <= p["n_groups"] <= p["n_tiles"]
+    assert p["iters"] * p["n_groups"] >= p["n_tiles"] > (p["iters"] - 1) * p["n_groups"]
     assert need <= w * 64 * p["slots"]  # data threads x slots
     if p["xcd_map"]:
         assert p["n_groups"] % 8 == 0
@@ -266,6 +275,40 @@ def test_plan_latency_bound_batches_take_one_vector_per_thread():
             check_plan(p, dt, T, H, H, N)
             assert p["slots"] == 1 and p["rows"] == 1, (dt, T, H, N, p)
     assert plan("bf16", 16384, 5120, 5120, 2)["slots"] > 1
+
+
+def test_plan_tile_layout_option():
+    old = ops.get_option("tile_layout")
+    try:
+        ops.set_option("tile_layout", 2)  # single-tensor tiles wherever allowed
+        for dt in ("bf16", "f32"):
+            for T, H, N in ((4097, 5120, 2), (16384, 4096, 1), (999, 5120, 4), (513, 5120, 8), (3, 1024, 2)):
+                p = plan(dt, T, H, H, N)
+                check_plan(p, dt, T, H, H, N)
+                assert p["st"] == 1, (dt, T, H, N, p)
+        # not allowed: Q and K of different widths, LayerNorm, E4M3
+        for dt, Hk in (("bf16", 1024), ("ln_bf16", 5120), ("e4m3_bf16", 5120)):
+            p = plan(dt, 4096, 5120, Hk, 4)
+            check_plan(p, dt, 4096, 5120, Hk, 4)
+            assert p["st"] == 0
+        ops.set_option("tile_layout", 1)  # mixed tiles only
+        for T in (4096, 16384):
+            p = plan("bf16", T, 5120, 5120, 2)
+            check_plan(p, "bf16", T, 5120, 5120, 2)
+            assert p["st"] == 0
+        with pytest.raises(ops.QKNormError):
+            ops.set_option("tile_layout", 3)
+    finally:
+        ops.set_option("tile_layout", old)
+
+
+def test_plan_prefill_shards_use_single_tensor_tiles():
+    # the measured launches of the bf16 prefill shards (width 5120 split 1-8 ways)
+    for N in (1, 2, 4, 8):
+        p = plan("bf16", 16384, 5120, 5120, N)
+        check_plan(p, "bf16", 16384, 5120, 5120, N)
+        assert p["st"] == 1, (N, p)
+    assert plan("bf16", 8192, 5120, 1024, 4)["st"] == 0  # GQA: widths differ
 
 
 def test_plan_refuses_grid_beyond_residency():

@@ -134,3 +134,41 @@ def test_power_of_two_scale_invariance_at_eps_zero(dtype):
     for m in (-3, 5):
         b = [to_host(t) for t in ops.layerwise_fwd(q * 2.0 ** m, k * 2.0 ** m, gq, gk, 4, 0.0)]
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.fixture
+def _layout_option():
+    old = ops.get_option("tile_layout")
+    yield
+    ops.set_option("tile_layout", old)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,H,N", [(37, 5120, 2), (1001, 4096, 1), (999, 5120, 4), (513, 5120, 8),
+                                   (4097, 1024, 2), (3, 256, 2), (16384, 5120, 2)])
+def test_single_tensor_tiles(dtype, T, H, N, _layout_option):
+    # Tiles that hold rows of one tensor (Q's tiles, then K's) compute every row
+    # exactly as mixed Q+K tiles do: on dyadic inputs (exact sums) the outputs are
+    # bitwise equal to the mixed layout's and to the split path's; on Gaussian
+    # inputs they meet the oracle's bar. Both layouts are forced explicitly.
+    q, k = dyadic(T, H, dtype, 5 * T), dyadic(T, H, dtype, 5 * T + 1)
+    gq, gk = gamma_of(H, dtype, 6), gamma_of(H, dtype, 7)
+    dq, dk, dgq, dgk = to_dev(q), to_dev(k), to_dev(gq), to_dev(gk)
+    outs = {}
+    for layout in (1, 2):
+        ops.set_option("tile_layout", layout)
+        assert ops.current_plan(dtype, T, H, H, N)["st"] == (layout == 2)
+        outs[layout] = [to_host(t) for t in ops.layerwise_fwd(dq, dk, dgq, dgk, N, 1e-6)]
+    assert np.array_equal(outs[1][0], outs[2][0]) and np.array_equal(outs[1][1], outs[2][1])
+    if T <= 1001:
+        _, _, yq = run_split(q, gq, N, 1e-6)
+        assert np.array_equal(outs[2][0], yq)
+    w = inputs.Workload("st", T, H, H, N, dtype)
+    d = inputs.make_host(w)
+    ops.set_option("tile_layout", 2)
+    oq, ok = ops.layerwise_fwd(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["gamma_q"]),
+                               to_dev(d["gamma_k"]), N, w.eps)
+    rows = slice(None) if T <= 4097 else np.r_[0:64, T // 2 - 32:T // 2 + 32, T - 64:T]
+    assert_parity(d["q"][rows], d["gamma_q"], to_host(oq)[rows], w.eps, "single-tensor tiles, q")
+    assert_parity(d["k"][rows], d["gamma_k"], to_host(ok)[rows], w.eps, "single-tensor tiles, k")
+    assert ops.check_fault() == ops.QKN_OK

@@ -163,31 +163,48 @@ FusedFn fused_fn_for(int fmt, int v)
     default: return fused_fn_ln<F32>(v);
     }
 }
-// Single-tensor tiles (RMSNorm in bf16 or fp32 with Hq == Hk): the variants with
-// 1-4 vectors per thread, with a one- or two-tile lag.
-template <class DT>
+// Single-tensor tiles (Hq == Hk): the variants with 1-4 vectors per thread
+// (E4M3: 1-3 with a one-tile lag, 1-2 with two), with the launch bounds of the
+// format's mixed-tile kernels.
+template <class DT, int NORM>
 FusedFn fused_fn_st(int v)
 {
     switch (v) {
-    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1, 1024, 0, true>;
-    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1, 1024, 0, true>;
-    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1, 1024, 0, true>;
-    case 3: return qkn::fused_qknorm_kernel<DT, 4, true, 1, 1024, 0, true>;
-    case 6: return qkn::fused_qknorm_kernel<DT, 1, true, 2, 1024, 0, true>;
-    case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024, 0, true>;
-    case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768, 0, true>;
-    case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512, 0, true>;
+    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1, 1024, NORM, true>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1, 1024, NORM, true>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1, 1024, NORM, true>;
+    case 3: return qkn::fused_qknorm_kernel<DT, 4, true, 1, 1024, NORM, true>;
+    case 6: return qkn::fused_qknorm_kernel<DT, 1, true, 2, 1024, NORM, true>;
+    case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024, NORM, true>;
+    case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768, NORM, true>;
+    case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512, NORM, true>;
     default: return nullptr;
     }
 }
-bool st_format(int fmt) { return fmt == QKN_FMT_BF16 || fmt == QKN_FMT_F32; }
+template <class DT>
+FusedFn fused_fn_st_e4m3(int v)
+{
+    switch (v) {
+    case 0: return qkn::fused_qknorm_kernel<DT, 1, true, 1, kE4m3MaxThreads[0], 0, true>;
+    case 1: return qkn::fused_qknorm_kernel<DT, 2, true, 1, kE4m3MaxThreads[1], 0, true>;
+    case 2: return qkn::fused_qknorm_kernel<DT, 3, true, 1, kE4m3MaxThreads[2], 0, true>;
+    case 6: return qkn::fused_qknorm_kernel<DT, 1, true, 2, kE4m3MaxThreads[6], 0, true>;
+    case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, kE4m3MaxThreads[7], 0, true>;
+    default: return nullptr;
+    }
+}
 // kernel of a format, variant and tile layout (st: single-tensor tiles)
 FusedFn fused_fn_layout(int fmt, int v, bool st)
 {
     if (!st) return fused_fn_for(fmt, v);
-    if (fmt == QKN_FMT_BF16) return fused_fn_st<Bf16>(v);
-    if (fmt == QKN_FMT_F32) return fused_fn_st<F32>(v);
-    return nullptr;
+    switch (fmt) {
+    case QKN_FMT_BF16: return fused_fn_st<Bf16, 0>(v);
+    case QKN_FMT_F32: return fused_fn_st<F32, 0>(v);
+    case QKN_FMT_E4M3_BF16: return fused_fn_st_e4m3<E4m3Bf16>(v);
+    case QKN_FMT_E4M3_E4M3: return fused_fn_st_e4m3<E4m3E4m3>(v);
+    case QKN_FMT_LN_BF16: return fused_fn_st<Bf16, 1>(v);
+    default: return fused_fn_st<F32, 1>(v);
+    }
 }
 bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
@@ -259,10 +276,11 @@ int hip_fail(hipError_t e, const char* what)
 struct DevInfo {
     int cu = 0;
     int wall_khz = 0;
+    int lds_cu = 0;  // LDS bytes per CU, the most one workgroup can hold
     bool occ_done[QKN_NUM_FORMATS] = {};
     int occ[QKN_NUM_FORMATS][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
-    // single-tensor-tile kernels of the bf16 and fp32 formats
-    int occ_st[2][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
+    // single-tensor-tile kernels
+    int occ_st[QKN_NUM_FORMATS][QKN_NUM_VARIANTS][QKN_MAX_DATA_WAVES + 1] = {};
 };
 
 std::mutex g_mu;
@@ -275,22 +293,33 @@ int device_info(int dev, int dtype, DevInfo** out)
         QKN_HIP(hipDeviceGetAttribute(&d.cu, hipDeviceAttributeMultiprocessorCount, dev));
         QKN_HIP(hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev));
         if (d.wall_khz <= 0) d.wall_khz = 100000;
+        QKN_HIP(hipDeviceGetAttribute(&d.lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev));
     }
     if (!d.occ_done[dtype]) {
-        for (int layout = 0; layout < (st_format(dtype) ? 2 : 1); ++layout) {
+        for (int layout = 0; layout < 2; ++layout) {
             const bool st = layout == 1;
             for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
                 FusedFn fn = fused_fn_layout(dtype, v, st);
-                const bool usable = fn != nullptr;
+                bool usable = fn != nullptr;
+                // data waves whose gamma (and beta) images fit the LDS next to the
+                // kernel's own arrays; more cannot be launched
+                int wfit = 0;
                 if (usable) {
-                    const size_t max_lds = gamma_lds_bytes(dtype, v, max_data_waves(dtype, v), st);
+                    hipFuncAttributes fa;
+                    QKN_HIP(hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(fn)));
+                    const size_t room = (size_t)d.lds_cu > fa.sharedSizeBytes ? d.lds_cu - fa.sharedSizeBytes : 0;
+                    for (int w = 1; w <= max_data_waves(dtype, v); ++w)
+                        if (gamma_lds_bytes(dtype, v, w, st) <= room) wfit = w;
+                    usable = wfit > 0;
+                }
+                if (usable) {
                     QKN_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                (int)max_lds));
+                                                (int)gamma_lds_bytes(dtype, v, wfit, st)));
                 }
                 for (int w = 0; w <= QKN_MAX_DATA_WAVES; ++w) {
                     int n = 0;
-                    if (usable && w >= 1 && w <= max_data_waves(dtype, v)) {
+                    if (usable && w >= 1 && w <= wfit) {
                         QKN_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
                             &n, reinterpret_cast<const void*>(fn), 64 * (w + 1),
                             gamma_lds_bytes(dtype, v, w, st)));
@@ -425,7 +454,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // whole waves, then K's. Single-tensor (RMSNorm in bf16 or fp32 with
     // Hq == Hk): a tile is r rows of one tensor, Q's tiles first, so there are
     // twice as many tiles and a tile's segments are its rows.
-    const bool st_ok = st_format(dtype) && Hq == Hk && bpc_st != nullptr && g_opt.tile_layout != 1;
+    const bool st_ok = Hq == Hk && bpc_st != nullptr && g_opt.tile_layout != 1;
     auto tile_vectors = [&](int64_t r, bool st) {
         return st ? r * wvq : ((r * wvq + 63) / 64) * 64 + r * wvk;
     };
@@ -506,8 +535,8 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         int dtype, wq, wk, n, v, w, rows, wpc, st;
     };
     static const Tuned kTuned[] = {
-        // single-tensor tiles first; the mixed-tile entries after them serve when
-        // QKN_OPT_TILE_LAYOUT asks for mixed tiles
+        // single-tensor tiles first where they measured faster; the mixed-tile
+        // entries after them serve when QKN_OPT_TILE_LAYOUT asks for mixed tiles
         {QKN_FMT_BF16, 5120, 5120, 1, 9, 5, 2, 1, 1},
         {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 4, 1, 1},
         {QKN_FMT_BF16, 1280, 1280, 4, 7, 10, 8, 1, 1},
@@ -517,11 +546,15 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_BF16, 1280, 1280, 4, 9, 5, 4, 1, 0},
         {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2, 0},
         {QKN_FMT_BF16, 1280, 256, 4, 9, 3, 4, 2, 0},
+        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 0, 15, 3, 1, 1},
+        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 5, 8, 2, 1},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1, 0},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 640, 640, 8, 6, 4, 3, 3, 0},
         {QKN_FMT_E4M3_BF16, 1280, 256, 4, 6, 6, 4, 2, 0},
+        {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 6, 15, 3, 1, 1},
+        {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 6, 10, 8, 1, 1},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1, 0},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3, 0},
@@ -938,8 +971,9 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     if (hit != cache.end()) {
         pl = hit->second;
     } else {
-        const int* occ_st = st_format(dtype) ? &di->occ_st[dtype][0][0] : nullptr;
-        if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, &di->occ[dtype][0][0], occ_st, aligned, &pl))) return rc;
+        if ((rc = plan(dtype, T, Hq, Hk, N, di->cu, &di->occ[dtype][0][0], &di->occ_st[dtype][0][0], aligned,
+                       &pl)))
+            return rc;
         if (cache.size() > 4096) cache.clear();
         cache.emplace(key, pl);
     }
@@ -1305,8 +1339,9 @@ int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_sh
     DevInfo* di = nullptr;
     if ((rc = device_info(dev, dtype, &di))) return rc;
     qknorm_plan pl;
-    const int* occ_st = st_format(dtype) ? &di->occ_st[dtype][0][0] : nullptr;
-    if ((rc = plan(dtype, 1 << 20, Hq, Hk, n_shards, di->cu, &di->occ[dtype][0][0], occ_st, 1, &pl))) return rc;
+    if ((rc = plan(dtype, 1 << 20, Hq, Hk, n_shards, di->cu, &di->occ[dtype][0][0], &di->occ_st[dtype][0][0], 1,
+                   &pl)))
+        return rc;
     *out = pl.variant < 0 ? 0
                           : (pl.st ? di->occ_st[dtype][pl.variant][pl.data_waves]
                                    : di->occ[dtype][pl.variant][pl.data_waves]) * di->cu;

@@ -277,7 +277,7 @@ struct FusedParams {
 // of any row; HBM streams one tensor at a time (a copy shaped like this kernel
 // moves the same bytes about 7 % faster than with Q and K mixed in each tile).
 // gamma then has two LDS images, gamma_q's and gamma_k's, in the same slot
-// order (RMSNorm only).
+// order; with LayerNorm, four (gamma_q, beta_q, gamma_k, beta_k).
 //
 // Pipeline: a group's tiles k = 0..K-1 go through one barrier per iteration.
 // In iteration k the data waves issue the loads of tile k+1, reduce tile k
@@ -293,7 +293,6 @@ template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT, int NORM = 0, boo
 __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
-    static_assert(!(ST && NORM), "single-tensor tiles are built for RMSNorm only");
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     constexpr int EV = DT::kVec;
@@ -499,27 +498,53 @@ fused_qknorm_kernel(FusedParams p)
         // unused slots take their tensor's last segment, which keeps segments
         // non-decreasing along (slot, vector) (their squares are 0)
         seg[i] = valid ? t * rows + r : t * rows + rows - 1;
-#pragma unroll
-        for (int g = 0; g < KG; ++g)
-            gam_lds[(i * ndt + dt) * KG + g] =
-                valid ? ld_cached(static_cast<const gam_t*>(p.gamma[t]) + col + g * (16 / (int)sizeof(gam_t)))
-                      : u32x4{0, 0, 0, 0};
-        if constexpr (ST) {
-            // gamma_k's image after gamma_q's VPT * ndt * KG words
+        // Images of VPT * ndt * KG words each: gamma, then (LayerNorm) beta, with
+        // a null beta staged as zeros. Single-tensor tiles stage the set of each
+        // tensor, Q's first; mixed tiles stage one set, each slot from its tensor.
+        // (Two spellings of the same staging: the streaming loop's speed depends
+        // on register assignment, which this code shifts, and each kernel keeps
+        // the spelling it was measured fastest with.)
+        if constexpr (!(ST && (NORM || EV == 16))) {
 #pragma unroll
             for (int g = 0; g < KG; ++g)
-                gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] =
-                    valid ? ld_cached(static_cast<const gam_t*>(p.gamma[1]) + col + g * (16 / (int)sizeof(gam_t)))
+                gam_lds[(i * ndt + dt) * KG + g] =
+                    valid ? ld_cached(static_cast<const gam_t*>(p.gamma[t]) + col + g * (16 / (int)sizeof(gam_t)))
                           : u32x4{0, 0, 0, 0};
-        }
-        if constexpr (NORM) {
-            // beta after gamma's VPT * ndt * KG words; a null beta stages zeros
-            const gam_t* bt = static_cast<const gam_t*>(p.beta[t]);
+            if constexpr (ST) {
+                // gamma_k's image after gamma_q's VPT * ndt * KG words
 #pragma unroll
-            for (int g = 0; g < KG; ++g)
-                gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] =
-                    (valid && bt) ? ld_cached(bt + col + g * (16 / (int)sizeof(gam_t)))
-                                  : u32x4{0, 0, 0, 0};
+                for (int g = 0; g < KG; ++g)
+                    gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] =
+                        valid ? ld_cached(static_cast<const gam_t*>(p.gamma[1]) + col + g * (16 / (int)sizeof(gam_t)))
+                              : u32x4{0, 0, 0, 0};
+            }
+            if constexpr (NORM) {
+                const gam_t* bt = static_cast<const gam_t*>(p.beta[t]);
+#pragma unroll
+                for (int g = 0; g < KG; ++g)
+                    gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] =
+                        (valid && bt) ? ld_cached(bt + col + g * (16 / (int)sizeof(gam_t)))
+                                      : u32x4{0, 0, 0, 0};
+            }
+        } else {
+#pragma unroll
+            for (int ts = 0; ts < (ST ? 2 : 1); ++ts) {
+                const int tt = ST ? ts : t;
+                const int base = ts * (NORM ? 2 : 1) * VPT * ndt;
+#pragma unroll
+                for (int g = 0; g < KG; ++g)
+                    gam_lds[(base + i * ndt + dt) * KG + g] =
+                        valid ? ld_cached(static_cast<const gam_t*>(p.gamma[tt]) + col + g * (16 / (int)sizeof(gam_t)))
+                              : u32x4{0, 0, 0, 0};
+                if constexpr (NORM) {
+                    const gam_t* bt = static_cast<const gam_t*>(p.beta[tt]);
+#pragma unroll
+                    for (int g = 0; g < KG; ++g)
+                        gam_lds[(base + VPT * ndt + i * ndt + dt) * KG + g] =
+                            (valid && bt) ? ld_cached(bt + col + g * (16 / (int)sizeof(gam_t)))
+                                          : u32x4{0, 0, 0, 0};
+                }
+            }
         }
     }
 
@@ -606,7 +631,7 @@ fused_qknorm_kernel(FusedParams p)
     };
     // ---- Phase B (compute path): u = x * gamma, independent of the exchange
     auto phase_b = [&](const u32x4 (&buf)[VPT], float (&u)[VPT][EV], int64_t tile) __attribute__((always_inline)) {
-        const int gimg = ten_of(tile) ? VPT * ndt : 0;  // gamma_k's image for K tiles
+        const int gimg = ten_of(tile) ? (NORM ? 2 : 1) * VPT * ndt : 0;  // K tiles: K's images
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             float f[EV], g[EV];
@@ -632,8 +657,9 @@ fused_qknorm_kernel(FusedParams p)
                 // y = u*rstd + (beta - mu*rstd*gamma)
                 const float nmr = -(mu_s[par][seg[i]] * r);
                 float g[EV], b[EV];
-                unpack_gamma(DT{}, &gam_lds[(i * ndt + dt) * KG], g);
-                unpack_gamma(DT{}, &gam_lds[(VPT * ndt + i * ndt + dt) * KG], b);
+                const int img = ten_of(tile) ? 2 * VPT * ndt : 0;  // K tiles: K's gamma and beta
+                unpack_gamma(DT{}, &gam_lds[(img + i * ndt + dt) * KG], g);
+                unpack_gamma(DT{}, &gam_lds[(img + VPT * ndt + i * ndt + dt) * KG], b);
 #pragma unroll
                 for (int e = 0; e < EV; ++e) o[e] = fmaf(u[i][e], r, fmaf(nmr, g[e], b[e]));
             }

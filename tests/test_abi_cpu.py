@@ -214,9 +214,9 @@ def check_plan(p, dtype, T, Hq, Hk, N, cu=CU, bpc=None):
     ev = EV[dtype]
     wvq, wvk = Hq // N // ev, Hk // N // ev
     if p["st"]:
-        # single-tensor tiles: RMSNorm in bf16/fp32 with Hq == Hk, rows of one tensor,
-        # Q's tiles then K's, one segment per row
-        assert dtype in ("bf16", "f32") and Hq == Hk and v not in (4, 5)
+        # single-tensor tiles: Hq == Hk, rows of one tensor, Q's tiles then K's,
+        # one segment per row
+        assert Hq == Hk and v not in (4, 5)
         assert 1 <= p["rows"] <= 8
         assert N * p["rows"] * STATS[dtype] <= 64
         assert p["n_tiles"] == 2 * -(-T // p["rows"])
@@ -281,15 +281,15 @@ def test_plan_tile_layout_option():
     old = ops.get_option("tile_layout")
     try:
         ops.set_option("tile_layout", 2)  # single-tensor tiles wherever allowed
-        for dt in ("bf16", "f32"):
+        for dt in FORMATS:
             for T, H, N in ((4097, 5120, 2), (16384, 4096, 1), (999, 5120, 4), (513, 5120, 8), (3, 1024, 2)):
                 p = plan(dt, T, H, H, N)
                 check_plan(p, dt, T, H, H, N)
                 assert p["st"] == 1, (dt, T, H, N, p)
-        # not allowed: Q and K of different widths, LayerNorm, E4M3
-        for dt, Hk in (("bf16", 1024), ("ln_bf16", 5120), ("e4m3_bf16", 5120)):
-            p = plan(dt, 4096, 5120, Hk, 4)
-            check_plan(p, dt, 4096, 5120, Hk, 4)
+        # not allowed: Q and K of different widths
+        for dt in FORMATS:
+            p = plan(dt, 4096, 5120, 1024, 4)
+            check_plan(p, dt, 4096, 5120, 1024, 4)
             assert p["st"] == 0
         ops.set_option("tile_layout", 1)  # mixed tiles only
         for T in (4096, 16384):

@@ -17,7 +17,7 @@ import torch
 from layerwise_qk_norm_amd import inputs, ops
 from oracle import oracle
 
-from _gpu import assert_parity, needs_gpu, run_split, to_dev, to_host
+from _gpu import assert_layernorm_parity, assert_parity, needs_gpu, run_fused, run_split, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -171,4 +171,49 @@ def test_single_tensor_tiles(dtype, T, H, N, _layout_option):
     rows = slice(None) if T <= 4097 else np.r_[0:64, T // 2 - 32:T // 2 + 32, T - 64:T]
     assert_parity(d["q"][rows], d["gamma_q"], to_host(oq)[rows], w.eps, "single-tensor tiles, q")
     assert_parity(d["k"][rows], d["gamma_k"], to_host(ok)[rows], w.eps, "single-tensor tiles, k")
+    assert ops.check_fault() == ops.QKN_OK
+
+
+@pytest.mark.parametrize("fmt", ["ln_bf16", "ln_f32", "e4m3_bf16", "e4m3_e4m3"])
+@pytest.mark.parametrize("T,H,N", [(37, 5120, 2), (999, 5120, 4), (513, 4096, 8), (1001, 2048, 1)])
+def test_single_tensor_tiles_other_formats(fmt, T, H, N, _layout_option):
+    # LayerNorm (four LDS images: gamma and beta of each tensor) and E4M3 (two-word
+    # bf16 stores) on single-tensor tiles: bitwise equal to mixed tiles on dyadic
+    # inputs (exact statistics), and held to the oracle on Gaussian inputs.
+    ln = fmt.startswith("ln")
+    rng = np.random.default_rng(T + N)
+    vq = torch.from_numpy((rng.integers(-16, 17, (T, H)) / 8.0).astype(np.float32)).cuda()
+    vk = torch.from_numpy((rng.integers(-16, 17, (T, H)) / 8.0).astype(np.float32)).cuda()
+    g = torch.from_numpy(rng.uniform(0.5, 1.5, (2, H)).astype(np.float32)).cuda()
+    if ln:
+        dt = torch.bfloat16 if fmt == "ln_bf16" else torch.float32
+        q, k, gq, gk = vq.to(dt), vk.to(dt), g[0].to(dt), g[1].to(dt)
+        bq, bk = (g[0] - 1).to(dt), (1 - g[1]).to(dt)
+        call = lambda: ops.layernorm_fwd(q, k, gq, gk, N, 1e-5, beta_q=bq, beta_k=bk)
+    else:
+        odt = torch.bfloat16 if fmt == "e4m3_bf16" else torch.float8_e4m3fn
+        q, k = vq.to(torch.float8_e4m3fn), vk.to(torch.float8_e4m3fn)
+        gq, gk = g[0].to(torch.bfloat16), g[1].to(torch.bfloat16)
+        call = lambda: ops.layerwise_fwd(q, k, gq, gk, N, 1e-6, out_dtype=odt)
+    outs = {}
+    for layout in (1, 2):
+        ops.set_option("tile_layout", layout)
+        assert ops.current_plan(fmt, T, H, H, N)["st"] == (layout == 2)
+        outs[layout] = [to_host(t) for t in call()]
+    assert np.array_equal(outs[1][0], outs[2][0]) and np.array_equal(outs[1][1], outs[2][1])
+    ops.set_option("tile_layout", 2)
+    if ln:
+        w = inputs.Workload("st", T, H, H, N, "bf16" if fmt == "ln_bf16" else "f32", norm="layer")
+        d = inputs.make_host(w)
+        t = {n: to_dev(d[n]) for n in ("q", "k", "gamma_q", "gamma_k", "beta_q", "beta_k")}
+        oq, ok = ops.layernorm_fwd(t["q"], t["k"], t["gamma_q"], t["gamma_k"], N, w.eps,
+                                   beta_q=t["beta_q"], beta_k=t["beta_k"])
+        assert_layernorm_parity(d["q"], d["gamma_q"], d["beta_q"], to_host(oq), w.eps, "st q")
+        assert_layernorm_parity(d["k"], d["gamma_k"], d["beta_k"], to_host(ok), w.eps, "st k")
+    else:
+        w = inputs.Workload("st", T, H, H, N, "e4m3", out_dtype=fmt.split("_")[1])
+        d = inputs.make_host(w)
+        oq, ok = run_fused(d, N, w.eps, w.out_dtype)
+        assert_parity(d["q"], d["gamma_q"], oq, w.eps, "st q")
+        assert_parity(d["k"], d["gamma_k"], ok, w.eps, "st k")
     assert ops.check_fault() == ops.QKN_OK

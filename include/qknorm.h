@@ -264,11 +264,11 @@ int qknorm_release_workspace(void);
  * iterations later, which decouples the shards of a group further. The e4m3
  * formats have variants 0, 1, 2, 6 and 7 (a 16-byte vector is 16 columns);
  * the LayerNorm formats have all but variant 5.
- * A tile is `rows` tokens of Q and of K (mixed layout), or, for RMSNorm in bf16
- * or fp32 with Hq == Hk, `rows` rows of one tensor (single-tensor layout, st =
- * 1: the first ceil(T/rows) tiles hold Q's rows, the rest K's, so that every
- * access of an iteration falls in one tensor; up to 8 rows). The measured
- * launches of the prefill-sized shards use the single-tensor layout; the
+ * A tile is `rows` tokens of Q and of K (mixed layout), or, with Hq == Hk,
+ * `rows` rows of one tensor (single-tensor layout, st = 1: the first
+ * ceil(T/rows) tiles hold Q's rows, the rest K's, so that every access of an
+ * iteration falls in one tensor; up to 8 rows). Measured launches of the
+ * prefill-sized shards use the single-tensor layout where it was faster; the
  * scoring rule plans mixed tiles unless QKN_OPT_TILE_LAYOUT asks otherwise.
  * Here the single-tensor kernels are taken to occupy the device like the mixed
  * ones (the real path queries both).

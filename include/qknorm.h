@@ -269,7 +269,9 @@ int qknorm_release_workspace(void);
  * ceil(T/rows) tiles hold Q's rows, the rest K's, so that every access of an
  * iteration falls in one tensor; up to 8 rows). Measured launches of the
  * prefill-sized shards use the single-tensor layout where it was faster; the
- * scoring rule plans mixed tiles unless QKN_OPT_TILE_LAYOUT asks otherwise.
+ * scoring rule plans mixed tiles, and moves streaming RMSNorm launches (bf16,
+ * fp32) of shards split 4 to 8 ways to single-tensor tiles of twice the
+ * rows, unless QKN_OPT_TILE_LAYOUT asks otherwise.
  * Here the single-tensor kernels are taken to occupy the device like the mixed
  * ones (the real path queries both).
  * `dtype` is a format (QKN_FMT_*). */

@@ -568,12 +568,16 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     };
     const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0 ||
                         g_opt.tile_layout == 2;
+    bool tuned = false;
     if (!forced && T >= 4096) {
         for (const Tuned& t : kTuned) {
             if (t.dtype == dtype && t.wq == Wq && t.wk == Wk && t.n == N &&
                 t.rows <= (t.st ? rows_cap_st : rows_cap))
                 consider(t.v, t.w, t.rows, t.wpc, t.st != 0);
-            if (best.v >= 0) break;  // the first entry that fits the device
+            if (best.v >= 0) {  // the first entry that fits the device
+                tuned = true;
+                break;
+            }
         }
     }
     // the search below uses mixed tiles, or single-tensor tiles where
@@ -601,6 +605,21 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
                 }
             }
         }
+    }
+    // Streaming RMSNorm shards split four or more ways ran faster on
+    // single-tensor tiles in a sweep of 20 such shapes (bf16 and fp32, widths
+    // 1024-16384 over N = 4 and 8, 16384 tokens): 18 faster, by up to 20 %,
+    // with the scored mixed launch moved over unchanged but for twice the rows
+    // per tile (the same bytes per tile, less Q's padding). With N = 1 or 2
+    // the two layouts were within noise of each other, so mixed tiles stay;
+    // wider splits were not measured.
+    if (best.v >= 0 && !best.st && !tuned && !forced && g_opt.tile_layout == 0 && st_ok &&
+        !latency_bound && N >= 4 && N <= 8 && (dtype == QKN_FMT_BF16 || dtype == QKN_FMT_F32) &&
+        2 * best.rows <= rows_cap_st) {
+        const Best mixed = best;
+        best.v = -1;
+        consider(mixed.v, mixed.w, 2 * mixed.rows, mixed.wpc, true);
+        if (best.v < 0) best = mixed;
     }
     if (best.v < 0) {
         // nothing fits: residency failure if some variant would fit the shape

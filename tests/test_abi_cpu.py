@@ -311,6 +311,32 @@ def test_plan_prefill_shards_use_single_tensor_tiles():
     assert plan("bf16", 8192, 5120, 1024, 4)["st"] == 0  # GQA: widths differ
 
 
+def test_plan_streaming_wide_splits_use_single_tensor_tiles():
+    # untuned streaming RMSNorm shards split 4 to 8 ways: the scored mixed
+    # launch, moved to single-tensor tiles of twice the rows
+    old = ops.get_option("tile_layout")
+    try:
+        for dt in ("bf16", "f32"):
+            for T, H, N in ((16384, 3072, 4), (16384, 8192, 8), (8192, 16384, 4), (16384, 1024, 8)):
+                ops.set_option("tile_layout", 0)
+                p = plan(dt, T, H, H, N)
+                check_plan(p, dt, T, H, H, N)
+                ops.set_option("tile_layout", 1)
+                m = plan(dt, T, H, H, N)
+                assert p["st"] == 1 and m["st"] == 0, (dt, T, H, N, p, m)
+                assert (p["variant"], p["data_waves"], p["rows"]) == (m["variant"], m["data_waves"], 2 * m["rows"])
+                assert p["n_groups"] == m["n_groups"]
+        ops.set_option("tile_layout", 0)
+        # N = 1, 2 or 16, other formats, latency-bound batches: mixed tiles
+        for dt, T, H, N in (("bf16", 16384, 3072, 2), ("f32", 16384, 8192, 1), ("bf16", 16384, 8192, 16),
+                            ("ln_bf16", 16384, 3072, 4),
+                            ("e4m3_bf16", 16384, 3072, 8), ("bf16", 64, 4096, 4)):
+            assert plan(dt, T, H, H, N)["st"] == 0, (dt, T, H, N)
+        assert plan("bf16", 16384, 8192, 2048, 4)["st"] == 0  # widths differ
+    finally:
+        ops.set_option("tile_layout", old)
+
+
 def test_plan_refuses_grid_beyond_residency():
     one = [[1] * (ops.MAX_DATA_WAVES + 1) for _ in range(ops.NUM_VARIANTS)]
     with pytest.raises(ops.QKNormError) as e:
@@ -352,7 +378,7 @@ def test_plan_forced_options_are_honoured():
 def test_plan_many_shards_uses_narrow_tiles():
     for N in (16, 32):
         p = plan("bf16", 4096, 4096, 4096, N)
-        assert p["variant"] >= 0 and N * 2 * p["rows"] <= 64
+        assert p["variant"] >= 0 and N * (1 if p["st"] else 2) * p["rows"] <= 64
         check_plan(p, "bf16", 4096, 4096, 4096, N)
     # LayerNorm exchanges two statistics: 16 shards fit one comm wave, 32 do not
     p = plan("ln_bf16", 4096, 4096, 4096, 16)

@@ -174,6 +174,38 @@ def test_single_tensor_tiles(dtype, T, H, N, _layout_option):
     assert ops.check_fault() == ops.QKN_OK
 
 
+@pytest.mark.parametrize("dtype,T,H,N", [("bf16", 4096, 3072, 8), ("f32", 4097, 2048, 4),
+                                         ("bf16", 8192, 4096, 4)])
+def test_wide_split_default_plan_uses_single_tensor_tiles(dtype, T, H, N, _layout_option):
+    # Streaming RMSNorm shards split 4-8 ways run on single-tensor tiles when
+    # nothing is forced: the scored mixed launch with twice the rows per tile.
+    # Same outputs as mixed tiles (bitwise on dyadic inputs) and the oracle's bar
+    # on Gaussian inputs, at sampled rows.
+    ops.set_option("tile_layout", 0)
+    p = ops.current_plan(dtype, T, H, H, N)
+    ops.set_option("tile_layout", 1)
+    m = ops.current_plan(dtype, T, H, H, N)
+    assert p["st"] == 1 and m["st"] == 0, (p, m)
+    assert (p["variant"], p["data_waves"], p["rows"]) == (m["variant"], m["data_waves"], 2 * m["rows"])
+    q, k = dyadic(T, H, dtype, 11 * T), dyadic(T, H, dtype, 11 * T + 1)
+    gq, gk = gamma_of(H, dtype, 12), gamma_of(H, dtype, 13)
+    dq, dk, dgq, dgk = to_dev(q), to_dev(k), to_dev(gq), to_dev(gk)
+    outs = {}
+    for layout in (0, 1):
+        ops.set_option("tile_layout", layout)
+        outs[layout] = [to_host(t) for t in ops.layerwise_fwd(dq, dk, dgq, dgk, N, 1e-6)]
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    ops.set_option("tile_layout", 0)
+    w = inputs.Workload("st_default", T, H, H, N, dtype)
+    d = inputs.make_host(w)
+    oq, ok = ops.layerwise_fwd(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["gamma_q"]),
+                               to_dev(d["gamma_k"]), N, w.eps)
+    rows = np.r_[0:64, T // 2 - 32:T // 2 + 32, T - 64:T]
+    assert_parity(d["q"][rows], d["gamma_q"], to_host(oq)[rows], w.eps, "default plan, q")
+    assert_parity(d["k"][rows], d["gamma_k"], to_host(ok)[rows], w.eps, "default plan, k")
+    assert ops.check_fault() == ops.QKN_OK
+
+
 @pytest.mark.parametrize("fmt", ["ln_bf16", "ln_f32", "e4m3_bf16", "e4m3_e4m3"])
 @pytest.mark.parametrize("T,H,N", [(37, 5120, 2), (999, 5120, 4), (513, 4096, 8), (1001, 2048, 1)])
 def test_single_tensor_tiles_other_formats(fmt, T, H, N, _layout_option):

@@ -547,14 +547,14 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2, 0},
         {QKN_FMT_BF16, 1280, 256, 4, 9, 3, 4, 2, 0},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 0, 15, 3, 1, 1},
-        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 5, 8, 2, 1},
+        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 5, 8, 1, 1},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1, 0},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 640, 640, 8, 6, 4, 3, 3, 0},
         {QKN_FMT_E4M3_BF16, 1280, 256, 4, 6, 6, 4, 2, 0},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 6, 15, 3, 1, 1},
-        {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 6, 10, 8, 1, 1},
+        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 8, 1, 1},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1, 0},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3, 0},

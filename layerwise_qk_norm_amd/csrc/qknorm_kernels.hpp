@@ -122,6 +122,19 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     r = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), r, true);       // bytes 2-3
     return (uint32_t)r;
 }
+// The same conversion for values known to lie within +-448, where saturation
+// changes nothing.
+__device__ __forceinline__ u32x4 pack_e4m3_in_range(const float* f)
+{
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i], f[4 * i + 1], 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i + 2], f[4 * i + 3], r, true);
+        v[i] = (uint32_t)r;
+    }
+    return v;
+}
 
 // gamma of one vector's columns (kGam words) -> fp32
 template <class F>
@@ -548,6 +561,10 @@ fused_qknorm_kernel(FusedParams p)
         }
     }
 
+    // E4M3 outputs: whether this wave saturates before converting (set below,
+    // once the first tile's loads are in flight)
+    bool sat = true;
+
     auto tile_of = [&](int k) __attribute__((always_inline)) -> int64_t { return group + (int64_t)k * p.n_groups; };
     // single-tensor tiles: the tile's tensor (wave-uniform) and its index within that tensor
     auto ten_of = [&](int64_t tile) __attribute__((always_inline)) -> bool { return ST && tile >= p.nq; };
@@ -664,7 +681,11 @@ fused_qknorm_kernel(FusedParams p)
                 for (int e = 0; e < EV; ++e) o[e] = fmaf(u[i][e], r, fmaf(nmr, g[e], b[e]));
             }
             u32x4 w[KO];
-            pack_out(DT{}, o, w);
+            if constexpr (sizeof(typename DT::out_t) == 1) {
+                if (sat) pack_out(DT{}, o, w); else w[0] = pack_e4m3_in_range(o);
+            } else {
+                pack_out(DT{}, o, w);
+            }
             if constexpr (kPair) {
                 // s0: lanes 0-31 keep their first half, lanes 32-63 receive the
                 // second half of lane - 32; s1: lanes 0-31 receive the first
@@ -719,6 +740,37 @@ fused_qknorm_kernel(FusedParams p)
 
     // k = 0
     load_tile(tile_of(0), cur);
+    // E4M3 outputs saturate at +-448. In every row |x_j| * r <= sqrt(H), since
+    // x_j^2 is one term of the row's sum of squares, so |y_j| <= sqrt(H) |gamma_j|
+    // up to the rounding of the fp32 sums (relative error below 2 H 2^-24). A
+    // wave whose gammas (its own staged columns) all keep that bound below 448,
+    // with margin, cannot produce a value that saturation would change, and
+    // converts without it. The test is wave-uniform. It compares bf16 magnitudes
+    // as integers (the low 15 bits order finite values, and infinities and NaN
+    // above them, so either keeps saturation on) against the limit truncated to
+    // bf16, which rounds it down.
+    if constexpr (sizeof(typename DT::out_t) == 1) {
+        static_assert(sizeof(gam_t) == 2, "E4M3 formats take bf16 gamma");
+        bool big = false;
+#pragma unroll
+        for (int ts = 0; ts < (ST ? 2 : 1); ++ts) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const float Hf = (float)p.H[ST ? ts : (tk[i] ? 1 : 0)];
+                const uint32_t lim = __float_as_uint(440.0f / (sqrtf(Hf) * (1.0f + Hf * 1.2e-7f))) >> 16;
+                uint32_t m = 0;
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    const u32x4 w = gam_lds[(ts * VPT * ndt + i * ndt + dt) * KG + g];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        m = max(m, max(w[d] & 0x7fffu, (w[d] >> 16) & 0x7fffu));
+                }
+                big |= m > lim;
+            }
+        }
+        sat = __any(big) != 0;
+    }
     wait_vmcnt<0>();
     if (PREFETCH) load_tile(tile_of(1), nxt);
     phase_a(cur, 0);

@@ -229,6 +229,48 @@ def test_nan_codes_and_saturation():
         assert_parity(x[[0]], g16, ok[[0]], 1e-6, f"saturation {out}")
 
 
+@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("T,H,N", [(64, 1024, 2), (37, 5120, 4), (300, 4096, 1), (129, 2560, 2)])
+def test_unsaturated_conversion_matches_saturating_split_path(T, H, N, layout):
+    """The fused E4M3 -> E4M3 path converts without saturation in waves whose gammas
+    keep sqrt(H)|gamma| under 448 (|x_j| * rms_inv <= sqrt(H) in every row). On a
+    dyadic grid (exact sums) its codes must equal the split path's, which always
+    saturates: rows that reach the bound (a single nonzero element, |y_j| close to
+    sqrt(H)|gamma_j|) against gammas under the skip limit, just over it, far over
+    448/sqrt(H) (those outputs saturate), NaN and infinite."""
+    rng = np.random.default_rng(H + T + N)
+    lim = 440.0 / (np.sqrt(H) * (1.0 + H * 1.2e-7))
+    xs, gs = [], []
+    for t_ in range(2):
+        v = rng.integers(-16, 17, (T, H)) / 8.0
+        for t in range(t_, T, 3):  # one row in three: one nonzero element
+            v[t] = 0.0
+            v[t, (t * 37 + 11 * t_) % H] = 2.0 if t % 2 else -2.0
+        xs.append(compare.e4m3_rne(v))
+        gv = rng.uniform(0.5, 0.98, H) * lim
+        blk = np.array_split(rng.permutation(H) if t_ else np.arange(H), 5)
+        gv[blk[1]] = 1.02 * lim
+        gv[blk[2]] = -1.2 * 448 / np.sqrt(H)
+        gv[blk[3][0]] = np.nan
+        gv[blk[4][0]] = np.inf
+        gs.append(bf16(gv))
+    old = ops.get_option("tile_layout")
+    try:
+        ops.set_option("tile_layout", layout)
+        oq, ok = run_fused({"q": xs[0], "k": xs[1], "gamma_q": gs[0], "gamma_k": gs[1]}, N, 1e-6, "e4m3")
+    finally:
+        ops.set_option("tile_layout", old)
+    for x, g, o in ((xs[0], gs[0], oq), (xs[1], gs[1], ok)):
+        _, _, ys = run_split(x, g, N, 1e-6, "e4m3")
+        assert np.array_equal(o, ys), np.argwhere(o != ys)[:8]
+    # the far-over block saturated where a row reached the bound
+    big = np.array_split(np.arange(H), 5)[2]
+    one_hot = [t for t in range(0, T, 3) if (t * 37) % H in big]
+    for t in one_hot:
+        assert oracle.decode_e4m3(oq[t, (t * 37) % H]) in (448.0, -448.0), t
+    assert ops.check_fault() == ops.QKN_OK
+
+
 def test_wrong_dtypes_are_rejected():
     q = torch.zeros((4, 64), dtype=E4, device="cuda:0")
     g = torch.ones(64, dtype=torch.bfloat16, device="cuda:0")

@@ -309,6 +309,13 @@ def test_plan_prefill_shards_use_single_tensor_tiles():
         check_plan(p, "bf16", 16384, 5120, 5120, N)
         assert p["st"] == 1, (N, p)
     assert plan("bf16", 8192, 5120, 1024, 4)["st"] == 0  # GQA: widths differ
+    # E4M3 entries, timed with rotating buffer sets (inputs beyond the Infinity Cache)
+    p = plan("e4m3_e4m3", 16384, 5120, 5120, 2)
+    assert (p["variant"], p["data_waves"], p["rows"], p["st"]) == (7, 10, 8, 1), p
+    p = plan("e4m3_e4m3", 16384, 5120, 5120, 4)
+    assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["n_groups"]) == (7, 3, 2, 0, 3 * 256 // 4), p
+    p = plan("e4m3_bf16", 16384, 5120, 5120, 4)
+    assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["n_groups"]) == (7, 5, 8, 1, 256 // 4), p
 
 
 def test_plan_streaming_wide_splits_use_single_tensor_tiles():

@@ -495,6 +495,16 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // thread (the tile spread over more waves) shorten it, where in streaming
     // batches more vectors per thread help.
     const bool latency_bound = batch / cu < kTarget;
+    // Streaming RMSNorm batches in bf16 or fp32 split one or two ways use
+    // constants refitted on the current kernels: 22 such shapes (widths
+    // 1024-16384, 4096-65536 tokens, every candidate timed with rotating
+    // buffer sets) put the rule's pick 4.5 % (at worst 18 %) from each shape's
+    // best launch with the general constants, 1.4 % (at worst 4.9 %) with a
+    // 40 KB in-flight target, 16 waves per CU and a larger bonus per row.
+    const bool refit = !latency_bound && N <= 2 && (dtype == QKN_FMT_BF16 || dtype == QKN_FMT_F32);
+    const double target = refit ? 40.0 * 1024 : kTarget;
+    const double wave_target = refit ? 16.0 : 8.0;
+    const double row_bonus = refit ? 0.4 : 0.2;
     auto consider = [&](int v, int w, int r, int wpc, bool st) {
         const Variant& k = kVariants[v];
         if (st && (!st_ok || r > rows_cap_st || !fused_fn_layout(dtype, v, true))) return;
@@ -509,8 +519,8 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         const double inflight = io * std::min((double)wgs * (double)(tv * 16), batch) / cu;
         const double waves = (double)wgs / cu * (w + 1);
         const double util = (double)tv / (double)(64 * w * k.vpt);
-        double sc = std::fabs(std::log2(std::max(inflight, 1.0) / kTarget)) +
-                    0.5 * std::fabs(std::log2(std::max(waves, 0.1) / 8.0)) - 0.2 * r -
+        double sc = std::fabs(std::log2(std::max(inflight, 1.0) / target)) +
+                    0.5 * std::fabs(std::log2(std::max(waves, 0.1) / wave_target)) - row_bonus * r -
                     1.0 * util + (latency_bound ? 0.6 : -0.2) * std::log2((double)k.vpt);
         if (N > 1 && k.lag == 1) sc += 0.5;
         // latency-bound: every token also gets its own workgroup group if the

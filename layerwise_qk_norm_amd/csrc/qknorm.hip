@@ -495,13 +495,17 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // thread (the tile spread over more waves) shorten it, where in streaming
     // batches more vectors per thread help.
     const bool latency_bound = batch / cu < kTarget;
-    // Streaming RMSNorm batches in bf16 or fp32 split one or two ways use
-    // constants refitted on the current kernels: 22 such shapes (widths
-    // 1024-16384, 4096-65536 tokens, every candidate timed with rotating
-    // buffer sets) put the rule's pick 4.5 % (at worst 18 %) from each shape's
-    // best launch with the general constants, 1.4 % (at worst 4.9 %) with a
-    // 40 KB in-flight target, 16 waves per CU and a larger bonus per row.
-    const bool refit = !latency_bound && N <= 2 && (dtype == QKN_FMT_BF16 || dtype == QKN_FMT_F32);
+    // Streaming batches split one or two ways in bf16 or fp32 (RMSNorm and
+    // LayerNorm) use constants refitted on the current kernels. For RMSNorm,
+    // 22 such shapes (widths 1024-16384, 4096-65536 tokens, every candidate
+    // timed with rotating buffer sets) put the rule's pick 4.5 % (at worst
+    // 18 %) from each shape's best launch with the general constants, 1.4 %
+    // (at worst 4.9 %) with a 40 KB in-flight target, 16 waves per CU and a
+    // larger bonus per row. On shapes outside the fit they were faster for
+    // RMSNorm (2.2 % in geomean) and for LayerNorm (up to 14 %).
+    const bool refit = !latency_bound && N <= 2 &&
+                       (dtype == QKN_FMT_BF16 || dtype == QKN_FMT_F32 || dtype == QKN_FMT_LN_BF16 ||
+                        dtype == QKN_FMT_LN_F32);
     const double target = refit ? 40.0 * 1024 : kTarget;
     const double wave_target = refit ? 16.0 : 8.0;
     const double row_bonus = refit ? 0.4 : 0.2;

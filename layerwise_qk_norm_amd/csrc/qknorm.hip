@@ -461,14 +461,15 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     auto tiles_of = [&](int64_t r, bool st) { return (st ? 2 : 1) * ((T + r - 1) / r); };
 
     // Candidates (variant, data waves, rows, workgroups per CU). The tile must
-    // fit the data threads' slots, and 2 * rows * N comm lanes must fit one
-    // wave. Each candidate is scored by how far it lies, on a log scale, from
-    // about 32 KB of tile loads plus stores in flight per CU and about 8 waves
-    // per CU, with preferences for more rows per tile, fuller slots and more
-    // vectors per thread, and against a one-tile lag when there are peers to
-    // wait for. The rule and its constants were fitted to the timings of every
-    // candidate launch of 29 shapes of all four formats on MI355X (mean 4.6 %
-    // from the best launch of each shape).
+    // fit the data threads' slots, and segments x statistics x N comm lanes
+    // must fit one wave. Each candidate is scored by how far it lies, on a log
+    // scale, from about 32 KB of tile loads plus stores in flight per CU and
+    // about 8 waves per CU, with preferences for more rows per tile, fuller
+    // slots and more vectors per thread, and against a one-tile lag when there
+    // are peers to wait for. These general constants were fitted to the
+    // timings of every candidate launch of 29 shapes of all four formats on
+    // MI355X (mean 4.6 % from the best launch of each shape); streaming
+    // batches split one or two ways use the refitted constants below.
     struct Best {
         int v = -1, w = 0, rows = 0, wpc = 0;
         bool st = false;

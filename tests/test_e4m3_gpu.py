@@ -230,7 +230,8 @@ def test_nan_codes_and_saturation():
 
 
 @pytest.mark.parametrize("layout", [1, 2])
-@pytest.mark.parametrize("T,H,N", [(64, 1024, 2), (37, 5120, 4), (300, 4096, 1), (129, 2560, 2)])
+@pytest.mark.parametrize("T,H,N", [(64, 1024, 2), (37, 5120, 4), (300, 4096, 1), (129, 2560, 2),
+                                   (1, 4096, 8), (4097, 2048, 8)])
 def test_unsaturated_conversion_matches_saturating_split_path(T, H, N, layout):
     """The fused E4M3 -> E4M3 path converts without saturation in waves whose gammas
     keep sqrt(H)|gamma| under 448 (|x_j| * rms_inv <= sqrt(H) in every row). On a

@@ -311,6 +311,8 @@ enum {
                                    at once (the apply kernels take at most 4) */
     QKN_OPT_TILE_LAYOUT = 11,   /* 0 = planner's choice, 1 = mixed Q+K tiles only,
                                    2 = single-tensor tiles wherever allowed */
+    QKN_OPT_WPC = 12,           /* 0 = planner's choice, else workgroups per CU the
+                                   planner's search must use (launch timing) */
     QKN_OPT_TEST_SKIP_PUBLISH = 8 /* test hook: 1 = fused workgroups never publish
                                      their partial, so every exchange with n_shards
                                      > 1 ends at the spin limit (kernel still exits) */

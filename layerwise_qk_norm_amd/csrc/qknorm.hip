@@ -253,6 +253,7 @@ struct Options {
     int64_t test_skip_publish = 0;
     int64_t split_vectors = 0;
     int64_t tile_layout = 0;
+    int64_t wpc = 0;
 };
 Options g_opt;
 
@@ -541,9 +542,10 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
             best.wgs = wgs;
         }
     };
-    // Launches measured fastest on MI355X for the prefill-sized Q/K shards of
-    // the letter's models (width 5120 split 1, 2, 4 or 8 ways; 5120/1024 split
-    // 4 ways), for bf16 and E4M3 activations and for LayerNorm, used for batches
+    // Launches measured fastest on MI355X (every candidate timed with rotating
+    // buffer sets) for the prefill-sized Q/K shards of the letter's models
+    // (width 5120 split 1, 2, 4 or 8 ways; 5120/1024 split 4 ways), for bf16
+    // and E4M3 activations and for LayerNorm, used for batches
     // of at least 4096 tokens when nothing is forced and the device can hold
     // them; the first fitting entry of a shape is taken.
     struct Tuned {
@@ -567,21 +569,22 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 640, 640, 8, 6, 4, 3, 3, 0},
-        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 6, 6, 4, 2, 0},
+        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 7, 3, 4, 3, 0},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 6, 15, 3, 1, 1},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 8, 1, 1},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1, 0},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3, 0},
         {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4, 0},
+        {QKN_FMT_E4M3_E4M3, 1280, 256, 4, 7, 3, 4, 3, 0},
         {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1, 0},
         {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1, 0},
         {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 10, 4, 1, 0},
         {QKN_FMT_LN_BF16, 640, 640, 8, 7, 3, 2, 4, 0},
-        {QKN_FMT_LN_BF16, 1280, 256, 4, 8, 2, 2, 3, 0},
+        {QKN_FMT_LN_BF16, 1280, 256, 4, 6, 12, 4, 2, 0},
         {QKN_FMT_LN_F32, 2560, 2560, 2, 9, 5, 1, 2, 0},
     };
-    const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0 ||
+    const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0 || g_opt.wpc > 0 ||
                         g_opt.tile_layout == 2;
     bool tuned = false;
     if (!forced && T >= 4096) {
@@ -615,6 +618,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
                 const int b = (st_search ? bpc_st : bpc)[v * (QKN_MAX_DATA_WAVES + 1) + w];
                 const int64_t tiles = tiles_of(r, st_search);
                 for (int wpc = 1; wpc <= b; ++wpc) {
+                    if (g_opt.wpc > 0 && wpc != g_opt.wpc) continue;
                     consider(v, w, r, wpc, st_search);
                     if ((int64_t)wpc * cu / N >= tiles) break;  // more would idle
                 }
@@ -1451,6 +1455,9 @@ int qknorm_set_option(int key, int64_t value)
     case QKN_OPT_TILE_LAYOUT:
         if (value < 0 || value > 2) return QKN_EINVAL;
         g_opt.tile_layout = value; return QKN_OK;
+    case QKN_OPT_WPC:
+        if (value < 0 || value > 64) return QKN_EINVAL;
+        g_opt.wpc = value; return QKN_OK;
     default: return QKN_EINVAL;
     }
 }
@@ -1469,6 +1476,7 @@ int64_t qknorm_get_option(int key)
     case QKN_OPT_TEST_SKIP_PUBLISH: return g_opt.test_skip_publish;
     case QKN_OPT_SPLIT_VECTORS: return g_opt.split_vectors;
     case QKN_OPT_TILE_LAYOUT: return g_opt.tile_layout;
+    case QKN_OPT_WPC: return g_opt.wpc;
     default: return INT64_MIN;
     }
 }

@@ -29,7 +29,7 @@ MAX_DATA_WAVES = 15
 MAX_SHARDS = 32
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
        "max_groups": 6, "force_split": 7, "test_skip_publish": 8, "data_waves": 9,
-       "split_vectors": 10, "tile_layout": 11}
+       "split_vectors": 10, "tile_layout": 11, "wpc": 12}
 
 
 class QKNormError(RuntimeError):

@@ -382,6 +382,25 @@ def test_plan_forced_options_are_honoured():
             ops.set_option(n, v)
 
 
+def test_plan_forced_workgroups_per_cu():
+    # QKN_OPT_WPC fixes the workgroups per CU of the planner's search (launch timing)
+    old = {n: ops.get_option(n) for n in ("force_variant", "rows", "wpc")}
+    try:
+        ops.set_option("force_variant", 9)
+        ops.set_option("rows", 4)
+        for wpc in (1, 2):
+            ops.set_option("wpc", wpc)
+            p = plan("bf16", 8192, 5120, 1024, 4)
+            check_plan(p, "bf16", 8192, 5120, 1024, 4)
+            assert (p["variant"], p["rows"]) == (9, 4)
+            assert p["n_groups"] == min(p["n_tiles"], wpc * CU // 4), p
+        with pytest.raises(ops.QKNormError):
+            ops.set_option("wpc", -1)
+    finally:
+        for n, v in old.items():
+            ops.set_option(n, v)
+
+
 def test_plan_many_shards_uses_narrow_tiles():
     for N in (16, 32):
         p = plan("bf16", 4096, 4096, 4096, N)

@@ -316,6 +316,12 @@ def test_plan_prefill_shards_use_single_tensor_tiles():
     assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["n_groups"]) == (7, 3, 2, 0, 3 * 256 // 4), p
     p = plan("e4m3_bf16", 16384, 5120, 5120, 4)
     assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["n_groups"]) == (7, 5, 8, 1, 256 // 4), p
+    # GQA entries (5120/1024 over 4 shards), retimed with exact workgroups per CU
+    for fmt in ("e4m3_bf16", "e4m3_e4m3"):
+        p = plan(fmt, 8192, 5120, 1024, 4)
+        assert (p["variant"], p["data_waves"], p["rows"], p["n_groups"]) == (7, 3, 4, 3 * 256 // 4), (fmt, p)
+    p = plan("ln_bf16", 8192, 5120, 1024, 4)
+    assert (p["variant"], p["data_waves"], p["rows"], p["n_groups"]) == (6, 12, 4, 2 * 256 // 4), p
 
 
 def test_plan_streaming_wide_splits_use_single_tensor_tiles():

@@ -101,6 +101,17 @@ def test_fused_full_size_all_rows(name):
     print(name, "q", rq, "k", rk)
 
 
+def test_gqa_e4m3_outputs_full_size():
+    """The GQA workload at full size (8192 tokens, the measured launch for its
+    shards) with E4M3 outputs, every row against the oracle."""
+    w = inputs.E4M3_CONFIGS["gqa_e4m3"]
+    d = inputs.make_host(w)
+    oq, ok = run_fused(d, w.n_shards, w.eps, "e4m3")
+    assert_parity(d["q"], d["gamma_q"], oq, w.eps, "gqa q -> e4m3")
+    assert_parity(d["k"], d["gamma_k"], ok, w.eps, "gqa k -> e4m3")
+    assert ops.check_fault() == ops.QKN_OK
+
+
 @pytest.mark.parametrize("out", ["bf16", "e4m3"])
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_split_reduced(name, out):

@@ -601,7 +601,12 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // the search below uses mixed tiles, or single-tensor tiles where
     // QKN_OPT_TILE_LAYOUT asks for them and the shape allows them
     const bool st_search = g_opt.tile_layout == 2 && st_ok;
-    if (best.v < 0) {
+    // E4M3 -> E4M3 over narrow shards (at most 160 vectors of Q and K per
+    // token): every best launch timed (widths 2048-5120 over 2-8 shards, GQA)
+    // ran three or four workgroups per CU, so the search starts there and
+    // widens only if nothing fits.
+    const bool narrow_e4 = dtype == QKN_FMT_E4M3_E4M3 && !forced && !latency_bound && N >= 2 && wvq + wvk <= 160;
+    for (int pass = narrow_e4 ? 0 : 1; pass < 2 && best.v < 0; ++pass) {
         for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
             if (!allowed(v)) continue;
             const Variant& k = kVariants[v];
@@ -619,6 +624,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
                 const int64_t tiles = tiles_of(r, st_search);
                 for (int wpc = 1; wpc <= b; ++wpc) {
                     if (g_opt.wpc > 0 && wpc != g_opt.wpc) continue;
+                    if (pass == 0 && wpc < 3) continue;
                     consider(v, w, r, wpc, st_search);
                     if ((int64_t)wpc * cu / N >= tiles) break;  // more would idle
                 }

@@ -407,6 +407,18 @@ def test_plan_forced_workgroups_per_cu():
             ops.set_option(n, v)
 
 
+def test_plan_narrow_e4m3_shards_use_several_workgroups_per_cu():
+    # E4M3 -> E4M3 over shards of at most 160 vectors of Q and K per token: the
+    # scored search starts at three workgroups per CU
+    for T, H, N in ((16384, 2048, 2), (16384, 4096, 4), (16384, 2560, 2), (8192, 6144, 8)):
+        p = plan("e4m3_e4m3", T, H, H, N)
+        check_plan(p, "e4m3_e4m3", T, H, H, N)
+        assert p["grid"] >= 3 * CU, (T, H, N, p)
+    # latency-bound calls keep one token per tile
+    p = plan("e4m3_e4m3", 64, 2048, 2048, 2)
+    assert p["rows"] == 1 and p["slots"] == 1, p
+
+
 def test_plan_many_shards_uses_narrow_tiles():
     for N in (16, 32):
         p = plan("bf16", 4096, 4096, 4096, N)

@@ -50,11 +50,18 @@ def layernorm_scaled_error(got, y, x, mean, rstd, gamma, beta, eps):
     g = np.abs(np.asarray(gamma, np.float64))[None, :]
     b = np.zeros_like(g) if beta is None else np.abs(np.asarray(beta, np.float64))[None, :]
     e = float(np.float32(eps))
-    sigma = np.sqrt(np.maximum(1.0 / (rstd * rstd) - e, 0.0))
-    scale = rstd[:, None] * g * (np.abs(xv) + np.abs(mean)[:, None] + sigma[:, None]) + b
-    err = np.abs(got - y) / scale
-    err[np.isnan(got) & np.isnan(y)] = 0.0
-    err[np.isnan(got) != np.isnan(y)] = np.inf
+    rstd = np.asarray(rstd, np.float64)
+    mean = np.asarray(mean, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        sigma = np.sqrt(np.maximum(1.0 / (rstd * rstd) - e, 0.0))
+        scale = rstd[:, None] * g * (np.abs(xv) + np.abs(mean)[:, None] + sigma[:, None]) + b
+    d = abs_diff(got, y)
+    # identical values (non-finite ones included) are exact whatever the scale;
+    # any other difference over a zero or non-finite scale is an infinite error
+    ok = np.isfinite(scale) & (scale > 0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(ok, d / np.where(ok, scale, 1.0), np.inf)
+    err[d == 0] = 0.0
     return err
 
 
@@ -94,24 +101,54 @@ def e4m3_accepts(codes: np.ndarray, y: np.ndarray, rel: float = E4M3_REL) -> np.
     return ok
 
 
-def rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+def abs_diff(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """|got - ref| elementwise, where two identical non-finite values (both NaN, or
+    the same infinity) differ by 0 and any other pair with a non-finite member
+    differs by infinity."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        e = np.abs(got - ref) / np.abs(ref)
-    zero = ref == 0
-    e[zero] = np.where(got[zero] == 0, 0.0, np.inf)
-    e[np.isnan(got) & ~np.isnan(ref)] = np.inf
-    both_nan = np.isnan(got) & np.isnan(ref)
-    e[both_nan] = 0.0
+    got, ref = np.broadcast_arrays(got, ref)
+    with np.errstate(invalid="ignore", over="ignore"):
+        d = np.abs(got - ref)
+    d = np.where(np.isfinite(got) & np.isfinite(ref), d, np.inf)
+    d[np.isnan(got) & np.isnan(ref)] = 0.0
+    d[np.isinf(ref) & (got == ref)] = 0.0
+    return d
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Elementwise |got - ref| / |ref| against the exact value ref.
+
+    An exact zero in ref accepts only a (signed) zero. A non-finite ref accepts
+    only the same value: NaN for NaN, the same infinity for an infinity. Every
+    other disagreement (a NaN or an infinity against a finite ref, a finite value
+    against a non-finite ref) is an infinite error, so no mismatch is ever NaN."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    got, ref = np.broadcast_arrays(got, ref)
+    d = abs_diff(got, ref)
+    e = np.full(ref.shape, np.inf)
+    fin = np.isfinite(ref) & (ref != 0)
+    with np.errstate(over="ignore"):
+        e[fin] = d[fin] / np.abs(ref[fin])
+    e[(ref == 0) & (got == 0)] = 0.0
+    e[~np.isfinite(ref) & (d == 0)] = 0.0
     return e
 
 
+def fold_max(a: float, b: float) -> float:
+    """max(a, b) for folding error maxima over chunks: NaN in either counts as an
+    infinite error (Python's max(0.0, nan) is 0.0, which would drop it)."""
+    if a != a or b != b:
+        return float("inf")
+    return a if a >= b else b
+
+
 def report(got: np.ndarray, ref: np.ndarray) -> dict:
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
+    """Largest relative error (``rel_err``) and, as context, the max-abs,
+    mean-abs and RMSE of the differences (``abs_diff``) the letter reports."""
     e = rel_err(got, ref)
-    d = np.abs(got - ref)
+    d = abs_diff(got, ref)
     return {
         "max_rel": float(e.max()) if e.size else 0.0,
         "max_abs": float(d.max()) if d.size else 0.0,

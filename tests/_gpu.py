@@ -48,9 +48,9 @@ def oracle_report(x: np.ndarray, gamma: np.ndarray, out: np.ndarray, eps: float,
         if out.dtype == np.uint8:
             worst["rejected"] += int(np.count_nonzero(~compare.e4m3_accepts(out[lo:hi], y)))
         r = compare.report(got, y)
-        worst["max_rel"] = max(worst["max_rel"], r["max_rel"])
-        worst["max_abs"] = max(worst["max_abs"], r["max_abs"])
-        d = np.abs(got - y)
+        worst["max_rel"] = compare.fold_max(worst["max_rel"], r["max_rel"])
+        worst["max_abs"] = compare.fold_max(worst["max_abs"], r["max_abs"])
+        d = compare.abs_diff(got, y)
         worst["sum_abs"] += float(d.sum())
         worst["sum_sq"] += float((d * d).sum())
         worst["n"] += r["n"]
@@ -108,9 +108,9 @@ def layernorm_report(x, gamma, beta, out, eps, chunk: int = 4096, threads: int =
         err = compare.layernorm_scaled_error(got, y, compare.decode_out(x[lo:hi]), mu, rs,
                                              compare.decode_out(gamma),
                                              None if beta is None else compare.decode_out(beta), eps)
-        worst = max(worst, float(err.max()) if err.size else 0.0)
-        d = np.abs(got - y)
-        max_abs = max(max_abs, float(d.max()) if d.size else 0.0)
+        worst = compare.fold_max(worst, float(err.max()) if err.size else 0.0)
+        d = compare.abs_diff(got, y)
+        max_abs = compare.fold_max(max_abs, float(d.max()) if d.size else 0.0)
         sum_sq += float((d * d).sum())
         n += d.size
     return {"max_scaled": worst, "max_abs": max_abs, "rmse": (sum_sq / max(n, 1)) ** 0.5, "n": n}

@@ -185,23 +185,36 @@ def test_timeout_is_reported_and_recovers():
     w = inputs.DECODE
     d = inputs.make_host(w)
     assert ops.check_fault() == ops.QKN_OK
-    ops.set_option("spin_limit_ns", 1_000_000)  # 1 ms
-    ops.set_option("test_skip_publish", 1)     # no partial is ever published
-    run_fused(d, 4, w.eps)
-    assert ops.check_fault() == ops.QKN_ETIMEOUT
-    assert ops.check_fault() == ops.QKN_OK  # cleared
-    ops.set_option("test_skip_publish", 0)
-    ops.set_option("spin_limit_ns", 1_000_000_000)
+    try:
+        ops.set_option("spin_limit_ns", 1_000_000)  # 1 ms
+        ops.set_option("test_skip_publish", 1)     # no partial is ever published
+        run_fused(d, 4, w.eps)
+        assert ops.check_fault() == ops.QKN_ETIMEOUT
+        assert ops.check_fault() == ops.QKN_OK  # cleared
+    finally:
+        # restore the defaults even when an assertion failed, so later tests do
+        # not inherit a 1 ms spin limit and a kernel that never publishes
+        ops.set_option("test_skip_publish", 0)
+        ops.set_option("spin_limit_ns", 1_000_000_000)
+        ops.check_fault()
     oq, ok = run_fused(d, 4, w.eps)
     assert ops.check_fault() == ops.QKN_OK
     assert_parity(d["q"], d["gamma_q"], oq, w.eps)
 
 
 def test_coresidency_query():
+    """The co-resident capacity the library reports for the prefill shape holds the
+    grid it plans, is a whole number of workgroups per CU, and fits the CU's wave
+    slots (4 SIMDs x 8 waves on gfx950) for that launch's workgroup size."""
+    plan = ops.current_plan("bf16", 16384, 5120, 5120, 2)
     n = ops.max_coresident_workgroups("bf16", 5120, 5120, 2)
-    props = torch.cuda.get_device_properties(0)
-    assert n >= 2 and n % 1 == 0
-    assert n <= props.multi_processor_count * 32
+    bpc, cu = ops.device_occupancy("bf16")
+    assert cu == torch.cuda.get_device_properties(0).multi_processor_count
+    assert n % cu == 0 and n // cu >= 1
+    assert plan["grid"] <= n, (plan, n)
+    assert n // cu <= 32 // (plan["data_waves"] + 1), (plan, n, cu)
+    if not plan["st"]:
+        assert n == bpc[plan["variant"]][plan["data_waves"]] * cu
 
 
 def test_bench_helpers_compute_the_same():

@@ -30,7 +30,7 @@ def assert_hw_parity(x, g, D, out, eps, what=""):
     worst = 0.0
     for lo in range(0, x.shape[0], 4096):
         y, _ = oracle.headwise(x[lo:lo + 4096], g, D, eps, threads=8)
-        worst = max(worst, compare.report(compare.decode_out(out[lo:lo + 4096]), y)["max_rel"])
+        worst = compare.fold_max(worst, compare.report(compare.decode_out(out[lo:lo + 4096]), y)["max_rel"])
     tol = compare.TOL["bf16" if out.dtype == np.uint16 else "f32"]
     assert worst <= tol, f"{what}: max rel err {worst:.3e} > {tol}"
     return worst

@@ -325,6 +325,14 @@ int64_t qknorm_get_option(int key);
 int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
                       int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
 
+/* Bandwidth ceiling for byte mixes that write twice what they read (E4M3
+ * inputs with bf16 outputs): every byte of q (bytes_q of them) becomes one
+ * 16-bit word of out_q, the byte zero-extended (out_q holds 2 * bytes_q
+ * bytes), and likewise k -> out_k. Pointers must be 16-byte aligned; an
+ * output overlapping any input or the other output is QKN_EOVERLAP. */
+int qknorm_bench_widen(const void* q, const void* k, void* out_q, void* out_k,
+                       int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
+
 /* Measurement helper: issues `repeats` back-to-back fused calls with the same
  * arguments (as the fused entry point of format `dtype`, a QKN_FMT_* value)
  * from C, so that launch-rate-bound shapes can be timed without a host

@@ -1508,6 +1508,29 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k, in
     return QKN_OK;
 }
 
+int qknorm_bench_widen(const void* q, const void* k, void* out_q, void* out_k, int64_t bytes_q,
+                       int64_t bytes_k, hipStream_t stream)
+{
+    t_hip_error.clear();
+    if (bytes_q < 0 || bytes_k < 0) return QKN_EINVAL;
+    if (bytes_q + bytes_k == 0) return QKN_OK;
+    if (!q || !k || !out_q || !out_k) return QKN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(out_q) || !aligned16(out_k)) return QKN_EINVAL;
+    if (overlaps(range_of(out_q, 2 * bytes_q), range_of(q, bytes_q)) ||
+        overlaps(range_of(out_q, 2 * bytes_q), range_of(k, bytes_k)) ||
+        overlaps(range_of(out_k, 2 * bytes_k), range_of(q, bytes_q)) ||
+        overlaps(range_of(out_k, 2 * bytes_k), range_of(k, bytes_k)) ||
+        overlaps(range_of(out_q, 2 * bytes_q), range_of(out_k, 2 * bytes_k)))
+        return QKN_EOVERLAP;
+    const int64_t ca = bytes_q / 8, cb = bytes_k / 8;
+    const int64_t blocks = std::max<int64_t>(1, (ca + 255) / 256 + (cb + 255) / 256);
+    if (blocks > 0x7fffffff) return QKN_EINVAL;
+    hipLaunchKernelGGL(qkn::widen2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, k, out_q,
+                       out_k, ca, cb, bytes_q - ca * 8, bytes_k - cb * 8);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
 int qknorm_bench_fused(int dtype, const void* q, const void* k, const void* gamma_q,
                        const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
                        float eps, void* out_q, void* out_k, int repeats, hipStream_t stream)

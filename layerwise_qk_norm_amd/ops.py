@@ -85,6 +85,7 @@ _SIGS = {
     "qknorm_set_option": [_I, _I64],
     "qknorm_get_option": [_I],
     "qknorm_bench_copy": [_P, _P, _P, _P, _I64, _I64, _P],
+    "qknorm_bench_widen": [_P, _P, _P, _P, _I64, _I64, _P],
     "qknorm_bench_fused": [_I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _I, _P],
 }
 _RESTYPE = {"qknorm_strerror": ctypes.c_char_p, "qknorm_last_hip_error": ctypes.c_char_p,
@@ -564,6 +565,18 @@ def bench_copy(q, k, out_q, out_k):
                                        out_k.data_ptr(), q.numel() * q.element_size(),
                                        k.numel() * k.element_size(), _stream(q.device)),
                "qknorm_bench_copy")
+
+
+def bench_widen(q, k, out_q, out_k):
+    """Ceiling for 1-byte inputs with 2-byte outputs: out = the input bytes zero-extended
+    to 16-bit words (``out_q`` and ``out_k`` hold twice the bytes of ``q`` and ``k``)."""
+    nq, nk = q.numel() * q.element_size(), k.numel() * k.element_size()
+    if out_q.numel() * out_q.element_size() != 2 * nq or out_k.numel() * out_k.element_size() != 2 * nk:
+        raise ValueError("outputs must hold twice the bytes of the inputs")
+    with torch.cuda.device(q.device):
+        _check(lib().qknorm_bench_widen(q.data_ptr(), k.data_ptr(), out_q.data_ptr(),
+                                        out_k.data_ptr(), nq, nk, _stream(q.device)),
+               "qknorm_bench_widen")
 
 
 def bench_fused(q, k, gamma_q, gamma_k, n_shards: int, eps: float, out_q, out_k, repeats: int):

@@ -152,6 +152,12 @@ def test_split_entry_points_reject_bad_arguments():
     assert L.qknorm_apply_scale_f32(FAKE[0], 0, FAKE[2], 4, 64, FAKE[3], None) == ops.QKN_EINVAL
     assert L.qknorm_bench_copy(FAKE[0] + 4, FAKE[1], FAKE[2], FAKE[3], 64, 64, None) == \
         ops.QKN_EINVAL
+    assert L.qknorm_bench_widen(FAKE[0] + 4, FAKE[1], FAKE[2], FAKE[3], 64, 64, None) == \
+        ops.QKN_EINVAL
+    # out_q (128 bytes from FAKE[2]) reaching into k
+    assert L.qknorm_bench_widen(FAKE[0], FAKE[2] + 64, FAKE[2], FAKE[3], 64, 64, None) == \
+        ops.QKN_EOVERLAP
+    assert L.qknorm_bench_widen(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 0, None) == ops.QKN_OK
 
 
 # ------------------------------------------------------------------ planner

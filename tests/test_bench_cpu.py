@@ -25,3 +25,20 @@ def test_several_ranks_are_refused_with_a_message():
     r = _bench(["--steps", "1", "--warmup", "0"], env={"WORLD_SIZE": "2", "RANK": "0", "LOCAL_RANK": "0"})
     assert r.returncode == 2, r.stdout
     assert "one GPU" in r.stdout
+
+
+def test_reused_activations_equal_full_draws():
+    """The bench draws the prefill activations once and reuses them for the
+    LayerNorm and headwise prefill workloads, whose draws are the same; what it
+    hands those legs must equal their own full draws (checked on 64 tokens)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    from layerwise_qk_norm_amd import inputs
+    cache = {}
+    bench.host_inputs(inputs.PREFILL.with_T(64), cache)
+    for w in (inputs.LN_PREFILL, inputs.HW_PREFILL, inputs.PREFILL_E4M3, inputs.GQA):
+        got, want = bench.host_inputs(w.with_T(64), cache), inputs.make_host(w.with_T(64))
+        assert sorted(got) == sorted(want)
+        for key in got:
+            assert np.array_equal(got[key], want[key]), (w.name, key)

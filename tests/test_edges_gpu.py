@@ -234,6 +234,16 @@ def test_bench_helpers_compute_the_same():
     oa, ob = torch.zeros_like(a), torch.zeros_like(b)
     ops.bench_copy(a, b, oa, ob)
     assert torch.equal(oa, a) and torch.equal(ob, b)
+    # the widening ceiling: each byte becomes a zero-extended 16-bit word (byte
+    # counts with and without whole 8-byte chunks, and a tensor of tail bytes only)
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    for na, nb in ((3 * 1003, 7), (4096, 2048 * 8 + 5), (8, 0)):
+        e = torch.randint(0, 256, (na,), dtype=torch.uint8, device="cuda:0", generator=g)
+        f = torch.randint(0, 256, (max(nb, 1),), dtype=torch.uint8, device="cuda:0", generator=g)[:nb]
+        oe = torch.full((na,), -1, dtype=torch.int16, device="cuda:0")
+        of = torch.full((max(nb, 1),), -1, dtype=torch.int16, device="cuda:0")[:nb]
+        ops.bench_widen(e, f, oe, of)
+        assert torch.equal(oe, e.to(torch.int16)) and torch.equal(of, f.to(torch.int16))
 
 
 

@@ -65,7 +65,9 @@ typedef enum qknorm_status {
     QKN_EHIP = -4,       /* a HIP runtime call or launch failed */
     QKN_ERESIDENCY = -5, /* not even n_shards workgroups can be co-resident */
     QKN_ETIMEOUT = -6,   /* (qknorm_check_fault) a shard exchange timed out */
-    QKN_ECAPTURE = -7    /* fused call issued on a stream under graph capture */
+    QKN_ECAPTURE = -7,   /* fused call issued on a stream under graph capture */
+    QKN_ESCRATCH = -8    /* (qknorm_layerwise_fwd_bf16_noalloc) the launch needs more
+                            exchange slots than the static scratch holds */
 } qknorm_status;
 
 typedef enum qknorm_dtype { QKN_BF16 = 0, QKN_F32 = 1, QKN_E4M3 = 2 } qknorm_dtype;
@@ -109,6 +111,34 @@ int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q,
                              const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
                              int n_shards, float eps, void* out_q, void* out_k,
                              hipStream_t stream);
+
+/* The bf16 fused call without any device allocation, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels, results and errors as
+ * qknorm_layerwise_fwd_bf16, except that the exchange slots, the fault word
+ * and the split fallback's statistics live in a static device array of the
+ * library (2 MiB of slots, 256 B, 1 MiB of fp32 statistics; about 3 MiB per
+ * device, held until the process ends) instead of a per-stream workspace:
+ *  - No hipMalloc, hipFree or other device allocation is made. The first call
+ *    on a device binds that device's copy of the array, clears it with a
+ *    kernel on `stream` and synchronises `stream` once. Host-side bookkeeping
+ *    (launch plans per shape) still lives in host memory.
+ *  - Every call on one device shares that device's array. Calls on the same
+ *    stream are ordered and safe; calls that overlap in time on one device
+ *    (different streams) race on the slots and give unspecified results.
+ *  - The 2^18 slots hold every launch the planner makes on a 256-CU device.
+ *    A launch that needs more (a larger device, or the QKN_OPT_STATIC_SLOTS
+ *    test limit) is refused with QKN_ESCRATCH before anything is launched.
+ *    The split fallback (unaligned or very wide shards) runs over token
+ *    chunks that fit the 1 MiB of statistics, so no token count is refused.
+ *  - A timed-out exchange sets the device's static fault word, which
+ *    qknorm_check_fault(stream) reports (and clears) like a workspace's.
+ *  - Streams under graph capture are refused (QKN_ECAPTURE), as for the
+ *    allocating call. */
+int qknorm_layerwise_fwd_bf16_noalloc(const void* q, const void* k, const void* gamma_q,
+                                      const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
+                                      int n_shards, float eps, void* out_q, void* out_k,
+                                      hipStream_t stream);
 
 /* The same for FP8 activations (the letter's FP8-E4M3 evaluation, Section
  * IV-C: FP32 accumulation for FP8-E4M3 inputs as for BF16): q and k are e4m3
@@ -226,7 +256,8 @@ int qknorm_apply_scale_e4m3(const void* x, const void* gamma, const float* rms_i
 /* ------------------------------------------------------------------ service */
 
 /* Synchronises `stream`, then reports and clears the fault word of that
- * stream's workspace: QKN_OK, QKN_ETIMEOUT, or QKN_EHIP. */
+ * stream's workspace and that of the current device's static scratch (the
+ * no-allocation call's): QKN_OK, QKN_ETIMEOUT (either was set), or QKN_EHIP. */
 int qknorm_check_fault(hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
@@ -313,6 +344,9 @@ enum {
                                    2 = single-tensor tiles wherever allowed */
     QKN_OPT_WPC = 12,           /* 0 = planner's choice, else workgroups per CU the
                                    planner's search must use (launch timing) */
+    QKN_OPT_STATIC_SLOTS = 13,  /* test hook: 0 = the no-allocation call may use all of
+                                   its static slots, else at most this many (so that
+                                   QKN_ESCRATCH can be exercised) */
     QKN_OPT_TEST_SKIP_PUBLISH = 8 /* test hook: 1 = fused workgroups never publish
                                      their partial, so every exchange with n_shards
                                      > 1 ends at the spin limit (kernel still exits) */
@@ -329,7 +363,9 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
  * inputs with bf16 outputs): every byte of q (bytes_q of them) becomes one
  * 16-bit word of out_q, the byte zero-extended (out_q holds 2 * bytes_q
  * bytes), and likewise k -> out_k. Pointers must be 16-byte aligned; an
- * output overlapping any input or the other output is QKN_EOVERLAP. */
+ * output overlapping any input or the other output is QKN_EOVERLAP. A
+ * tensor of 0 bytes may be passed as a null pointer (also for
+ * qknorm_bench_copy). */
 int qknorm_bench_widen(const void* q, const void* k, void* out_q, void* out_k,
                        int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
 

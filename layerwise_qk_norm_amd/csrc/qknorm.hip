@@ -399,6 +399,69 @@ int ensure_scratch(Workspace* w, size_t floats, hipStream_t stream)
     return QKN_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+
+// The no-allocation entry point keeps its scratch in one file-scope device
+// array instead of a workspace: 64-bit exchange slots, then a block holding the
+// fault word, then fp32 statistics for the split fallback. Each device holds
+// its own copy until the process ends. 2^18 slots hold every bf16 RMSNorm
+// launch the planner can make on a device of 256 compute units (at most 16
+// workgroups per CU, each with at most 2 x lag x 2 x rows = 64 slots).
+constexpr size_t kStaticSlots = size_t(1) << 18;         // 2 MiB
+constexpr size_t kStaticFaultWords = 32;                  // 256 B (fault word first)
+constexpr size_t kStaticSplitFloats = size_t(1) << 18;    // 1 MiB
+constexpr size_t kStaticWords = kStaticSlots + kStaticFaultWords + kStaticSplitFloats / 2;
+
+}  // namespace
+
+// Host code never passes the array's name to a kernel or a copy: in host code it
+// is a stand-in, not a device address. Each device's address comes from
+// hipGetSymbolAddress (static_scratch_for below).
+static __device__ __align__(256) unsigned long long scratch[kStaticWords];
+
+namespace {
+
+struct StaticScratch {
+    unsigned long long* base = nullptr;  // this device's copy of `scratch`
+    uint32_t tag_base = 1;               // tag of the next call's first tile
+    unsigned long long* slots() const { return base; }
+    uint32_t* fault() const { return reinterpret_cast<uint32_t*>(base + kStaticSlots); }
+    float* split() const { return reinterpret_cast<float*>(base + kStaticSlots + kStaticFaultWords); }
+};
+std::map<int, StaticScratch> g_static;
+// test hook (QKN_OPT_STATIC_SLOTS): slots of the static array a call may use, 0 = all
+size_t g_static_slot_limit = 0;
+
+int fill_words(unsigned long long* p, size_t n, hipStream_t stream)
+{
+    const unsigned blocks = (unsigned)std::max<size_t>(1, std::min<size_t>((n + 255) / 256, 2048));
+    hipLaunchKernelGGL(qkn::fill_u64_kernel, dim3(blocks), dim3(256), 0, stream, p, (int64_t)n, 0ull);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+// Binds the current device's copy of the array on its first use: the address
+// from hipGetSymbolAddress (with that device current), every word cleared by a
+// kernel on `stream`, and that stream synchronised once, so that a first call
+// on another stream of the device also starts from cleared slots. Slot tags
+// then start at 1, above the cleared words' 0.
+int static_scratch_for(int dev, hipStream_t stream, StaticScratch** out)
+{
+    StaticScratch& s = g_static[dev];
+    if (!s.base) {
+        void* p = nullptr;
+        QKN_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return QKN_EHIP;
+        const int rc = fill_words(static_cast<unsigned long long*>(p), kStaticWords, stream);
+        if (rc) return rc;
+        QKN_HIP(hipStreamSynchronize(stream));
+        s.base = static_cast<unsigned long long*>(p);
+        s.tag_base = 1;
+    }
+    *out = &s;
+    return QKN_OK;
+}
+
 // ---------------------------------------------------------------- validation
 
 struct Range {
@@ -944,10 +1007,57 @@ int headwise_fwd(int fmt, const void* q, const void* k, const void* gq, const vo
 
 // ---------------------------------------------------------------- fused entry
 
-// bq, bk: LayerNorm's beta (either may be null); null for the RMSNorm formats
+// The fused entry point's split fallback (shapes the fused kernel does not
+// take): the three split kernels per tensor, over token chunks whose fp32
+// statistics fit the `floats` words at `buf` ((N+1) per token for RMSNorm,
+// 2N+2 for LayerNorm). Rows are independent, so chunking changes no result.
+int split_fallback(int dtype, const void* q, const void* k, const void* gq, const void* gk,
+                   const void* bq, const void* bk, int64_t T, int64_t Hq, int64_t Hk, int N,
+                   float eps, void* oq, void* ok, float* buf, size_t floats, hipStream_t stream)
+{
+    const Fmt f = fmt_of(dtype);
+    const bool ln = is_layernorm(dtype);
+    const size_t per_token = ln ? (size_t)(2 * N + 2) : (size_t)(N + 1);
+    const int64_t chunk = std::min<int64_t>(T, (int64_t)(floats / per_token));
+    if (chunk < 1) return QKN_ENOMEM;
+    const void* xs[2] = {q, k};
+    const void* gs[2] = {gq, gk};
+    const void* bs[2] = {bq, bk};
+    void* ys[2] = {oq, ok};
+    const int64_t Hs[2] = {Hq, Hk};
+    int rc = QKN_OK;
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+        const int64_t tc = std::min(chunk, T - t0);
+        for (int i = 0; i < 2; ++i) {
+            const void* x = static_cast<const char*>(xs[i]) + t0 * Hs[i] * f.in;
+            void* y = static_cast<char*>(ys[i]) + t0 * Hs[i] * f.out;
+            if (ln) {
+                float* sums = buf;
+                float* sumsq = sums + (size_t)N * tc;
+                float* mean = sumsq + (size_t)N * tc;
+                float* rstd = mean + tc;
+                if ((rc = launch_stats(dtype, x, tc, Hs[i], N, sums, sumsq, stream))) return rc;
+                if ((rc = launch_combine_stats(sums, sumsq, tc, Hs[i], N, eps, mean, rstd, stream))) return rc;
+                if ((rc = launch_apply_norm(dtype, x, gs[i], bs[i], mean, rstd, tc, Hs[i], y, stream)))
+                    return rc;
+            } else {
+                float* part = buf;
+                float* rinv = buf + (size_t)N * tc;
+                if ((rc = launch_sumsq(dtype, x, tc, Hs[i], N, part, stream))) return rc;
+                if ((rc = launch_combine(part, tc, Hs[i], N, eps, rinv, stream))) return rc;
+                if ((rc = launch_apply(dtype, x, gs[i], rinv, tc, Hs[i], y, stream))) return rc;
+            }
+        }
+    }
+    return QKN_OK;
+}
+
+// bq, bk: LayerNorm's beta (either may be null); null for the RMSNorm formats.
+// noalloc: the scratch is this device's copy of the static array (no device
+// memory is allocated), else the (device, stream) workspace.
 int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const void* gk,
                   const void* bq, const void* bk, int64_t T, int64_t Hq, int64_t Hk, int N,
-                  float eps, void* oq, void* ok, hipStream_t stream)
+                  float eps, void* oq, void* ok, hipStream_t stream, bool noalloc = false)
 {
     t_hip_error.clear();
     int rc = check_dims(T, Hq, N);
@@ -987,7 +1097,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
             };
             rc = layerwise_fwd(dtype, at(q, Hq, f.in), at(k, Hk, f.in), gq, gk, bq, bk, tc, Hq, Hk,
                                N, eps, const_cast<void*>(at(oq, Hq, f.out)),
-                               const_cast<void*>(at(ok, Hk, f.out)), stream);
+                               const_cast<void*>(at(ok, Hk, f.out)), stream, noalloc);
             if (rc) return rc;
         }
         return QKN_OK;
@@ -1003,7 +1113,12 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     DevInfo* di = nullptr;
     if ((rc = device_info(dev, dtype, &di))) return rc;
     Workspace* ws = nullptr;
-    if ((rc = workspace_for(dev, stream, &ws))) return rc;
+    StaticScratch* ss = nullptr;
+    if (noalloc) {
+        if ((rc = static_scratch_for(dev, stream, &ss))) return rc;
+    } else if ((rc = workspace_for(dev, stream, &ws))) {
+        return rc;
+    }
 
     const int aligned = aligned16(q) && aligned16(k) && aligned16(gq) && aligned16(gk) &&
                         aligned16(oq) && aligned16(ok) && (!bq || aligned16(bq)) &&
@@ -1022,53 +1137,42 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
         cache.emplace(key, pl);
     }
 
-    if (pl.variant < 0 && is_layernorm(dtype)) {
-        // LayerNorm with the three split kernels, per tensor
-        const size_t need = (size_t)(2 * N + 2) * (size_t)T;
-        if ((rc = ensure_scratch(ws, need, stream))) return rc;
-        float* sums = ws->scratch;
-        float* sumsq = sums + (size_t)N * T;
-        float* mean = sumsq + (size_t)N * T;
-        float* rstd = mean + T;
-        const void* xs[2] = {q, k};
-        const void* gs[2] = {gq, gk};
-        const void* bs[2] = {bq, bk};
-        void* ys[2] = {oq, ok};
-        const int64_t Hs[2] = {Hq, Hk};
-        for (int i = 0; i < 2; ++i) {
-            if ((rc = launch_stats(dtype, xs[i], T, Hs[i], N, sums, sumsq, stream))) return rc;
-            if ((rc = launch_combine_stats(sums, sumsq, T, Hs[i], N, eps, mean, rstd, stream))) return rc;
-            if ((rc = launch_apply_norm(dtype, xs[i], gs[i], bs[i], mean, rstd, T, Hs[i], ys[i], stream)))
-                return rc;
-        }
-        return QKN_OK;
-    }
     if (pl.variant < 0) {
         // Shapes the fused kernel cannot hold in registers (or unaligned): the
         // same computation with the three split kernels, per tensor.
-        const size_t need = (size_t)(N + 1) * (size_t)T;
+        if (noalloc)
+            return split_fallback(dtype, q, k, gq, gk, bq, bk, T, Hq, Hk, N, eps, oq, ok, ss->split(),
+                                  kStaticSplitFloats, stream);
+        const size_t need = (size_t)(is_layernorm(dtype) ? 2 * N + 2 : N + 1) * (size_t)T;
         if ((rc = ensure_scratch(ws, need, stream))) return rc;
-        float* part = ws->scratch;
-        float* rinv = ws->scratch + (size_t)N * T;
-        const void* xs[2] = {q, k};
-        const void* gs[2] = {gq, gk};
-        void* ys[2] = {oq, ok};
-        const int64_t Hs[2] = {Hq, Hk};
-        for (int i = 0; i < 2; ++i) {
-            if ((rc = launch_sumsq(dtype, xs[i], T, Hs[i], N, part, stream))) return rc;
-            if ((rc = launch_combine(part, T, Hs[i], N, eps, rinv, stream))) return rc;
-            if ((rc = launch_apply(dtype, xs[i], gs[i], rinv, T, Hs[i], ys[i], stream))) return rc;
-        }
-        return QKN_OK;
+        return split_fallback(dtype, q, k, gq, gk, bq, bk, T, Hq, Hk, N, eps, oq, ok, ws->scratch, need,
+                              stream);
     }
 
     const size_t entries =
         (size_t)pl.n_groups * 2 * kVariants[pl.variant].lag * N * f.stats * 2 * pl.rows;
-    if ((rc = ensure_slots(ws, entries, stream))) return rc;
-    if ((uint64_t)ws->tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
+    unsigned long long* slots = nullptr;
+    size_t slot_entries = 0;  // every slot the tags of this scratch have touched
+    uint32_t* fault = nullptr;
+    uint32_t* tag_base = nullptr;
+    if (noalloc) {
+        const size_t usable = g_static_slot_limit ? std::min(g_static_slot_limit, kStaticSlots) : kStaticSlots;
+        if (entries > usable) return QKN_ESCRATCH;
+        slots = ss->slots();
+        slot_entries = kStaticSlots;
+        fault = ss->fault();
+        tag_base = &ss->tag_base;
+    } else {
+        if ((rc = ensure_slots(ws, entries, stream))) return rc;
+        slots = ws->slots;
+        slot_entries = ws->slot_entries;
+        fault = ws->fault;
+        tag_base = &ws->tag_base;
+    }
+    if ((uint64_t)*tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
         // tags would wrap: clear every slot so no stale tag can match
-        QKN_HIP(hipMemsetAsync(ws->slots, 0, ws->slot_entries * sizeof(unsigned long long), stream));
-        ws->tag_base = 1;
+        if ((rc = fill_words(slots, slot_entries, stream))) return rc;
+        *tag_base = 1;
     }
 
     FusedParams p;
@@ -1093,14 +1197,14 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     p.n_groups = pl.n_groups;
     p.xcd_map = pl.xcd_map;
     p.eps = eps;
-    p.tag_base = ws->tag_base;
-    p.slots = ws->slots;
-    p.fault = ws->fault;
+    p.tag_base = *tag_base;
+    p.slots = slots;
+    p.fault = fault;
     const double ticks = (double)g_opt.spin_ns * 1e-9 * (double)di->wall_khz * 1e3;
     p.spin_ticks = ticks < 1.0 ? 1 : (uint64_t)ticks;
     p.test_flags = g_opt.test_skip_publish ? 1u : 0u;
     p.nq = pl.st ? (T + pl.rows - 1) / pl.rows : 0;
-    ws->tag_base += (uint32_t)pl.iters;
+    *tag_base += (uint32_t)pl.iters;
 
     FusedFn fn = fused_fn_layout(dtype, pl.variant, pl.st != 0);
     if (!fn) return QKN_EINVAL;
@@ -1164,6 +1268,15 @@ int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q, 
 {
     return layerwise_fwd(QKN_F32, q, k, gamma_q, gamma_k, nullptr, nullptr, T, Hq, Hk, n_shards,
                          eps, out_q, out_k, stream);
+}
+
+int qknorm_layerwise_fwd_bf16_noalloc(const void* q, const void* k, const void* gamma_q,
+                                      const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
+                                      int n_shards, float eps, void* out_q, void* out_k,
+                                      hipStream_t stream)
+{
+    return layerwise_fwd(QKN_FMT_BF16, q, k, gamma_q, gamma_k, nullptr, nullptr, T, Hq, Hk, n_shards,
+                         eps, out_q, out_k, stream, true);
 }
 
 int qknorm_layerwise_fwd_e4m3(const void* q, const void* k, const void* gamma_q, const void* gamma_k,
@@ -1342,18 +1455,25 @@ int qknorm_check_fault(hipStream_t stream)
     int rc = current_device(&dev);
     if (rc) return rc;
     QKN_HIP(hipStreamSynchronize(stream));
-    uint32_t* fault = nullptr;
+    // the stream's workspace and the device's static scratch each hold a fault word
+    uint32_t* faults[2] = {nullptr, nullptr};
     {
         std::lock_guard<std::mutex> lock(g_mu);
         auto it = g_ws.find({dev, stream});
-        if (it == g_ws.end() || !it->second.fault) return QKN_OK;
-        fault = it->second.fault;
+        if (it != g_ws.end()) faults[0] = it->second.fault;
+        auto st = g_static.find(dev);
+        if (st != g_static.end() && st->second.base) faults[1] = st->second.fault();
     }
-    uint32_t h = 0;
-    QKN_HIP(hipMemcpy(&h, fault, sizeof h, hipMemcpyDeviceToHost));
-    if (h == 0) return QKN_OK;
-    QKN_HIP(hipMemset(fault, 0, sizeof h));
-    return QKN_ETIMEOUT;
+    bool timed_out = false;
+    for (uint32_t* fault : faults) {
+        if (!fault) continue;
+        uint32_t h = 0;
+        QKN_HIP(hipMemcpy(&h, fault, sizeof h, hipMemcpyDeviceToHost));
+        if (h == 0) continue;
+        QKN_HIP(hipMemset(fault, 0, sizeof h));
+        timed_out = true;
+    }
+    return timed_out ? QKN_ETIMEOUT : QKN_OK;
 }
 
 const char* qknorm_strerror(int status)
@@ -1367,6 +1487,7 @@ const char* qknorm_strerror(int status)
     case QKN_ERESIDENCY: return "the device cannot hold n_shards co-resident workgroups";
     case QKN_ETIMEOUT: return "a shard exchange timed out; outputs of that call are unspecified";
     case QKN_ECAPTURE: return "the fused path cannot be issued under stream capture";
+    case QKN_ESCRATCH: return "the call needs more exchange slots than the static scratch holds";
     default: return "unknown status";
     }
 }
@@ -1464,6 +1585,9 @@ int qknorm_set_option(int key, int64_t value)
     case QKN_OPT_WPC:
         if (value < 0 || value > 64) return QKN_EINVAL;
         g_opt.wpc = value; return QKN_OK;
+    case QKN_OPT_STATIC_SLOTS:
+        if (value < 0 || (uint64_t)value > kStaticSlots) return QKN_EINVAL;
+        g_static_slot_limit = (size_t)value; return QKN_OK;
     default: return QKN_EINVAL;
     }
 }
@@ -1483,6 +1607,7 @@ int64_t qknorm_get_option(int key)
     case QKN_OPT_SPLIT_VECTORS: return g_opt.split_vectors;
     case QKN_OPT_TILE_LAYOUT: return g_opt.tile_layout;
     case QKN_OPT_WPC: return g_opt.wpc;
+    case QKN_OPT_STATIC_SLOTS: return (int64_t)g_static_slot_limit;
     default: return INT64_MIN;
     }
 }
@@ -1493,7 +1618,8 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k, in
     t_hip_error.clear();
     if (bytes_q < 0 || bytes_k < 0) return QKN_EINVAL;
     if (bytes_q + bytes_k == 0) return QKN_OK;
-    if (!q || !k || !out_q || !out_k) return QKN_EINVAL;
+    // a tensor of no bytes may come with a null pointer (empty tensors have none)
+    if ((bytes_q && (!q || !out_q)) || (bytes_k && (!k || !out_k))) return QKN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(out_q) || !aligned16(out_k)) return QKN_EINVAL;
     const int64_t va = bytes_q / 16, vb = bytes_k / 16;
     int dev = 0, cu = 0, rc = current_device(&dev);
@@ -1514,7 +1640,8 @@ int qknorm_bench_widen(const void* q, const void* k, void* out_q, void* out_k, i
     t_hip_error.clear();
     if (bytes_q < 0 || bytes_k < 0) return QKN_EINVAL;
     if (bytes_q + bytes_k == 0) return QKN_OK;
-    if (!q || !k || !out_q || !out_k) return QKN_EINVAL;
+    // a tensor of no bytes may come with a null pointer (empty tensors have none)
+    if ((bytes_q && (!q || !out_q)) || (bytes_k && (!k || !out_k))) return QKN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(out_q) || !aligned16(out_k)) return QKN_EINVAL;
     if (overlaps(range_of(out_q, 2 * bytes_q), range_of(q, bytes_q)) ||
         overlaps(range_of(out_q, 2 * bytes_q), range_of(k, bytes_k)) ||

@@ -1232,6 +1232,14 @@ copy2_kernel(const void* a, const void* b, void* oa, void* ob, int64_t va, int64
     }
 }
 
+// Sets n 64-bit words at p to v (a kernel rather than a memset, so that the
+// clearing is an ordinary kernel node wherever the call is recorded).
+__global__ void __launch_bounds__(256)
+fill_u64_kernel(unsigned long long* p, int64_t n, unsigned long long v)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
 // Bandwidth ceiling for byte mixes that write twice what they read (E4M3 in,
 // bf16 out): every input byte becomes one 16-bit output word, the byte
 // zero-extended. Each thread loads 8 input bytes and stores their 16 output

@@ -19,7 +19,7 @@ _lib = None
 _lock = threading.Lock()
 
 QKN_OK, QKN_EINVAL, QKN_EOVERLAP, QKN_ENOMEM, QKN_EHIP = 0, -1, -2, -3, -4
-QKN_ERESIDENCY, QKN_ETIMEOUT, QKN_ECAPTURE = -5, -6, -7
+QKN_ERESIDENCY, QKN_ETIMEOUT, QKN_ECAPTURE, QKN_ESCRATCH = -5, -6, -7, -8
 QKN_BF16, QKN_F32, QKN_E4M3 = 0, 1, 2
 # kernel formats (input x / gamma / output y), the ``dtype`` of the planning calls
 FORMATS = {"bf16": 0, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 3, "ln_bf16": 4, "ln_f32": 5}
@@ -29,7 +29,7 @@ MAX_DATA_WAVES = 15
 MAX_SHARDS = 32
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
        "max_groups": 6, "force_split": 7, "test_skip_publish": 8, "data_waves": 9,
-       "split_vectors": 10, "tile_layout": 11, "wpc": 12}
+       "split_vectors": 10, "tile_layout": 11, "wpc": 12, "static_slots": 13}
 
 
 class QKNormError(RuntimeError):
@@ -57,6 +57,7 @@ _P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
 _SIGS = {
     "qknorm_layerwise_fwd_bf16": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
     "qknorm_layerwise_fwd_f32": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
+    "qknorm_layerwise_fwd_bf16_noalloc": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P],
     "qknorm_layerwise_fwd_e4m3": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _I, _P],
     "qknorm_shard_sumsq_bf16": [_P, _I64, _I64, _I, _P, _P],
     "qknorm_shard_sumsq_f32": [_P, _I64, _I64, _I, _P, _P],

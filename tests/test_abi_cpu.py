@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported_and_bound():
 
 
 def test_strerror_and_options():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert ops.strerror(code) and ops.strerror(code) != "unknown status"
     assert ops.strerror(-99) == "unknown status"
     old = ops.get_option("rows")
@@ -158,6 +158,8 @@ def test_split_entry_points_reject_bad_arguments():
     assert L.qknorm_bench_widen(FAKE[0], FAKE[2] + 64, FAKE[2], FAKE[3], 64, 64, None) == \
         ops.QKN_EOVERLAP
     assert L.qknorm_bench_widen(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 0, None) == ops.QKN_OK
+    assert L.qknorm_bench_widen(FAKE[0], 0, FAKE[2], 0, 64, 8, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_copy(0, FAKE[1], FAKE[2], FAKE[3], 16, 16, None) == ops.QKN_EINVAL
 
 
 # ------------------------------------------------------------------ planner

@@ -4,6 +4,10 @@
   [--kernel-trace TRACE_CSV --window KERNEL:START:COUNT]`` writes the per-kernel duration
   table of a ``--kernel-trace --stats`` run and, with a window, the average over one
   run of consecutive dispatches (the benchmark's timed steps, after its warmup).
+  ``--bench-json LINE_JSON --leg PATH --kernel NAME`` takes the window from the
+  profiled benchmark's own JSON line instead: the leg's timed steps start after its
+  preroll calls and the warmup (``--leg`` is the dotted key of the leg, e.g. ``gqa``
+  or ``e4m3.prefill_to_bf16``; empty for the headline leg).
 ``python -m layerwise_qk_norm_amd.profiling sq OUT_TXT CSV... --cmd "..."`` writes the
   instruction-issue counters (SQ_*) of the fused prefill kernel next to the copy
   kernel's, averaged per dispatch, from one or more ``--pmc`` runs.
@@ -57,6 +61,19 @@ def window_stats(trace_csv: str, kernel: str, start: int, count: int):
     return {"name": sel[0]["Kernel_Name"], "n": len(dur), "avg_us": statistics.mean(dur),
             "min_us": min(dur), "max_us": max(dur),
             "start_to_start_us": statistics.mean(gap) if gap else float("nan")}
+
+
+def bench_window(line_json: str, leg: str, kernel: str) -> str:
+    """KERNEL:START:COUNT of a leg's timed steps in a profiled benchmark run: the
+    leg's kernel was launched ``preroll.calls`` times, then ``warmup`` times, then
+    ``steps`` timed times (each leg's kernel is launched by that leg only)."""
+    import json
+    d = json.load(open(line_json))
+    node = d
+    for part in [p for p in leg.split(".") if p]:
+        node = node[part]
+    start = int(node["preroll"]["calls"]) + int(d["warmup"])
+    return f"{kernel}:{start}:{int(d['steps'])}"
 
 
 def summarize_trace(stats_csv: str, out_txt: str, cmd: str, note: str = "",
@@ -179,6 +196,9 @@ def main():
     t.add_argument("--kernel-trace", default="", help="kernel trace CSV for --window")
     t.add_argument("--window", default="",
                    help="KERNEL_SUBSTRING:START:COUNT, dispatches averaged on their own")
+    t.add_argument("--bench-json", default="", help="the profiled run's JSON line")
+    t.add_argument("--leg", default="", help="dotted key of the leg in that line")
+    t.add_argument("--kernel", default="", help="kernel-name substring of the leg's kernel")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_csv")
     f.add_argument("write_csv")
@@ -199,7 +219,8 @@ def main():
     if a.what == "sq":
         summarize_sq(a.csvs, a.out_txt, a.cmd, a.kernel, a.title)
     elif a.what == "trace":
-        summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note, a.kernel_trace, a.window)
+        window = a.window or (bench_window(a.bench_json, a.leg, a.kernel) if a.bench_json else "")
+        summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note, a.kernel_trace, window)
     else:
         summarize_traffic(a.fetch_csv, a.write_csv, a.out_txt, a.cmd_fetch, a.cmd_write,
                           a.algorithmic_bytes, a.kernel, a.title)

@@ -121,3 +121,120 @@ def assert_layernorm_parity(x, gamma, beta, out, eps, what=""):
     tol = compare.TOL[dtype_name(out)]
     assert r["max_scaled"] <= tol, f"{what}: max scaled err {r['max_scaled']:.3e} > {tol} ({r})"
     return r
+
+
+# ---------------------------------------------------------------- launch coverage
+
+_FMT_BYTES = {"bf16": (2, 2), "f32": (4, 4), "e4m3_bf16": (1, 2), "e4m3_e4m3": (1, 1),
+              "ln_bf16": (2, 2), "ln_f32": (4, 4)}
+
+
+def launched_plans(fmt: str, T: int, Hq: int, Hk: int, n_shards: int):
+    """[(first token, plan)] of the fused launches one call makes: the host runs
+    tensors that reach 2^31 - 2^16 bytes as consecutive launches over token
+    ranges (the buffer descriptors take 32-bit offsets), each planned on its own."""
+    from layerwise_qk_norm_amd import ops
+    e_in, e_out = _FMT_BYTES[fmt]
+    tmax = ((1 << 31) - (1 << 16)) // (max(Hq, Hk) * max(e_in, e_out))
+    out = []
+    for t0 in range(0, T, tmax):
+        tc = min(tmax, T - t0)
+        out.append((t0, ops.current_plan(fmt, tc, Hq, Hk, n_shards)))
+    return out
+
+
+def group_tile_rows(fmt: str, T: int, Hq: int, Hk: int, n_shards: int):
+    """Token rows of Q and of K (two sorted arrays) held by the first and the last
+    tile of every workgroup group of the launches a call makes, plus, with
+    single-tensor tiles, the last Q tile and the first K tile. Group g walks
+    tiles g, g + n_groups, ... (the stride loop), so checking these rows element
+    by element compares every group's work with the oracle."""
+    rq, rk = [], []
+    for t0, pl in launched_plans(fmt, T, Hq, Hk, n_shards):
+        if pl["variant"] < 0:
+            continue
+        tc = min(T - t0, ((1 << 31) - (1 << 16)) // (max(Hq, Hk) * max(_FMT_BYTES[fmt])))
+        G, n, r, st = pl["n_groups"], pl["n_tiles"], pl["rows"], pl["st"]
+        g = np.arange(min(G, n))
+        tiles = np.concatenate([g, g + ((n - 1 - g) // G) * G])
+        nq = (tc + r - 1) // r if st else n
+        if st:
+            tiles = np.concatenate([tiles, [nq - 1, nq]])
+        tiles = np.unique(tiles[(tiles >= 0) & (tiles < n)])
+        for t in tiles:
+            if st and t >= nq:
+                lo = (t - nq) * r
+                rk.append(np.arange(t0 + lo, t0 + min(tc, lo + r)))
+            else:
+                lo = t * r
+                rows = np.arange(t0 + lo, t0 + min(tc, lo + r))
+                rq.append(rows)
+                if not st:
+                    rk.append(rows)
+    cat = lambda a: np.unique(np.concatenate(a)) if a else np.zeros(0, np.int64)
+    return cat(rq), cat(rk)
+
+
+# ---------------------------------------------------------------- every row, fp64 on the device
+
+def _rel_err_dev(got, ref):
+    """Elementwise relative error on the device with the oracle checker's rules: an
+    exact zero must be a zero, and NaN anywhere it is not matched is infinite."""
+    err = (got - ref).abs() / ref.abs()
+    err = torch.where(ref == 0, torch.where(got == 0, 0.0, float("inf")), err)
+    same_nan = torch.isnan(got) & torch.isnan(ref)
+    err = torch.where(same_nan, 0.0, torch.nan_to_num(err, nan=float("inf")))
+    return err
+
+
+def device_rms_check(x, g, y, eps: float, tol: float, what: str = ""):
+    """Every element of every row against x * gamma / sqrt(mean(x^2) + eps) computed in
+    fp64 by PyTorch on the device (a plain reference beside the oracle, which checks
+    the sampled rows): max relative error <= tol."""
+    e = float(np.float32(eps))
+    gd = g.double()
+    rows = max(1, (1 << 24) // x.shape[1])
+    worst = 0.0
+    for lo in range(0, x.shape[0], rows):
+        xs = x[lo:lo + rows].double()
+        ref = xs * gd * torch.rsqrt((xs * xs).mean(dim=1, keepdim=True) + e)
+        worst = compare.fold_max(worst, _rel_err_dev(y[lo:lo + rows].double(), ref).max().item())
+    assert worst <= tol, f"{what}: every-row fp64 check, max rel err {worst:.3e} > {tol}"
+    return worst
+
+
+def device_headwise_check(x, g, y, D: int, eps: float, tol: float, what: str = ""):
+    """device_rms_check per head of D columns (gamma [D] shared by the heads)."""
+    e = float(np.float32(eps))
+    gd = g.double()
+    rows = max(1, (1 << 24) // x.shape[1])
+    worst = 0.0
+    for lo in range(0, x.shape[0], rows):
+        xs = x[lo:lo + rows].double().reshape(-1, D)
+        ref = xs * gd * torch.rsqrt((xs * xs).mean(dim=1, keepdim=True) + e)
+        got = y[lo:lo + rows].double().reshape(-1, D)
+        worst = compare.fold_max(worst, _rel_err_dev(got, ref).max().item())
+    assert worst <= tol, f"{what}: every-row fp64 check, max rel err {worst:.3e} > {tol}"
+    return worst
+
+
+def device_layernorm_check(x, g, b, y, eps: float, tol: float, what: str = ""):
+    """Every element against (x - mean) / sqrt(var + eps) * gamma + beta in fp64 on the
+    device (two-pass variance), the error taken against the operand scale
+    rstd * |gamma| * (|x| + |mean| + sigma) + |beta| as the oracle's LayerNorm check."""
+    e = float(np.float32(eps))
+    gd, bd = g.double(), (torch.zeros_like(g, dtype=torch.float64) if b is None else b.double())
+    rows = max(1, (1 << 24) // x.shape[1])
+    worst = 0.0
+    for lo in range(0, x.shape[0], rows):
+        xs = x[lo:lo + rows].double()
+        mu = xs.mean(dim=1, keepdim=True)
+        var = ((xs - mu) ** 2).mean(dim=1, keepdim=True)
+        rstd = torch.rsqrt(var + e)
+        ref = (xs - mu) * rstd * gd + bd
+        scale = rstd * gd.abs() * (xs.abs() + mu.abs() + var.sqrt()) + bd.abs()
+        d = (y[lo:lo + rows].double() - ref).abs()
+        err = torch.nan_to_num(torch.where(d == 0, 0.0, d / scale), nan=float("inf"))
+        worst = compare.fold_max(worst, err.max().item())
+    assert worst <= tol, f"{what}: every-row fp64 check, max scaled err {worst:.3e} > {tol}"
+    return worst

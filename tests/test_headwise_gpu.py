@@ -14,7 +14,7 @@ import torch
 from layerwise_qk_norm_amd import inputs, ops
 from oracle import compare, oracle
 
-from _gpu import needs_gpu, to_dev, to_host
+from _gpu import device_headwise_check, needs_gpu, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -144,16 +144,10 @@ def test_sweep_full_size(w):
                                      np.random.default_rng(zlib.crc32(w.name.encode()))
                                      .integers(0, w.T, 40)]))
     idx = torch.as_tensor(rows, device="cuda:0")
-    tol = 1e-2 if w.dtype == "bf16" else 1e-5
     D = w.head_dim
     for x, g, y, gh in ((q, gq, oq, hd["gamma_q"]), (k, gk, ok, hd["gamma_k"])):
         assert_hw_parity(to_host(x.index_select(0, idx)), gh, D, to_host(y.index_select(0, idx)),
                          w.eps, w.name)
-        # every (row, head): mean((y/gamma)^2) = m/(m + eps), m the head's mean square
-        for lo in range(0, w.T, 4096):
-            xs = x[lo:lo + 4096].double().view(-1, D)
-            ys = y[lo:lo + 4096].double().view(-1, D) / g.double()
-            m = (xs * xs).mean(dim=1)
-            want = m / (m + float(np.float32(w.eps)))
-            assert (((ys * ys).mean(dim=1) - want).abs() / want).max().item() <= tol
+        # every element of every head against a plain fp64 reference on the device
+        device_headwise_check(x, g, y, D, w.eps, compare.TOL[w.dtype], w.name)
     del q, k, oq, ok

@@ -16,7 +16,8 @@ import torch
 from layerwise_qk_norm_amd import inputs, ops
 from oracle import compare, oracle
 
-from _gpu import assert_layernorm_parity, needs_gpu, to_dev, to_host
+from _gpu import (assert_layernorm_parity, device_layernorm_check, group_tile_rows, needs_gpu, to_dev,
+                  to_host)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -173,17 +174,13 @@ def test_sweep_full_size(w):
     rows = np.unique(np.concatenate([[0, 1, w.T // 2, w.T - 1],
                                      np.random.default_rng(zlib.crc32(w.name.encode()))
                                      .integers(0, w.T, 40)]))
-    idx = torch.as_tensor(rows, device="cuda:0")
-    tol = 1e-2 if w.dtype == "bf16" else 1e-5
-    for x, g, b, y, gh, bh in ((q, gq, bq, oq, hd["gamma_q"], hd["beta_q"]),
-                               (k, gk, bk, ok, hd["gamma_k"], hd["beta_k"])):
+    # plus every row of the first and last tile of every group of the launch made
+    plan_q, plan_k = group_tile_rows(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
+    for x, g, b, y, gh, bh, pr in ((q, gq, bq, oq, hd["gamma_q"], hd["beta_q"], plan_q),
+                                   (k, gk, bk, ok, hd["gamma_k"], hd["beta_k"], plan_k)):
+        idx = torch.as_tensor(np.union1d(rows, pr), device="cuda:0")
         assert_layernorm_parity(to_host(x.index_select(0, idx)), gh, bh,
                                 to_host(y.index_select(0, idx)), w.eps, w.name)
-        # every row: z = (y - beta)/gamma has mean 0 and mean square var/(var + eps)
-        for lo in range(0, w.T, 4096):
-            xs, z = x[lo:lo + 4096].double(), (y[lo:lo + 4096].double() - b.double()) / g.double()
-            var = xs.var(dim=1, unbiased=False)
-            want = var / (var + float(np.float32(w.eps)))
-            assert (z.mean(dim=1).abs() <= tol * 4).all()
-            assert (((z * z).mean(dim=1) - want).abs() / want <= tol).all()
+        # every element of every row against a plain fp64 reference on the device
+        device_layernorm_check(x, g, b, y, w.eps, compare.TOL[w.dtype], w.name)
     del q, k, oq, ok

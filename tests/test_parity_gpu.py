@@ -4,8 +4,9 @@
   (several tiles and a ragged tail) and at their full sizes (all rows);
 * the split entry points (partials, reciprocal RMS, outputs);
 * all 320 sweep points at full size, in the launch configuration the
-  benchmark uses: sampled rows against the oracle, every row against the
-  unit-RMS property.
+  benchmark uses: against the oracle on sampled rows and on every row of the
+  first and last tile of every workgroup group of the launch made; every row
+  against a plain fp64 reference computed on the device.
 Tolerances: max relative error 8e-3 for bf16 outputs, 1e-5 for fp32 outputs,
 1e-5 for fp32 statistics.
 """
@@ -18,7 +19,8 @@ import torch
 from layerwise_qk_norm_amd import inputs, ops
 from oracle import compare, oracle
 
-from _gpu import assert_parity, needs_gpu, run_fused, run_split, to_dev, to_host
+from _gpu import (assert_parity, device_rms_check, group_tile_rows, needs_gpu, run_fused, run_split,
+                  to_dev, to_host)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -64,23 +66,14 @@ def _sample_rows(T: int, rng) -> np.ndarray:
     return np.unique(np.concatenate([fixed, rng.integers(0, T, 40)]).clip(0, T - 1))
 
 
-def _unit_rms_property(x: torch.Tensor, g: torch.Tensor, y: torch.Tensor, eps: float, tol: float):
-    """Every row: mean((y/gamma)^2) = m/(m+eps) with m = mean(x^2), checked in fp64."""
-    gd = g.double()
-    for lo in range(0, x.shape[0], 4096):
-        xs, ys = x[lo:lo + 4096].double(), y[lo:lo + 4096].double()
-        m = (xs * xs).mean(dim=1)
-        want = m / (m + float(np.float32(eps)))
-        got = ((ys / gd) ** 2).mean(dim=1)
-        err = ((got - want).abs() / want).max().item()
-        assert err <= tol, f"unit-RMS property off by {err:.3e}"
-
-
 SWEEP = list(inputs.sweep())
 
 
 @pytest.mark.parametrize("w", SWEEP, ids=[w.name for w in SWEEP])
 def test_sweep_full_size(w):
+    """Oracle on 45 sampled rows plus every row of the first and last tile of every
+    workgroup group of the launch actually made; every row of both tensors against a
+    plain fp64 reference on the device."""
     torch.cuda.empty_cache()
     q = inputs.make_device_activations(w, "q", "cuda:0", torch)
     k = inputs.make_device_activations(w, "k", "cuda:0", torch)
@@ -88,10 +81,11 @@ def test_sweep_full_size(w):
     gq, gk = to_dev(hd["gamma_q"]), to_dev(hd["gamma_k"])
     oq, ok = ops.layerwise_fwd(q, k, gq, gk, w.n_shards, w.eps)
     assert ops.check_fault() == ops.QKN_OK
-    rows = _sample_rows(w.T, np.random.default_rng(zlib.crc32(w.name.encode())))
-    idx = torch.as_tensor(rows, device="cuda:0")
-    for x, g, y, gh in ((q, gq, oq, hd["gamma_q"]), (k, gk, ok, hd["gamma_k"])):
+    sample = _sample_rows(w.T, np.random.default_rng(zlib.crc32(w.name.encode())))
+    plan_q, plan_k = group_tile_rows(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
+    for x, g, y, gh, pr in ((q, gq, oq, hd["gamma_q"], plan_q), (k, gk, ok, hd["gamma_k"], plan_k)):
+        idx = torch.as_tensor(np.union1d(sample, pr), device="cuda:0")
         assert_parity(to_host(x.index_select(0, idx)), gh, to_host(y.index_select(0, idx)),
                       w.eps, w.name)
-        _unit_rms_property(x, g, y, w.eps, 1e-2 if w.dtype == "bf16" else 1e-5)
+        device_rms_check(x, g, y, w.eps, compare.TOL[w.dtype], w.name)
     del q, k, oq, ok

@@ -85,7 +85,11 @@ enum {
     QKN_NUM_FORMATS = 6
 };
 
-#define QKN_MAX_SHARDS 32
+/* Up to 64 logical shards. The fused kernel's exchange wave holds shards x
+ * segments x statistics <= 64 slots: mixed Q+K tiles (two segments per token)
+ * take at most 32 shards, single-tensor tiles of one row up to 64 (RMSNorm);
+ * other wide splits run the split kernels from the same entry point. */
+#define QKN_MAX_SHARDS 64
 
 /* ------------------------------------------------------------------ fused
  * Fused Q+K layerwise RMSNorm (Algorithm 1, Phases A-C, persistent grid of

@@ -26,7 +26,7 @@ FORMATS = {"bf16": 0, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 3, "ln_bf16": 4, "l
 E4M3 = torch.float8_e4m3fn
 NUM_VARIANTS = 10
 MAX_DATA_WAVES = 15
-MAX_SHARDS = 32
+MAX_SHARDS = 64
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
        "max_groups": 6, "force_split": 7, "test_skip_publish": 8, "data_waves": 9,
        "split_vectors": 10, "tile_layout": 11, "wpc": 12, "static_slots": 13}

@@ -63,7 +63,7 @@ def fwd(T=4, Hq=64, Hk=64, N=2, eps=1e-6, ptrs=None, fn="qknorm_layerwise_fwd_bf
     return getattr(ops.lib(), fn)(q, k, gq, gk, T, Hq, Hk, N, eps, oq, ok, None)
 
 
-@pytest.mark.parametrize("kw", [dict(N=0), dict(N=33), dict(N=3), dict(Hq=0), dict(Hk=-2),
+@pytest.mark.parametrize("kw", [dict(N=0), dict(N=65), dict(N=3), dict(Hq=0), dict(Hk=-2),
                                 dict(T=-1), dict(eps=-1e-6), dict(eps=float("nan")),
                                 dict(eps=float("inf")), dict(Hq=100, Hk=64, N=8)])
 def test_fused_rejects_bad_arguments(kw):
@@ -122,7 +122,7 @@ def test_layernorm_entry_points_reject_bad_arguments():
         a = ptrs or FAKE
         return getattr(L, f"qknorm_layernorm_fwd_{fn}")(a[0], a[1], a[2], a[3], betas[0], betas[1],
                                                         T, Hq, Hk, N, eps, a[4], a[5], None)
-    for kw in (dict(N=3), dict(T=-1), dict(eps=-1.0), dict(Hq=0), dict(N=33)):
+    for kw in (dict(N=3), dict(T=-1), dict(eps=-1.0), dict(Hq=0), dict(N=65)):
         assert ln(**kw) == ops.QKN_EINVAL
         assert ln(fn="f32", **kw) == ops.QKN_EINVAL
     assert ln(T=0, ptrs=[0] * 6, betas=(0, 0)) == ops.QKN_OK

@@ -37,14 +37,39 @@ def test_ragged_token_counts(T, dtype):
     assert_parity(d["k"], d["gamma_k"], ok, w.eps)
 
 
-@pytest.mark.parametrize("N", [1, 3, 5, 16, 32])
+@pytest.mark.parametrize("N", [1, 3, 5, 16, 32, 48, 64])
 def test_shard_counts(N):
-    H = 256 * N  # 32-wide bf16 shards at N=32... every N divides H
+    H = 256 * N  # 256-wide bf16 shards: every N divides H
     w = inputs.Workload("n", 130, H, H, N, "bf16")
     d = inputs.make_host(w)
     oq, ok = run_fused(d, N, w.eps)
     assert_parity(d["q"], d["gamma_q"], oq, w.eps)
     assert_parity(d["k"], d["gamma_k"], ok, w.eps)
+
+
+@pytest.mark.parametrize("N", [33, 64])
+def test_wide_splits_on_single_tensor_tiles(N):
+    """More than 32 shards fit the exchange wave only with single-tensor tiles of
+    one row (one segment per tile): forced here, the fused kernel runs 64-member
+    groups; the planner's default for such splits is the split kernels."""
+    H = 64 * N
+    w = inputs.Workload("wide", 77, H, H, N, "bf16")
+    d = inputs.make_host(w)
+    try:
+        ops.set_option("tile_layout", 2)
+        plan = ops.current_plan("bf16", w.T, H, H, N)
+        assert plan["variant"] >= 0 and plan["st"] == 1 and plan["rows"] == 1, plan
+        assert plan["grid"] % N == 0
+        oq, ok = run_fused(d, N, w.eps)
+    finally:
+        ops.set_option("tile_layout", 0)
+    assert ops.check_fault() == ops.QKN_OK
+    assert_parity(d["q"], d["gamma_q"], oq, w.eps)
+    assert_parity(d["k"], d["gamma_k"], ok, w.eps)
+    # by default the planner runs such splits on the split kernels
+    assert ops.current_plan("bf16", w.T, H, H, N)["variant"] == -1
+    p, r, y = run_split(d["q"], d["gamma_q"], N, w.eps)
+    assert_parity(d["q"], d["gamma_q"], y, w.eps)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -65,7 +65,8 @@ typedef enum qknorm_status {
     QKN_EHIP = -4,       /* a HIP runtime call or launch failed */
     QKN_ERESIDENCY = -5, /* not even n_shards workgroups can be co-resident */
     QKN_ETIMEOUT = -6,   /* (qknorm_check_fault) a shard exchange timed out */
-    QKN_ECAPTURE = -7,   /* fused call issued on a stream under graph capture */
+    QKN_ECAPTURE = -7,   /* fused call under graph capture with the cooperative
+                            launch option (not recordable) */
     QKN_ESCRATCH = -8    /* (qknorm_layerwise_fwd_bf16_noalloc) the launch needs more
                             exchange slots than the static scratch holds */
 } qknorm_status;
@@ -104,8 +105,16 @@ enum {
  * different streams use different workspaces. A shard exchange that does not
  * complete within the spin limit (default 1 s) abandons the wait, leaves the
  * outputs unspecified and records a fault that qknorm_check_fault reports.
- * The fused path refuses streams under graph capture (QKN_ECAPTURE); the
- * split path below is capturable.
+ *
+ * Under stream capture a fused call allocates nothing and records two kernel
+ * nodes: one that clears the exchange slots the launch uses, then the fused
+ * kernel. Their scratch is a static per-device array reserved for recorded
+ * launches (about 3 MiB), so every replay starts from cleared slots. Replays
+ * of recorded fused launches that overlap in time on one device race on that
+ * array; so do two graphs replayed concurrently. A recorded launch refused
+ * for size (QKN_ESCRATCH) would need more than 2^18 slots. The cooperative
+ * launch option is not recordable (QKN_ECAPTURE). The split path below is
+ * capturable as well.
  */
 int qknorm_layerwise_fwd_bf16(const void* q, const void* k, const void* gamma_q,
                               const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
@@ -137,8 +146,8 @@ int qknorm_layerwise_fwd_f32(const void* q, const void* k, const void* gamma_q,
  *    chunks that fit the 1 MiB of statistics, so no token count is refused.
  *  - A timed-out exchange sets the device's static fault word, which
  *    qknorm_check_fault(stream) reports (and clears) like a workspace's.
- *  - Streams under graph capture are refused (QKN_ECAPTURE), as for the
- *    allocating call. */
+ *  - Under stream capture it records, like the allocating call, a clearing
+ *    kernel and the fused kernel on the array reserved for recorded launches. */
 int qknorm_layerwise_fwd_bf16_noalloc(const void* q, const void* k, const void* gamma_q,
                                       const void* gamma_k, int64_t T, int64_t Hq, int64_t Hk,
                                       int n_shards, float eps, void* out_q, void* out_k,

@@ -419,6 +419,14 @@ constexpr size_t kStaticWords = kStaticSlots + kStaticFaultWords + kStaticSplitF
 // hipGetSymbolAddress (static_scratch_for below).
 static __device__ __align__(256) unsigned long long scratch[kStaticWords];
 
+// Scratch of fused launches recorded under stream capture, laid out like
+// `scratch`. Every recorded launch is preceded by a recorded fill kernel that
+// zeroes the slots it uses, so each replay starts from cleared slots with tags
+// counted from 1; eager calls (tags from a host counter) never use it. Bound by
+// address only (graph_scratch_for below), since a capturing stream may not be
+// synchronised.
+static __device__ __align__(256) unsigned long long graph_scratch[kStaticWords];
+
 namespace {
 
 struct StaticScratch {
@@ -431,6 +439,21 @@ struct StaticScratch {
 std::map<int, StaticScratch> g_static;
 // test hook (QKN_OPT_STATIC_SLOTS): slots of the static array a call may use, 0 = all
 size_t g_static_slot_limit = 0;
+
+std::map<int, StaticScratch> g_graph;  // per device: graph_scratch (tag_base unused)
+
+int graph_scratch_for(int dev, StaticScratch** out)
+{
+    StaticScratch& s = g_graph[dev];
+    if (!s.base) {
+        void* p = nullptr;
+        QKN_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(graph_scratch)));
+        if (!p) return QKN_EHIP;
+        s.base = static_cast<unsigned long long*>(p);
+    }
+    *out = &s;
+    return QKN_OK;
+}
 
 int fill_words(unsigned long long* p, size_t n, hipStream_t stream)
 {
@@ -1105,7 +1128,9 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
 
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     QKN_HIP(hipStreamIsCapturing(stream, &cap));
-    if (cap != hipStreamCaptureStatusNone) return QKN_ECAPTURE;
+    // under capture: graph_scratch, a recorded clearing of the slots, tags from 1
+    const bool captured = cap != hipStreamCaptureStatusNone;
+    if (captured && g_opt.cooperative) return QKN_ECAPTURE;
 
     std::lock_guard<std::mutex> lock(g_mu);
     int dev = 0;
@@ -1114,11 +1139,14 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     if ((rc = device_info(dev, dtype, &di))) return rc;
     Workspace* ws = nullptr;
     StaticScratch* ss = nullptr;
-    if (noalloc) {
+    if (captured) {
+        if ((rc = graph_scratch_for(dev, &ss))) return rc;
+    } else if (noalloc) {
         if ((rc = static_scratch_for(dev, stream, &ss))) return rc;
     } else if ((rc = workspace_for(dev, stream, &ws))) {
         return rc;
     }
+    const bool in_static = captured || noalloc;  // scratch in a static array
 
     const int aligned = aligned16(q) && aligned16(k) && aligned16(gq) && aligned16(gk) &&
                         aligned16(oq) && aligned16(ok) && (!bq || aligned16(bq)) &&
@@ -1140,7 +1168,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     if (pl.variant < 0) {
         // Shapes the fused kernel cannot hold in registers (or unaligned): the
         // same computation with the three split kernels, per tensor.
-        if (noalloc)
+        if (in_static)
             return split_fallback(dtype, q, k, gq, gk, bq, bk, T, Hq, Hk, N, eps, oq, ok, ss->split(),
                                   kStaticSplitFloats, stream);
         const size_t need = (size_t)(is_layernorm(dtype) ? 2 * N + 2 : N + 1) * (size_t)T;
@@ -1155,7 +1183,15 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     size_t slot_entries = 0;  // every slot the tags of this scratch have touched
     uint32_t* fault = nullptr;
     uint32_t* tag_base = nullptr;
-    if (noalloc) {
+    uint32_t graph_tag = 1;
+    if (captured) {
+        if (entries > kStaticSlots) return QKN_ESCRATCH;
+        slots = ss->slots();
+        fault = ss->fault();
+        tag_base = &graph_tag;
+        // recorded before the launch: every replay clears the slots it will use
+        if ((rc = fill_words(slots, entries, stream))) return rc;
+    } else if (noalloc) {
         const size_t usable = g_static_slot_limit ? std::min(g_static_slot_limit, kStaticSlots) : kStaticSlots;
         if (entries > usable) return QKN_ESCRATCH;
         slots = ss->slots();
@@ -1169,7 +1205,7 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
         fault = ws->fault;
         tag_base = &ws->tag_base;
     }
-    if ((uint64_t)*tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
+    if (!captured && (uint64_t)*tag_base + (uint64_t)pl.iters + 1 >= (uint64_t(1) << 32)) {
         // tags would wrap: clear every slot so no stale tag can match
         if ((rc = fill_words(slots, slot_entries, stream))) return rc;
         *tag_base = 1;
@@ -1456,13 +1492,15 @@ int qknorm_check_fault(hipStream_t stream)
     if (rc) return rc;
     QKN_HIP(hipStreamSynchronize(stream));
     // the stream's workspace and the device's static scratch each hold a fault word
-    uint32_t* faults[2] = {nullptr, nullptr};
+    uint32_t* faults[3] = {nullptr, nullptr, nullptr};
     {
         std::lock_guard<std::mutex> lock(g_mu);
         auto it = g_ws.find({dev, stream});
         if (it != g_ws.end()) faults[0] = it->second.fault;
         auto st = g_static.find(dev);
         if (st != g_static.end() && st->second.base) faults[1] = st->second.fault();
+        auto gr = g_graph.find(dev);
+        if (gr != g_graph.end() && gr->second.base) faults[2] = gr->second.fault();
     }
     bool timed_out = false;
     for (uint32_t* fault : faults) {
@@ -1486,7 +1524,7 @@ const char* qknorm_strerror(int status)
     case QKN_EHIP: return "HIP runtime error";
     case QKN_ERESIDENCY: return "the device cannot hold n_shards co-resident workgroups";
     case QKN_ETIMEOUT: return "a shard exchange timed out; outputs of that call are unspecified";
-    case QKN_ECAPTURE: return "the fused path cannot be issued under stream capture";
+    case QKN_ECAPTURE: return "the cooperative launch option cannot be recorded under stream capture";
     case QKN_ESCRATCH: return "the call needs more exchange slots than the static scratch holds";
     default: return "unknown status";
     }

@@ -6,7 +6,7 @@ import torch
 from layerwise_qk_norm_amd import inputs, ops
 from oracle import compare, oracle
 
-from _gpu import assert_layernorm_parity, assert_parity, needs_gpu, run_fused, run_split, to_dev, to_host
+from _gpu import DEV, assert_layernorm_parity, assert_parity, needs_gpu, run_fused, run_split, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -170,27 +170,85 @@ def test_bf16_output_rounds_to_nearest_even():
     assert np.all(y[0] == 0x3F81) and np.all(y[1] == 0x3F80)
 
 
+def _fused_calls():
+    """Fused calls of several kinds on fixed tensors, each returning its outputs:
+    the decode and a ragged prefill-shaped batch (fused kernel), an unaligned
+    shape (the split fallback of the fused entry point), E4M3 and LayerNorm, and
+    the no-allocation entry point through the C ABI."""
+    calls = []
+    for w in (inputs.DECODE, inputs.PREFILL.with_T(389), inputs.Workload("u", 70, 100, 60, 4, "bf16")):
+        d = inputs.make_host(w)
+        t = [to_dev(d[n]) for n in ("q", "k", "gamma_q", "gamma_k")]
+        o = [torch.empty_like(t[0]), torch.empty_like(t[1])]
+        calls.append((lambda t=t, o=o, w=w: ops.layerwise_fwd(*t, w.n_shards, w.eps, out_q=o[0], out_k=o[1]), o))
+    d8 = inputs.make_host(inputs.DECODE_E4M3.with_T(77))
+    t8 = [to_dev(d8[n]) for n in ("q", "k", "gamma_q", "gamma_k")]
+    o8 = [torch.empty(t8[0].shape, dtype=torch.bfloat16, device=DEV),
+          torch.empty(t8[1].shape, dtype=torch.bfloat16, device=DEV)]
+    calls.append((lambda: ops.layerwise_fwd(*t8, 4, 1e-6, out_q=o8[0], out_k=o8[1]), o8))
+    wl = inputs.LN_DECODE
+    dl = inputs.make_host(wl)
+    tl = {n: to_dev(dl[n]) for n in dl}
+    ol = [torch.empty_like(tl["q"]), torch.empty_like(tl["k"])]
+    calls.append((lambda: ops.layernorm_fwd(tl["q"], tl["k"], tl["gamma_q"], tl["gamma_k"], wl.n_shards,
+                                            wl.eps, beta_q=tl["beta_q"], beta_k=tl["beta_k"],
+                                            out_q=ol[0], out_k=ol[1]), ol))
+    dn = inputs.make_host(inputs.GQA.with_T(300))
+    tn = [to_dev(dn[n]) for n in ("q", "k", "gamma_q", "gamma_k")]
+    on = [torch.empty_like(tn[0]), torch.empty_like(tn[1])]
+
+    def noalloc():
+        rc = ops.lib().qknorm_layerwise_fwd_bf16_noalloc(
+            tn[0].data_ptr(), tn[1].data_ptr(), tn[2].data_ptr(), tn[3].data_ptr(), 300, 5120, 1024, 4,
+            1e-6, on[0].data_ptr(), on[1].data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert rc == ops.QKN_OK
+    calls.append((noalloc, on))
+    return calls
+
+
 def test_graph_capture():
+    """Fused calls are recordable: each records a clearing kernel and the fused
+    kernel on the scratch reserved for recorded launches. Replays, with eager work
+    and synchronisation between them, give the eager outputs bit for bit."""
+    calls = _fused_calls()
+    for fn, _ in calls:
+        fn()
+    torch.cuda.synchronize()
+    eager = [[t.clone() for t in outs] for _, outs in calls]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for fn, _ in calls:
+                fn()
+    torch.cuda.current_stream().wait_stream(s)
     w = inputs.DECODE
     d = inputs.make_host(w)
     q, gq = to_dev(d["q"]), to_dev(d["gamma_q"])
     k, gk = to_dev(d["k"]), to_dev(d["gamma_k"])
-    s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
-        # the fused path refuses capture
-        g = torch.cuda.CUDAGraph()
-        with pytest.raises(ops.QKNormError) as e:
-            with torch.cuda.graph(g, stream=s):
-                ops.layerwise_fwd(q, k, gq, gk, 4)
-        assert e.value.status == ops.QKN_ECAPTURE
-    # the split path is capturable; replays match eager, with eager work between them
+    for rep in range(3):
+        for _, outs in calls:
+            for t in outs:
+                t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, outs), ref in zip(calls, eager):
+            for t, r in zip(outs, ref):
+                assert torch.equal(t, r), f"replay {rep}"
+        ops.layerwise_fwd(q, k, gq, gk, 4)  # eager work between replays
+        ops.check_fault()
+        torch.cuda.synchronize()
+    assert ops.check_fault() == ops.QKN_OK
+    # the split path is capturable too; replays match eager
     p = torch.empty((4, w.T), dtype=torch.float32, device="cuda:0")
     r = torch.empty((w.T,), dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(q)
     ops.shard_sumsq(q, 4, p)
     ops.combine_scale(p, w.Hq, w.eps, r)
     ops.apply_scale(q, gq, r, y)
-    eager = y.clone()
+    eager_y = y.clone()
     g2 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g2):
         ops.shard_sumsq(q, 4, p)
@@ -201,9 +259,34 @@ def test_graph_capture():
         p.zero_()
         g2.replay()
         torch.cuda.synchronize()
-        assert torch.equal(y, eager)
+        assert torch.equal(y, eager_y)
         ops.layerwise_fwd(q, k, gq, gk, 4)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_graph_replay_reports_a_timeout():
+    """A recorded launch whose exchange times out (forced by the never-publish test
+    hook, recorded with a 1 ms spin limit) sets the fault word that check_fault reports;
+    the options are restored for later tests."""
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    q, k = to_dev(d["q"]), to_dev(d["k"])
+    gq, gk = to_dev(d["gamma_q"]), to_dev(d["gamma_k"])
+    oq, ok = torch.empty_like(q), torch.empty_like(k)
+    assert ops.check_fault() == ops.QKN_OK
+    g = torch.cuda.CUDAGraph()
+    try:
+        ops.set_option("spin_limit_ns", 1_000_000)
+        ops.set_option("test_skip_publish", 1)
+        with torch.cuda.graph(g):
+            ops.layerwise_fwd(q, k, gq, gk, 4, w.eps, out_q=oq, out_k=ok)
+    finally:
+        ops.set_option("test_skip_publish", 0)
+        ops.set_option("spin_limit_ns", 1_000_000_000)
+    g.replay()
+    torch.cuda.synchronize()
+    assert ops.check_fault() == ops.QKN_ETIMEOUT
+    assert ops.check_fault() == ops.QKN_OK
 
 
 def test_timeout_is_reported_and_recovers():

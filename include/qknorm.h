@@ -268,10 +268,25 @@ int qknorm_apply_scale_e4m3(const void* x, const void* gamma, const float* rms_i
 
 /* ------------------------------------------------------------------ service */
 
-/* Synchronises `stream`, then reports and clears the fault word of that
- * stream's workspace and that of the current device's static scratch (the
- * no-allocation call's): QKN_OK, QKN_ETIMEOUT (either was set), or QKN_EHIP. */
+/* Synchronises `stream`, then reports and clears the fault words of that
+ * stream's workspace, of the current device's static scratch arrays (the
+ * no-allocation call's and the recorded launches') and the device's timeout
+ * flag: QKN_OK, QKN_ETIMEOUT (any was set), or QKN_EHIP. */
 int qknorm_check_fault(hipStream_t stream);
+
+/* Whether a fused launch on the current device has timed out since the last
+ * qknorm_check_fault, without synchronising anything: 1 or 0. A launch sets
+ * the device's flag (a word of pinned host memory) when it abandons an
+ * exchange, so this turns 1 once that launch has reached its timeout; launches
+ * still running are not seen. The flag exists from the first fused call made
+ * outside stream capture; launches recorded under capture do not set it (their
+ * timeouts are reported by qknorm_check_fault only). */
+int qknorm_fault_pending(void);
+
+/* Host address of the current device's timeout flag (allocated here if needed;
+ * NULL if pinned memory is unavailable): nonzero once a fused launch timed out,
+ * cleared by qknorm_check_fault. Lets a binding poll it without a call. */
+const uint32_t* qknorm_fault_flag(void);
 
 /* Static English text for a status code (never NULL). */
 const char* qknorm_strerror(int status);

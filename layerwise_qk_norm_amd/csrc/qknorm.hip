@@ -287,6 +287,38 @@ struct DevInfo {
 std::mutex g_mu;
 std::map<int, DevInfo> g_dev;
 
+// Per device: a word of pinned, device-mapped host memory that a fused launch
+// sets when an exchange times out, so that the host can see a fault without
+// synchronising (qknorm_fault_pending); qknorm_check_fault clears it. Its device
+// address sits next to each fault word (fault + 2) of the workspaces and of the
+// no-allocation scratch; launches recorded under capture set the device fault
+// word only.
+struct FaultFlag {
+    uint32_t* host = nullptr;
+    uint32_t* dev = nullptr;
+};
+std::map<int, FaultFlag> g_flag;
+
+// The current device's flag, allocated on first use outside stream capture
+// (null while none exists).
+FaultFlag* fault_flag(int dev, bool may_alloc)
+{
+    FaultFlag& f = g_flag[dev];
+    if (!f.host && may_alloc) {
+        void* h = nullptr;
+        if (hipHostMalloc(&h, 64, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) return &f;
+        void* d = nullptr;
+        if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess) {
+            (void)hipHostFree(h);
+            return &f;
+        }
+        *static_cast<volatile uint32_t*>(h) = 0;
+        f.host = static_cast<uint32_t*>(h);
+        f.dev = static_cast<uint32_t*>(d);
+    }
+    return &f;
+}
+
 int device_info(int dev, int dtype, DevInfo** out)
 {
     DevInfo& d = g_dev[dev];
@@ -350,6 +382,16 @@ struct Workspace {
 
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
+// Stores the device's timeout flag address at fault + 2 (after the fault block
+// was cleared on the same stream), where a timed-out launch finds it.
+int bind_fault_flag(int dev, uint32_t* fault, hipStream_t stream)
+{
+    const FaultFlag* f = fault_flag(dev, true);
+    if (!f->dev) return QKN_OK;  // no pinned memory: device fault word only
+    QKN_HIP(hipMemcpyAsync(fault + 2, &f->dev, sizeof f->dev, hipMemcpyHostToDevice, stream));
+    return QKN_OK;
+}
+
 int workspace_for(int dev, hipStream_t stream, Workspace** out)
 {
     Workspace& w = g_ws[{dev, stream}];
@@ -359,6 +401,8 @@ int workspace_for(int dev, hipStream_t stream, Workspace** out)
         if (hipMalloc(&p, 256) != hipSuccess) return QKN_ENOMEM;
         w.fault = static_cast<uint32_t*>(p);
         QKN_HIP(hipMemsetAsync(w.fault, 0, 256, stream));
+        const int rc = bind_fault_flag(dev, w.fault, stream);
+        if (rc) return rc;
     }
     *out = &w;
     return QKN_OK;
@@ -475,10 +519,14 @@ int static_scratch_for(int dev, hipStream_t stream, StaticScratch** out)
         void* p = nullptr;
         QKN_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
         if (!p) return QKN_EHIP;
-        const int rc = fill_words(static_cast<unsigned long long*>(p), kStaticWords, stream);
+        int rc = fill_words(static_cast<unsigned long long*>(p), kStaticWords, stream);
         if (rc) return rc;
-        QKN_HIP(hipStreamSynchronize(stream));
         s.base = static_cast<unsigned long long*>(p);
+        if ((rc = bind_fault_flag(dev, s.fault(), stream))) {
+            s.base = nullptr;
+            return rc;
+        }
+        QKN_HIP(hipStreamSynchronize(stream));
         s.tag_base = 1;
     }
     *out = &s;
@@ -1503,6 +1551,15 @@ int qknorm_check_fault(hipStream_t stream)
         if (gr != g_graph.end() && gr->second.base) faults[2] = gr->second.fault();
     }
     bool timed_out = false;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto fl = g_flag.find(dev);
+        if (fl != g_flag.end() && fl->second.host) {
+            volatile uint32_t* h = fl->second.host;
+            if (*h) timed_out = true;
+            *h = 0;
+        }
+    }
     for (uint32_t* fault : faults) {
         if (!fault) continue;
         uint32_t h = 0;
@@ -1512,6 +1569,24 @@ int qknorm_check_fault(hipStream_t stream)
         timed_out = true;
     }
     return timed_out ? QKN_ETIMEOUT : QKN_OK;
+}
+
+int qknorm_fault_pending(void)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto fl = g_flag.find(dev);
+    if (fl == g_flag.end() || !fl->second.host) return 0;
+    return *static_cast<volatile uint32_t*>(fl->second.host) != 0;
+}
+
+const uint32_t* qknorm_fault_flag(void)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(g_mu);
+    return fault_flag(dev, true)->host;
 }
 
 const char* qknorm_strerror(int status)

@@ -261,7 +261,8 @@ struct FusedParams {
     float eps;
     uint32_t tag_base;     // tag of a group's first tile; its tile k uses tag_base + k
     unsigned long long* slots;  // [n_groups][2*LAG][n_shards][stats*2*rows]
-    uint32_t* fault;
+    uint32_t* fault;       // fault word; the 64-bit word at fault + 2 holds the device
+                           // address of a pinned host word also set on a timeout, or 0
     uint64_t spin_ticks;   // wall-clock ticks a comm wave may wait for one tile
     uint32_t test_flags;   // bit 0: never publish (forces the timeout path)
     int64_t nq;            // single-tensor tiles: tiles 0..nq-1 hold Q rows, nq..n_tiles-1 K rows
@@ -386,7 +387,13 @@ fused_qknorm_kernel(FusedParams p)
                         }
                         if (!__any(need)) break;
                         if (wall_clock64() - t0 > p.spin_ticks) {
-                            if (lane == 0) atomicOr(p.fault, 1u);
+                            if (lane == 0) {
+                                atomicOr(p.fault, 1u);
+                                uint32_t* const host = reinterpret_cast<uint32_t*>(
+                                    *reinterpret_cast<const unsigned long long*>(p.fault + 2));
+                                if (host)
+                                    __hip_atomic_store(host, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                            }
                             abandon = true;
                             break;
                         }

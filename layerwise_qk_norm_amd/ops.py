@@ -76,6 +76,8 @@ _SIGS = {
     "qknorm_headwise_fwd_bf16": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _P],
     "qknorm_headwise_fwd_f32": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _P],
     "qknorm_check_fault": [_P],
+    "qknorm_fault_pending": [],
+    "qknorm_fault_flag": [],
     "qknorm_strerror": [_I],
     "qknorm_last_hip_error": [],
     "qknorm_max_coresident_workgroups": [_I, _I64, _I64, _I, ctypes.POINTER(_I)],
@@ -90,7 +92,7 @@ _SIGS = {
     "qknorm_bench_fused": [_I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _I, _P],
 }
 _RESTYPE = {"qknorm_strerror": ctypes.c_char_p, "qknorm_last_hip_error": ctypes.c_char_p,
-            "qknorm_get_option": ctypes.c_int64}
+            "qknorm_get_option": ctypes.c_int64, "qknorm_fault_flag": ctypes.c_void_p}
 
 
 def library_path() -> str:
@@ -205,9 +207,31 @@ def _current_device() -> int:
     return _GET_DEVICE() if _GET_DEVICE is not None else torch.cuda.current_device()
 
 
+_FLAGS = {}  # device index -> the device's timeout flag (pinned host word), or None
+
+
+def _timeout_flag(index: int):
+    f = _FLAGS.get(index, False)
+    if f is False:
+        with torch.cuda.device(index):
+            addr = lib().qknorm_fault_flag()
+        f = ctypes.c_uint32.from_address(addr) if addr else None
+        _FLAGS[index] = f
+    return f
+
+
 def _issue(fn, args, index: int, what: str):
     """Calls a C entry point on the current stream of device ``index``, with that
-    device current (the library plans and keeps its workspace per current device)."""
+    device current (the library plans and keeps its workspace per current device).
+
+    Before issuing it reads the device's timeout flag, a word of pinned host memory
+    that a fused launch sets when it abandons an exchange: if an earlier call timed
+    out, its outputs are unspecified and this raises QKNormError (QKN_ETIMEOUT)
+    without issuing, until check_fault() clears the flag."""
+    f = _timeout_flag(index)
+    if f is not None and f.value:
+        raise QKNormError(QKN_ETIMEOUT, f"{what}: an earlier fused call on cuda:{index} timed out "
+                          "(its outputs are unspecified; check_fault() clears this)")
     if _current_device() == index:
         status = fn(*args, _raw_stream(index))
     else:
@@ -502,8 +526,17 @@ def apply_scale(x, gamma, rms_inv, out=None, out_dtype=None):
     return out
 
 
+def fault_pending(device=None) -> bool:
+    """Whether a fused launch on the device has timed out since the last
+    check_fault(), without synchronising (launches still running are not seen)."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    with torch.cuda.device(device):
+        return bool(lib().qknorm_fault_pending())
+
+
 def check_fault(device=None) -> int:
-    """Synchronise the current stream and return (and clear) its fault status."""
+    """Synchronise the current stream and return (and clear) its fault status, the
+    static scratch arrays' and the device's timeout flag."""
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
     with torch.cuda.device(device):
         return lib().qknorm_check_fault(_stream(device))

@@ -310,6 +310,48 @@ def test_timeout_is_reported_and_recovers():
     assert_parity(d["q"], d["gamma_q"], oq, w.eps)
 
 
+def test_timeout_is_loud_at_the_next_python_call():
+    """A timed-out launch issued through the C ABI (no check) sets the device's
+    pinned timeout flag: fault_pending() sees it without synchronising once the
+    launch has ended, the next call through the binding raises QKN_ETIMEOUT
+    without issuing, and check_fault() clears everything."""
+    w = inputs.DECODE
+    d = inputs.make_host(w)
+    q, k = to_dev(d["q"]), to_dev(d["k"])
+    gq, gk = to_dev(d["gamma_q"]), to_dev(d["gamma_k"])
+    oq, ok = torch.empty_like(q), torch.empty_like(k)
+    assert ops.check_fault() == ops.QKN_OK
+    ops.layerwise_fwd(q, k, gq, gk, 4, w.eps, out_q=oq, out_k=ok)  # the flag exists from here
+    torch.cuda.synchronize()
+    assert not ops.fault_pending()
+    try:
+        ops.set_option("spin_limit_ns", 1_000_000)
+        ops.set_option("test_skip_publish", 1)
+        rc = ops.lib().qknorm_layerwise_fwd_bf16(q.data_ptr(), k.data_ptr(), gq.data_ptr(), gk.data_ptr(),
+                                                 w.T, w.Hq, w.Hk, 4, w.eps, oq.data_ptr(), ok.data_ptr(),
+                                                 torch.cuda.current_stream().cuda_stream)
+        assert rc == ops.QKN_OK
+        torch.cuda.synchronize()
+    finally:
+        ops.set_option("test_skip_publish", 0)
+        ops.set_option("spin_limit_ns", 1_000_000_000)
+    try:
+        assert ops.fault_pending()
+        oq.fill_(7.0)
+        with pytest.raises(ops.QKNormError) as e:
+            ops.layerwise_fwd(q, k, gq, gk, 4, w.eps, out_q=oq, out_k=ok)
+        assert e.value.status == ops.QKN_ETIMEOUT
+        torch.cuda.synchronize()
+        assert bool((oq == 7.0).all())  # nothing was issued
+    finally:
+        assert ops.check_fault() == ops.QKN_ETIMEOUT
+    assert not ops.fault_pending()
+    assert ops.check_fault() == ops.QKN_OK
+    ops.layerwise_fwd(q, k, gq, gk, 4, w.eps, out_q=oq, out_k=ok)
+    torch.cuda.synchronize()
+    assert_parity(d["q"], d["gamma_q"], to_host(oq), w.eps)
+
+
 def test_coresidency_query():
     """The co-resident capacity the library reports for the prefill shape holds the
     grid it plans, is a whole number of workgroups per CU, and fits the CU's wave

@@ -57,14 +57,18 @@ TRAFFIC_SUMMARY_LN = os.path.join(PROFILES, "fused_layernorm_prefill_T16384_traf
 TRAFFIC_SUMMARY_E4M3_E4M3 = os.path.join(PROFILES, "fused_prefill_e4m3_to_e4m3_T16384_traffic.txt")
 TRAFFIC_SUMMARY_HW = os.path.join(PROFILES, "headwise_prefill_T16384_traffic.txt")
 TRAFFIC_SUMMARY_GQA = os.path.join(PROFILES, "fused_gqa_T8192_traffic.txt")
+# the headwise kernel is one-shot (no planner): its launch is named by its shape
+HEADWISE_PLAN = {"kernel": "headwise", "vectors_per_head": 16, "threads": 256}
+PMC_PLANS = os.path.join(ROOT, "gpurun_out", "pmc_plans.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def read_traffic(path=TRAFFIC_SUMMARY):
-    """HBM bytes per launch from a committed counter summary, if it is current."""
+def read_traffic(path, plan):
+    """HBM bytes per launch from a committed counter summary, if it is current: taken
+    on the same device code and with the launch plan this run uses."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -72,8 +76,8 @@ def read_traffic(path=TRAFFIC_SUMMARY):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    from layerwise_qk_norm_amd.profiling import kernel_source_sha
-    if kv.get("kernel_source_sha") != kernel_source_sha():
+    from layerwise_qk_norm_amd.profiling import kernel_source_sha, plan_line
+    if kv.get("kernel_source_sha") != kernel_source_sha() or kv.get("plan") != plan_line(plan):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -188,11 +192,11 @@ def leg_layernorm(args, torch, stream, prep):
     if ops.check_fault() != ops.QKN_OK:
         raise RuntimeError("LayerNorm prefill reported an exchange timeout")
     nbytes = w.algorithmic_bytes()
+    plan = ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
     out["prefill"] = {
         "workload": f"T={w.T}, Q and K width {w.Hq}, bf16, gamma and beta, {w.n_shards} logical shards",
-        "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre,
-        "plan": ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards),
-        "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_LN)),
+        "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre, "plan": plan,
+        "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_LN, plan)),
         "ceiling": ceiling("copy of the same bytes (the bf16 prefill copy leg)",
                            prep["copy_bytes"], prep["copy_ms"], ms, "shared with the copy leg")}
     wd, t, (oq, ok) = prep["ln_decode"]
@@ -241,10 +245,10 @@ def leg_gqa(args, torch, stream, prep):
     copy_ms, copy_pre = timed_leg(copy, args, stream, torch)
     nbytes = w.algorithmic_bytes()
     moved = nbytes - (w.Hq + w.Hk) * w.elem_bytes
+    plan = ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
     return {"workload": f"T={w.T}, Q width {w.Hq}, K width {w.Hk}, bf16, {w.n_shards} logical shards",
-            "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre,
-            "plan": ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards),
-            "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_GQA)),
+            "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre, "plan": plan,
+            "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_GQA, plan)),
             "ceiling": ceiling("copy of Q and K, three rotating sets", moved, copy_ms, ms, copy_pre)}
 
 
@@ -262,7 +266,7 @@ def leg_headwise(args, torch, stream, prep):
     return {"prefill": {
         "workload": f"T={w.T}, Q and K width {w.Hq} ({w.Hq // w.head_dim} heads of {w.head_dim}), bf16",
         "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre,
-        "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_HW)),
+        "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_HW, HEADWISE_PLAN)),
         "ceiling": ceiling("copy of the same bytes (the bf16 prefill copy leg)",
                            prep["copy_bytes"], prep["copy_ms"], ms, "shared with the copy leg")}}
 
@@ -299,12 +303,12 @@ def leg_e4m3(args, torch, stream, prep):
         cms, cpre = timed_leg(ceil_fn, args, stream, torch)
         nbytes = w.algorithmic_bytes()
         moved = nbytes - (w.Hq + w.Hk) * 2
-        traffic = read_traffic(TRAFFIC_SUMMARY_E4M3 if w.out == "bf16" else TRAFFIC_SUMMARY_E4M3_E4M3)
+        plan = ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards)
+        traffic = read_traffic(TRAFFIC_SUMMARY_E4M3 if w.out == "bf16" else TRAFFIC_SUMMARY_E4M3_E4M3, plan)
         out[key] = {
             "workload": f"T={w.T}, Q and K width {w.Hq}, E4M3 in, bf16 gamma, {w.out} out, "
                         f"{w.n_shards} logical shards",
-            "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre,
-            "plan": ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards),
+            "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre, "plan": plan,
             "roofline": roofline(nbytes, ms, traffic),
             "ceiling": ceiling(kind, moved, cms, ms, cpre)}
     wd, dgq, dgk, (q, k, oq, ok) = prep["decode_e4m3"]
@@ -496,6 +500,15 @@ def run_pmc(torch, prep):
         ops.headwise_fwd(q, k, hq, hk, wh.head_dim, wh.eps, out_q=oq, out_k=ok)
     torch.cuda.synchronize()
     assert ops.check_fault() == ops.QKN_OK
+    # the launch plan of each profiled kernel, for the traffic summaries
+    plans = {"prefill": ops.current_plan(w.fmt, w.T, w.Hq, w.Hk, w.n_shards),
+             "headwise": HEADWISE_PLAN}
+    for key in ("prefill_to_bf16", "prefill_to_e4m3", "gqa"):
+        wk = prep[key][0]
+        plans[key] = ops.current_plan(wk.fmt, wk.T, wk.Hq, wk.Hk, wk.n_shards)
+    plans["ln_prefill"] = ops.current_plan(wl.fmt, wl.T, wl.Hq, wl.Hk, wl.n_shards)
+    os.makedirs(os.path.dirname(PMC_PLANS), exist_ok=True)
+    json.dump(plans, open(PMC_PLANS, "w"), indent=1, sort_keys=True)
     log("pmc mode done: 5 launches each of the fused bf16 prefill kernel and of the copy of "
         f"{w.T * (w.Hq + w.Hk) * w.elem_bytes} bytes read, then 5 each of fused E4M3->bf16 and "
         "E4M3->E4M3 prefill, GQA, LayerNorm prefill and headwise prefill")
@@ -617,7 +630,7 @@ def main():
     log("timing the tiny workload ...")
     tiny = leg_tiny(torch, stream, prep)
 
-    traffic = read_traffic()
+    traffic = read_traffic(TRAFFIC_SUMMARY, plan)
     out = {
         "metric": METRIC,
         "value": round(gbs, 1),

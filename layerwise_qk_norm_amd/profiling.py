@@ -17,8 +17,10 @@
   is scaled by what it reads for the copy kernel of known size in the same run
   (the copy reads and writes exactly the prefill workload's Q and K bytes).
 
-Summaries record the source hash of the kernels they measured; the benchmark
-uses a traffic figure only while that hash matches the current sources.
+Summaries record the hash of the device code they measured (the kernels'
+header) and, for traffic, the launch plan of the kernel (from the plans file that
+``bench.py --pmc`` writes); the benchmark uses a traffic figure only while both
+match the current sources and the plan it launches.
 """
 from __future__ import annotations
 
@@ -29,7 +31,8 @@ import os
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("qknorm_kernels.hpp", "qknorm.hip")]
+# the device code: every kernel and its inlined helpers live in this header
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", "qknorm_kernels.hpp")]
 
 # The copy kernel of the --pmc run moves the prefill workload's Q and K:
 # 16384 x (5120 + 5120) bf16 values read and the same written.
@@ -108,9 +111,16 @@ def _per_kernel(csv_path: str):
     return out
 
 
+def plan_line(plan) -> str:
+    """The launch plan as the one-line JSON the summaries and the benchmark compare."""
+    import json
+    return json.dumps(plan, sort_keys=True)
+
+
 def summarize_traffic(fetch_csv: str, write_csv: str, out_txt: str, cmd_fetch: str,
                       cmd_write: str, algorithmic_bytes: int, kernel: str = "fused_qknorm_kernel<qkn::Bf16",
-                      title: str = "fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)"):
+                      title: str = "fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)",
+                      plan=None):
     fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
     copy_name = next(n for n in fetch if "copy2_kernel" in n)
     fused_name = next(n for n in fetch if kernel in n)
@@ -130,6 +140,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_txt: str, cmd_fetch: s
         f"# copy kernel of known size: {COPY_BYTES} B read and {COPY_BYTES} B written",
         f"kernel_source_sha: {kernel_source_sha()}",
         f"kernel: {short(fused_name)}",
+        f"plan: {plan_line(plan) if plan is not None else 'none'}",
         f"dispatches: {len(fetch[fused_name])} (FETCH_SIZE), {len(write[fused_name])} (WRITE_SIZE)",
         f"fetch_kib_per_dispatch: {kib_f:.3f}",
         f"write_kib_per_dispatch: {kib_w:.3f}",
@@ -209,6 +220,8 @@ def main():
     f.add_argument("--kernel", default="fused_qknorm_kernel<qkn::Bf16",
                    help="substring of the kernel name to summarise")
     f.add_argument("--title", default="fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)")
+    f.add_argument("--plans", default="", help="plans file written by bench.py --pmc")
+    f.add_argument("--leg", default="", help="key of the kernel's launch in the plans file")
     q = sub.add_parser("sq")
     q.add_argument("out_txt")
     q.add_argument("csvs", nargs="+")
@@ -222,8 +235,12 @@ def main():
         window = a.window or (bench_window(a.bench_json, a.leg, a.kernel) if a.bench_json else "")
         summarize_trace(a.stats_csv, a.out_txt, a.cmd, a.note, a.kernel_trace, window)
     else:
+        plan = None
+        if a.plans:
+            import json
+            plan = json.load(open(a.plans)).get(a.leg)
         summarize_traffic(a.fetch_csv, a.write_csv, a.out_txt, a.cmd_fetch, a.cmd_write,
-                          a.algorithmic_bytes, a.kernel, a.title)
+                          a.algorithmic_bytes, a.kernel, a.title, plan)
 
 
 if __name__ == "__main__":

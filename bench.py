@@ -176,6 +176,22 @@ def ceiling(kind, moved_bytes, ms, fused_ms, preroll):
             "fused_frac_of_ceiling": round(ms / fused_ms, 4), "preroll": preroll}
 
 
+def skeleton(args, stream, torch, bufs, w, fmt, moved_bytes, fused_ms):
+    """The fused call's own launch plan run as a copy (no arithmetic, no exchange) on
+    the leg's buffer sets: what the persistent streaming structure itself moves, and
+    the fused kernel's fraction of it."""
+    from layerwise_qk_norm_amd import ops
+
+    def run(i):
+        q, k, oq, ok = bufs[i % len(bufs)]
+        ops.bench_skeleton(q, k, oq, ok, w.n_shards, fmt)
+
+    ms, pre = timed_leg(run, args, stream, torch)
+    return {"kind": "the fused call's launch plan as a copy (no arithmetic, no exchange)",
+            "bytes": moved_bytes, "ms": round(ms, 5), "GBs": round(moved_bytes / (ms * 1e-3) / 1e9, 1),
+            "fused_frac_of_skeleton": round(ms / fused_ms, 4), "preroll": pre}
+
+
 # ---------------------------------------------------------------- legs
 
 def leg_layernorm(args, torch, stream, prep):
@@ -198,7 +214,8 @@ def leg_layernorm(args, torch, stream, prep):
         "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre, "plan": plan,
         "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_LN, plan)),
         "ceiling": ceiling("copy of the same bytes (the bf16 prefill copy leg)",
-                           prep["copy_bytes"], prep["copy_ms"], ms, "shared with the copy leg")}
+                           prep["copy_bytes"], prep["copy_ms"], ms, "shared with the copy leg"),
+        "skeleton": skeleton(args, stream, torch, bufs, w, "ln_bf16", prep["copy_bytes"], ms)}
     wd, t, (oq, ok) = prep["ln_decode"]
 
     def dec(_):
@@ -249,7 +266,8 @@ def leg_gqa(args, torch, stream, prep):
     return {"workload": f"T={w.T}, Q width {w.Hq}, K width {w.Hk}, bf16, {w.n_shards} logical shards",
             "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre, "plan": plan,
             "roofline": roofline(nbytes, ms, read_traffic(TRAFFIC_SUMMARY_GQA, plan)),
-            "ceiling": ceiling("copy of Q and K, three rotating sets", moved, copy_ms, ms, copy_pre)}
+            "ceiling": ceiling("copy of Q and K, three rotating sets", moved, copy_ms, ms, copy_pre),
+            "skeleton": skeleton(args, stream, torch, bufs, w, "bf16", moved, ms)}
 
 
 def leg_headwise(args, torch, stream, prep):
@@ -310,7 +328,8 @@ def leg_e4m3(args, torch, stream, prep):
                         f"{w.n_shards} logical shards",
             "algorithmic_bytes": nbytes, "ms": round(ms, 5), "preroll": pre, "plan": plan,
             "roofline": roofline(nbytes, ms, traffic),
-            "ceiling": ceiling(kind, moved, cms, ms, cpre)}
+            "ceiling": ceiling(kind, moved, cms, ms, cpre),
+            "skeleton": skeleton(args, stream, torch, bufs, w, w.fmt, moved, ms)}
     wd, dgq, dgk, (q, k, oq, ok) = prep["decode_e4m3"]
     ops.bench_fused(q, k, dgq, dgk, wd.n_shards, wd.eps, oq, ok, 200)
     reps = 2000
@@ -568,11 +587,12 @@ def main():
         raise RuntimeError("fused kernel reported an exchange timeout")
     gbs = nbytes / (ms * 1e-3) / 1e9
 
-    log("timing copy ceiling and split path ...")
+    log("timing copy ceiling, the launch skeleton and the split path ...")
     copy_bytes = nbytes - (w.Hq + w.Hk) * w.elem_bytes
     copy_ms, copy_pre = timed_leg(copy, args, stream, torch)
     copy_gbs = copy_bytes / (copy_ms * 1e-3) / 1e9
     prep["copy_bytes"], prep["copy_ms"] = copy_bytes, copy_ms
+    skel = skeleton(args, stream, torch, bufs, w, w.fmt, copy_bytes, ms)
     ops.set_option("force_split", 1)
     try:
         split_ms, split_pre = timed_leg(fused, args, stream, torch)
@@ -657,6 +677,7 @@ def main():
                    "host_visible_prepared_us_per_call": round(host_prep_us, 2)},
         "copy": {"GBs": round(copy_gbs, 1), "ms": round(copy_ms, 5),
                  "fused_frac_of_copy": round(gbs / copy_gbs, 4), "preroll": copy_pre},
+        "skeleton": skel,
         "split": {"GBs": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "ms": round(split_ms, 5),
                   "preroll": split_pre},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,

@@ -397,6 +397,18 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
 int qknorm_bench_widen(const void* q, const void* k, void* out_q, void* out_k,
                        int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
 
+/* Ceiling of the persistent streaming structure for measurements: launches,
+ * for format `dtype` (QKN_FMT_*) and this shape, the fused call's own plan
+ * (grid, workgroup size, tiles, slot layout, groups, XCD mapping, one barrier
+ * per tile and one-tile prefetch) with no arithmetic and no exchange, storing
+ * every byte of q and k unchanged to out_q and out_k (formats whose output
+ * element is twice the input's: each byte zero-extended to a 16-bit word).
+ * Pointers 16-byte aligned; outputs overlapping an input or each other are
+ * QKN_EOVERLAP; a shape the fused kernel does not run (split kernels) or a
+ * tensor of 2^31 - 2^16 bytes or more is QKN_EINVAL. */
+int qknorm_bench_skeleton(int dtype, const void* q, const void* k, void* out_q, void* out_k,
+                          int64_t T, int64_t Hq, int64_t Hk, int n_shards, hipStream_t stream);
+
 /* Measurement helper: issues `repeats` back-to-back fused calls with the same
  * arguments (as the fused entry point of format `dtype`, a QKN_FMT_* value)
  * from C, so that launch-rate-bound shapes can be timed without a host

@@ -20,6 +20,7 @@
 #include <utility>
 
 #include "qknorm_kernels.hpp"
+#include "qknorm_skeleton.hpp"
 
 namespace {
 
@@ -205,6 +206,26 @@ FusedFn fused_fn_layout(int fmt, int v, bool st)
     case QKN_FMT_LN_BF16: return fused_fn_st<Bf16, 1>(v);
     default: return fused_fn_st<F32, 1>(v);
     }
+}
+using SkelFn = void (*)(qkn::SkeletonParams);
+template <bool ST, bool WIDEN>
+SkelFn skeleton_fn_vpt(int vpt)
+{
+    switch (vpt) {
+    case 1: return qkn::skeleton_kernel<1, ST, WIDEN>;
+    case 2: return qkn::skeleton_kernel<2, ST, WIDEN>;
+    case 3: return qkn::skeleton_kernel<3, ST, WIDEN>;
+    case 4: return WIDEN ? nullptr : qkn::skeleton_kernel<4, ST, false>;
+    case 6: return WIDEN ? nullptr : qkn::skeleton_kernel<6, ST, false>;
+    case 9: return WIDEN ? nullptr : qkn::skeleton_kernel<9, ST, false>;
+    default: return nullptr;
+    }
+}
+// the skeleton matching a fused launch's vectors per thread, tile layout and byte mix
+SkelFn skeleton_fn(int vpt, bool st, bool widen)
+{
+    if (st) return widen ? skeleton_fn_vpt<true, true>(vpt) : skeleton_fn_vpt<true, false>(vpt);
+    return widen ? skeleton_fn_vpt<false, true>(vpt) : skeleton_fn_vpt<false, false>(vpt);
 }
 bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
@@ -1767,6 +1788,59 @@ int qknorm_bench_widen(const void* q, const void* k, void* out_q, void* out_k, i
     if (blocks > 0x7fffffff) return QKN_EINVAL;
     hipLaunchKernelGGL(qkn::widen2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, k, out_q,
                        out_k, ca, cb, bytes_q - ca * 8, bytes_k - cb * 8);
+    QKN_HIP(hipGetLastError());
+    return QKN_OK;
+}
+
+int qknorm_bench_skeleton(int dtype, const void* q, const void* k, void* out_q, void* out_k, int64_t T,
+                          int64_t Hq, int64_t Hk, int n_shards, hipStream_t stream)
+{
+    t_hip_error.clear();
+    if (!fmt_valid(dtype)) return QKN_EINVAL;
+    int rc = check_dims(T, Hq, n_shards);
+    if (rc) return rc;
+    if ((rc = check_dims(T, Hk, n_shards))) return rc;
+    if (T == 0) return QKN_OK;
+    if (!q || !k || !out_q || !out_k) return QKN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(out_q) || !aligned16(out_k)) return QKN_EINVAL;
+    const Fmt f = fmt_of(dtype);
+    const Range rq = range_of(q, T * Hq * f.in), rk = range_of(k, T * Hk * f.in);
+    const Range roq = range_of(out_q, T * Hq * f.out), rok = range_of(out_k, T * Hk * f.out);
+    if (overlaps(roq, rok) || overlaps(roq, rq) || overlaps(roq, rk) || overlaps(rok, rq) || overlaps(rok, rk))
+        return QKN_EOVERLAP;
+    // one launch: every tensor below 2^31 - 2^16 bytes (32-bit buffer offsets)
+    if (T * std::max(Hq, Hk) * std::max(f.in, f.out) > (int64_t(1) << 31) - (int64_t(1) << 16)) return QKN_EINVAL;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if ((rc = current_device(&dev))) return rc;
+    DevInfo* di = nullptr;
+    if ((rc = device_info(dev, dtype, &di))) return rc;
+    qknorm_plan pl;
+    if ((rc = plan(dtype, T, Hq, Hk, n_shards, di->cu, &di->occ[dtype][0][0], &di->occ_st[dtype][0][0], 1, &pl)))
+        return rc;
+    if (pl.variant < 0) return QKN_EINVAL;  // the shape has no fused launch to mirror
+    const SkelFn fn = skeleton_fn(kVariants[pl.variant].vpt, pl.st != 0, f.out == 2 * f.in);
+    if (!fn) return QKN_EINVAL;
+    qkn::SkeletonParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x[0] = q;
+    p.x[1] = k;
+    p.y[0] = out_q;
+    p.y[1] = out_k;
+    p.T = T;
+    p.n_tiles = pl.n_tiles;
+    p.nq = pl.st ? (T + pl.rows - 1) / pl.rows : 0;
+    p.H[0] = (int32_t)Hq;
+    p.H[1] = (int32_t)Hk;
+    p.Wv[0] = (int32_t)(Hq / n_shards / f.ev);
+    p.Wv[1] = (int32_t)(Hk / n_shards / f.ev);
+    p.rows = pl.rows;
+    p.nwd = pl.data_waves;
+    p.n_shards = n_shards;
+    p.n_groups = pl.n_groups;
+    p.xcd_map = pl.xcd_map;
+    p.in_bytes = f.in;
+    hipLaunchKernelGGL(fn, dim3(pl.grid), dim3(pl.threads), 0, stream, p);
     QKN_HIP(hipGetLastError());
     return QKN_OK;
 }

@@ -89,6 +89,7 @@ _SIGS = {
     "qknorm_get_option": [_I],
     "qknorm_bench_copy": [_P, _P, _P, _P, _I64, _I64, _P],
     "qknorm_bench_widen": [_P, _P, _P, _P, _I64, _I64, _P],
+    "qknorm_bench_skeleton": [_I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P],
     "qknorm_bench_fused": [_I, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _I, _P],
 }
 _RESTYPE = {"qknorm_strerror": ctypes.c_char_p, "qknorm_last_hip_error": ctypes.c_char_p,
@@ -611,6 +612,19 @@ def bench_widen(q, k, out_q, out_k):
         _check(lib().qknorm_bench_widen(q.data_ptr(), k.data_ptr(), out_q.data_ptr(),
                                         out_k.data_ptr(), nq, nk, _stream(q.device)),
                "qknorm_bench_widen")
+
+
+def bench_skeleton(q, k, out_q, out_k, n_shards: int, fmt: str = ""):
+    """The fused call's launch plan for this shape run as a copy (no arithmetic, no
+    exchange): out = the input bytes, or each byte zero-extended when the output
+    element is twice the input's. ``fmt`` names a format of ``FORMATS`` (by default
+    the RMSNorm format of the tensors' dtypes)."""
+    T, Hq = q.shape
+    Hk = k.shape[1]
+    f = FORMATS[fmt] if fmt else format_of(q.dtype, out_q.dtype)
+    with torch.cuda.device(q.device):
+        _check(lib().qknorm_bench_skeleton(f, q.data_ptr(), k.data_ptr(), out_q.data_ptr(), out_k.data_ptr(),
+                                           T, Hq, Hk, n_shards, _stream(q.device)), "qknorm_bench_skeleton")
 
 
 def bench_fused(q, k, gamma_q, gamma_k, n_shards: int, eps: float, out_q, out_k, repeats: int):

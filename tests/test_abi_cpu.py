@@ -162,6 +162,29 @@ def test_split_entry_points_reject_bad_arguments():
     assert L.qknorm_bench_copy(0, FAKE[1], FAKE[2], FAKE[3], 16, 16, None) == ops.QKN_EINVAL
 
 
+def test_bench_skeleton_rejects_bad_arguments():
+    """The copy skeleton of a fused launch validates like the fused call (no GPU
+    is touched before the arguments pass)."""
+    L = ops.lib()
+    q, k, oq, ok = FAKE[:4]
+    bf16 = ops.FORMATS["bf16"]
+    assert L.qknorm_bench_skeleton(99, q, k, oq, ok, 4, 64, 64, 2, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_skeleton(bf16, q + 4, k, oq, ok, 4, 64, 64, 2, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_skeleton(bf16, q, 0, oq, ok, 4, 64, 64, 2, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_skeleton(bf16, q, k, oq, ok, -1, 64, 64, 2, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_skeleton(bf16, q, k, oq, ok, 4, 64, 64, 3, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_skeleton(bf16, q, k, oq, ok, 0, 64, 64, 2, None) == ops.QKN_OK
+    # out_q (512 bytes) reaching into k; out_k on top of out_q
+    assert L.qknorm_bench_skeleton(bf16, q, k, k - 256, ok, 4, 64, 64, 2, None) == ops.QKN_EOVERLAP
+    assert L.qknorm_bench_skeleton(bf16, q, k, oq, oq + 16, 4, 64, 64, 2, None) == ops.QKN_EOVERLAP
+    # E4M3 inputs with bf16 outputs: out_q holds twice q's bytes (256 -> 512)
+    e4b = ops.FORMATS["e4m3_bf16"]
+    assert L.qknorm_bench_skeleton(e4b, q, k, k - 256, ok, 4, 64, 64, 2, None) == ops.QKN_EOVERLAP
+    # one launch only: tensors below 2^31 - 2^16 bytes
+    far = [(i + 1) << 40 for i in range(4)]  # 1 TiB apart: no overlap even at this size
+    assert L.qknorm_bench_skeleton(bf16, *far, 1 << 20, 4096, 4096, 2, None) == ops.QKN_EINVAL
+
+
 # ------------------------------------------------------------------ planner
 
 CU = 256

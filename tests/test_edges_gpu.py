@@ -497,3 +497,48 @@ def test_prepared_call_validates_once_and_reports_errors():
     with pytest.raises(ops.QKNormError) as e:
         bad()
     assert e.value.status == ops.QKN_EINVAL
+
+
+def _random_bytes(shape, dtype, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    n = int(np.prod(shape)) * torch.empty(0, dtype=dtype).element_size()
+    return torch.randint(0, 256, (n,), generator=g, dtype=torch.uint8, device=DEV).view(dtype).view(shape)
+
+
+@pytest.mark.parametrize("fmt,T,Hq,Hk,N,layout", [
+    ("bf16", 389, 5120, 5120, 2, 0), ("bf16", 389, 5120, 5120, 2, 1), ("bf16", 389, 5120, 5120, 2, 2),
+    ("bf16", 1001, 5120, 1024, 4, 0), ("bf16", 16384, 5120, 5120, 2, 0), ("bf16", 8192, 5120, 1024, 4, 0),
+    ("f32", 200, 2048, 1024, 2, 0), ("ln_bf16", 300, 4096, 4096, 4, 0),
+    ("e4m3_e4m3", 777, 5120, 5120, 2, 0), ("e4m3_bf16", 500, 5120, 5120, 2, 0),
+    ("e4m3_bf16", 16384, 5120, 5120, 2, 0),
+])
+def test_bench_skeleton_moves_every_byte(fmt, T, Hq, Hk, N, layout):
+    """The copy skeleton of a fused launch (the fused call's own plan, without the
+    arithmetic) stores every byte of q and k, unchanged or zero-extended."""
+    ops.set_option("tile_layout", layout)
+    tin = {"bf16": torch.bfloat16, "f32": torch.float32, "ln_bf16": torch.bfloat16,
+           "e4m3_e4m3": torch.float8_e4m3fn, "e4m3_bf16": torch.float8_e4m3fn}[fmt]
+    tout = torch.bfloat16 if fmt == "e4m3_bf16" else tin
+    q, k = _random_bytes((T, Hq), tin, 1), _random_bytes((T, Hk), tin, 2)
+    oq = torch.full((T, Hq), 0, dtype=torch.uint8 if tout == torch.float8_e4m3fn else torch.int16, device=DEV)
+    ok = torch.full((T, Hk), 0, dtype=oq.dtype, device=DEV)
+    if tout == torch.float32:
+        oq, ok = oq.to(torch.int32), ok.to(torch.int32)
+    oq.fill_(-1 if oq.dtype != torch.uint8 else 0xAB)
+    ok.fill_(-1 if ok.dtype != torch.uint8 else 0xAB)
+    oq, ok = oq.view(tout), ok.view(tout)
+    ops.bench_skeleton(q, k, oq, ok, N, fmt)
+    torch.cuda.synchronize()
+    for x, y in ((q, oq), (k, ok)):
+        xb = x.view(torch.uint8)
+        if fmt == "e4m3_bf16":
+            assert torch.equal(y.view(torch.int16).to(torch.int32) & 0xffff, xb.to(torch.int32)), fmt
+        else:
+            assert torch.equal(y.contiguous().view(torch.uint8), xb), (fmt, T, Hq, Hk, N, layout)
+
+
+def test_bench_skeleton_refuses_split_shapes():
+    # shard widths that are not whole vectors run the split kernels: no fused plan to mirror
+    q = torch.zeros((8, 100), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ops.QKNormError):
+        ops.bench_skeleton(q, q.clone(), torch.empty_like(q), torch.empty_like(q), 4)

@@ -360,7 +360,9 @@ enum {
     QKN_OPT_FORCE_VARIANT = 2,  /* -1 = planner's choice, else a variant id */
     QKN_OPT_ROWS = 3,           /* 0 = planner's choice, else rows per tile (<= 4; single-tensor
                                    tiles <= 8) */
-    QKN_OPT_XCD_MAP = 4,        /* -1 = auto, 0 = off, 1 = on when possible */
+    QKN_OPT_XCD_MAP = 4,        /* -1 = planner's choice (a group's members on one XCD,
+                                   except for the tuned launches measured faster
+                                   without), 0 = off, 1 = on when possible */
     QKN_OPT_COOPERATIVE = 5,    /* 1 = hipLaunchCooperativeKernel, 0 = plain */
     QKN_OPT_MAX_GROUPS = 6,     /* 0 = no cap, else cap on workgroup groups */
     QKN_OPT_FORCE_SPLIT = 7,    /* 1 = fused entry points run the split kernels */

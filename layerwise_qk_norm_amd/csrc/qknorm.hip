@@ -702,46 +702,53 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     // (width 5120 split 1, 2, 4 or 8 ways; 5120/1024 split 4 ways), for bf16
     // and E4M3 activations and for LayerNorm, used for batches
     // of at least 4096 tokens when nothing is forced and the device can hold
-    // them; the first fitting entry of a shape is taken.
+    // them; the first fitting entry of a shape is taken. `xcd` 0: the launch
+    // measured fastest with a group's members on different XCDs (narrow shards
+    // and wide splits, where one slow XCD would otherwise hold back every group
+    // placed on it); 1: members on one XCD.
     struct Tuned {
         int dtype, wq, wk, n, v, w, rows, wpc, st;
+        int xcd = 1;
     };
     static const Tuned kTuned[] = {
         // single-tensor tiles first where they measured faster; the mixed-tile
         // entries after them serve when QKN_OPT_TILE_LAYOUT asks for mixed tiles
         {QKN_FMT_BF16, 5120, 5120, 1, 9, 5, 2, 1, 1},
         {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 4, 1, 1},
-        {QKN_FMT_BF16, 1280, 1280, 4, 7, 10, 8, 1, 1},
+        {QKN_FMT_BF16, 1280, 1280, 4, 7, 11, 8, 1, 1, 0},
+        {QKN_FMT_BF16, 640, 640, 8, 6, 8, 3, 3, 0, 0},
         {QKN_FMT_BF16, 640, 640, 8, 9, 3, 8, 2, 1},
         {QKN_FMT_BF16, 5120, 5120, 1, 3, 5, 1, 1, 0},
         {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 2, 1, 0},
         {QKN_FMT_BF16, 1280, 1280, 4, 9, 5, 4, 1, 0},
         {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2, 0},
-        {QKN_FMT_BF16, 1280, 256, 4, 9, 3, 4, 2, 0},
+        {QKN_FMT_BF16, 1280, 256, 4, 8, 2, 2, 4, 0, 0},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 0, 15, 3, 1, 1},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 5, 8, 1, 1},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1, 0},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},
-        {QKN_FMT_E4M3_BF16, 640, 640, 8, 6, 4, 3, 3, 0},
-        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 7, 3, 4, 3, 0},
+        {QKN_FMT_E4M3_BF16, 640, 640, 8, 7, 2, 3, 4, 0, 0},
+        {QKN_FMT_E4M3_BF16, 1280, 256, 4, 7, 3, 4, 3, 0, 0},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 6, 15, 3, 1, 1},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 8, 1, 1},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1, 0},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3, 0},
-        {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4, 0},
+        {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4, 0, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 256, 4, 7, 3, 4, 3, 0},
         {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1, 0},
         {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1, 0},
         {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 10, 4, 1, 0},
+        {QKN_FMT_LN_BF16, 640, 640, 8, 6, 5, 4, 4, 1, 0},
         {QKN_FMT_LN_BF16, 640, 640, 8, 7, 3, 2, 4, 0},
-        {QKN_FMT_LN_BF16, 1280, 256, 4, 6, 12, 4, 2, 0},
+        {QKN_FMT_LN_BF16, 1280, 256, 4, 6, 12, 4, 2, 0, 0},
         {QKN_FMT_LN_F32, 2560, 2560, 2, 9, 5, 1, 2, 0},
     };
     const bool forced = g_opt.force_variant >= 0 || g_opt.rows > 0 || g_opt.force_data_waves > 0 || g_opt.wpc > 0 ||
                         g_opt.tile_layout == 2;
     bool tuned = false;
+    bool tuned_xcd = true;
     if (!forced && T >= 4096) {
         for (const Tuned& t : kTuned) {
             if (t.dtype == dtype && t.wq == Wq && t.wk == Wk && t.n == N &&
@@ -749,6 +756,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
                 consider(t.v, t.w, t.rows, t.wpc, t.st != 0);
             if (best.v >= 0) {  // the first entry that fits the device
                 tuned = true;
+                tuned_xcd = t.xcd != 0;
                 break;
             }
         }
@@ -818,8 +826,11 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     const int64_t n_tiles = tiles_of(rows, best.st);
     int64_t groups = best.wgs / N;
     if (g_opt.max_groups > 0) groups = std::min<int64_t>(groups, g_opt.max_groups);
+    // a group's members share one XCD unless turned off (the option, or the
+    // tuned launch's measurement)
+    const bool want_xcd = g_opt.xcd_map == 1 || (g_opt.xcd_map == -1 && tuned_xcd);
     int xcd = 0;
-    if (g_opt.xcd_map != 0 && groups >= 8) {
+    if (want_xcd && groups >= 8) {
         if (groups < n_tiles) groups -= groups % 8;  // capped: round to whole XCD sets
         xcd = (groups % 8 == 0) ? 1 : 0;
     }

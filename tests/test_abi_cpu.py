@@ -482,3 +482,26 @@ def test_plan_randomised_invariants():
             assert e.status == ops.QKN_ERESIDENCY
             continue
         check_plan(p, dt, T, Hq, Hk, N, cu, bpc)
+
+
+def test_plan_xcd_mapping_follows_the_tuned_launch():
+    """With the option at -1 a tuned launch keeps its measured XCD placement: a
+    group's members on one XCD for the bf16 prefill split two ways, spread over
+    XCDs for GQA and the eight-way splits; 0 and 1 force it either way. (A device
+    roomy enough for every tuned launch.)"""
+    roomy = [[0] + [8] * 15 for _ in range(10)]
+    assert ops.get_option("xcd_map") == -1
+    p = plan("bf16", 16384, 5120, 5120, 2, bpc=roomy)
+    assert p["xcd_map"] == 1 and (p["variant"], p["rows"], p["st"]) == (9, 4, 1), p
+    g = plan("bf16", 8192, 5120, 1024, 4, bpc=roomy)
+    assert g["xcd_map"] == 0 and (g["variant"], g["data_waves"], g["rows"], g["n_groups"]) == (8, 2, 2, 256), g
+    for dt in ("bf16", "e4m3_bf16", "e4m3_e4m3", "ln_bf16"):
+        assert plan(dt, 16384, 5120, 5120, 8, bpc=roomy)["xcd_map"] == 0, dt
+    assert plan("e4m3_e4m3", 8192, 5120, 1024, 4, bpc=roomy)["xcd_map"] == 1
+    try:
+        ops.set_option("xcd_map", 1)
+        assert plan("bf16", 8192, 5120, 1024, 4, bpc=roomy)["xcd_map"] == 1
+        ops.set_option("xcd_map", 0)
+        assert plan("bf16", 16384, 5120, 5120, 2, bpc=roomy)["xcd_map"] == 0
+    finally:
+        ops.set_option("xcd_map", -1)

@@ -724,8 +724,10 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2, 0},
         {QKN_FMT_BF16, 1280, 256, 4, 8, 2, 2, 4, 0, 0},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 0, 15, 3, 1, 1},
+        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 3, 2, 3, 0, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 5, 8, 1, 1},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1, 0},
+        {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 1, 10, 4, 1, 0, 0},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 640, 640, 8, 7, 2, 3, 4, 0, 0},

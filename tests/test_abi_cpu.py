@@ -346,7 +346,8 @@ def test_plan_prefill_shards_use_single_tensor_tiles():
     p = plan("e4m3_e4m3", 16384, 5120, 5120, 4)
     assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["n_groups"]) == (7, 3, 2, 0, 3 * 256 // 4), p
     p = plan("e4m3_bf16", 16384, 5120, 5120, 4)
-    assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["n_groups"]) == (7, 5, 8, 1, 256 // 4), p
+    assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["n_groups"]) == (7, 3, 2, 0, 3 * 256 // 4), p
+    assert p["xcd_map"] == 0, p
     # GQA entries (5120/1024 over 4 shards), retimed with exact workgroups per CU
     for fmt in ("e4m3_bf16", "e4m3_e4m3"):
         p = plan(fmt, 8192, 5120, 1024, 4)
@@ -498,6 +499,8 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
     for dt in ("bf16", "e4m3_bf16", "e4m3_e4m3", "ln_bf16"):
         assert plan(dt, 16384, 5120, 5120, 8, bpc=roomy)["xcd_map"] == 0, dt
     assert plan("e4m3_e4m3", 8192, 5120, 1024, 4, bpc=roomy)["xcd_map"] == 1
+    e = plan("e4m3_bf16", 16384, 5120, 5120, 2, bpc=roomy)
+    assert e["xcd_map"] == 0 and (e["variant"], e["data_waves"], e["rows"]) == (1, 10, 4), e
     try:
         ops.set_option("xcd_map", 1)
         assert plan("bf16", 8192, 5120, 1024, 4, bpc=roomy)["xcd_map"] == 1

@@ -385,7 +385,9 @@ int qknorm_set_option(int key, int64_t value);
 int64_t qknorm_get_option(int key);
 
 /* Bandwidth ceiling for measurements: copies q -> out_q and k -> out_k
- * (bytes_q, bytes_k bytes) with the fused kernel's access widths. */
+ * (bytes_q, bytes_k bytes) with the fused kernel's access widths. Pointers
+ * must be 16-byte aligned; an output overlapping any input or the other
+ * output is QKN_EOVERLAP. */
 int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
                       int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
 

@@ -1768,13 +1768,15 @@ int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k, in
     // a tensor of no bytes may come with a null pointer (empty tensors have none)
     if ((bytes_q && (!q || !out_q)) || (bytes_k && (!k || !out_k))) return QKN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(out_q) || !aligned16(out_k)) return QKN_EINVAL;
+    if (overlaps(range_of(out_q, bytes_q), range_of(q, bytes_q)) ||
+        overlaps(range_of(out_q, bytes_q), range_of(k, bytes_k)) ||
+        overlaps(range_of(out_k, bytes_k), range_of(q, bytes_q)) ||
+        overlaps(range_of(out_k, bytes_k), range_of(k, bytes_k)) ||
+        overlaps(range_of(out_q, bytes_q), range_of(out_k, bytes_k)))
+        return QKN_EOVERLAP;
     const int64_t va = bytes_q / 16, vb = bytes_k / 16;
-    int dev = 0, cu = 0, rc = current_device(&dev);
-    if (rc) return rc;
-    QKN_HIP(hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev));
     const int64_t blocks = std::max<int64_t>(1, (va + 255) / 256 + (vb + 255) / 256);
     if (blocks > 0x7fffffff) return QKN_EINVAL;
-    (void)cu;
     hipLaunchKernelGGL(qkn::copy2_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, k, out_q,
                        out_k, va, vb, bytes_q - va * 16, bytes_k - vb * 16);
     QKN_HIP(hipGetLastError());

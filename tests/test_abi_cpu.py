@@ -160,6 +160,10 @@ def test_split_entry_points_reject_bad_arguments():
     assert L.qknorm_bench_widen(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 0, None) == ops.QKN_OK
     assert L.qknorm_bench_widen(FAKE[0], 0, FAKE[2], 0, 64, 8, None) == ops.QKN_EINVAL
     assert L.qknorm_bench_copy(0, FAKE[1], FAKE[2], FAKE[3], 16, 16, None) == ops.QKN_EINVAL
+    # out_k (64 bytes from FAKE[2] + 48) reaching over out_q's last 16 bytes
+    assert L.qknorm_bench_copy(FAKE[0], FAKE[1], FAKE[2], FAKE[2] + 48, 64, 64, None) == \
+        ops.QKN_EOVERLAP
+    assert L.qknorm_bench_copy(FAKE[0], FAKE[1], FAKE[0], FAKE[3], 64, 64, None) == ops.QKN_EOVERLAP
 
 
 def test_bench_skeleton_rejects_bad_arguments():

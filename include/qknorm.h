@@ -362,7 +362,10 @@ enum {
                                    tiles <= 8) */
     QKN_OPT_XCD_MAP = 4,        /* -1 = planner's choice (a group's members on one XCD,
                                    except for the tuned launches measured faster
-                                   without), 0 = off, 1 = on when possible */
+                                   without and for streaming fp32 shards split
+                                   4-8 ways and bf16 shards split 4 ways with
+                                   rows of at least 1 KiB), 0 = off, 1 = on when
+                                   possible */
     QKN_OPT_COOPERATIVE = 5,    /* 1 = hipLaunchCooperativeKernel, 0 = plain */
     QKN_OPT_MAX_GROUPS = 6,     /* 0 = no cap, else cap on workgroup groups */
     QKN_OPT_FORCE_SPLIT = 7,    /* 1 = fused entry points run the split kernels */

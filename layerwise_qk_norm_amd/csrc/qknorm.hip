@@ -828,9 +828,21 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     const int64_t n_tiles = tiles_of(rows, best.st);
     int64_t groups = best.wgs / N;
     if (g_opt.max_groups > 0) groups = std::min<int64_t>(groups, g_opt.max_groups);
-    // a group's members share one XCD unless turned off (the option, or the
-    // tuned launch's measurement)
-    const bool want_xcd = g_opt.xcd_map == 1 || (g_opt.xcd_map == -1 && tuned_xcd);
+    // a group's members share one XCD unless turned off (the option, the tuned
+    // launch's measurement, or the rule below). Untuned streaming RMSNorm
+    // shapes were timed with members on one XCD and spread (bf16 and fp32,
+    // widths 1024-16384, 4096-65536 tokens, 2-8 shards): spread was faster on
+    // 31 of 32 fp32 shapes split four or eight ways (by up to 14 %; 3 % slower on
+    // the other), and never slower on the 12 bf16 shapes split four ways with
+    // shard rows of at least 1 KiB (up to 10.5 % faster). Narrower bf16 shards
+    // split four ways, bf16 split eight ways and splits of two gained or lost a
+    // few percent from shape to shape (eight ways on one workgroup per CU: 2-5 %
+    // slower spread), and LayerNorm and E4M3 likewise, so they keep one XCD.
+    bool spread = !tuned_xcd;
+    if (!tuned && !forced && !latency_bound && g_opt.xcd_map == -1)
+        spread = (dtype == QKN_FMT_F32 && N >= 4 && N <= 8) ||
+                 (dtype == QKN_FMT_BF16 && N == 4 && std::min(wvq, wvk) * 16 >= 1024);
+    const bool want_xcd = g_opt.xcd_map == 1 || (g_opt.xcd_map == -1 && !spread);
     int xcd = 0;
     if (want_xcd && groups >= 8) {
         if (groups < n_tiles) groups -= groups % 8;  // capped: round to whole XCD sets

@@ -512,3 +512,38 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
         assert plan("bf16", 16384, 5120, 5120, 2, bpc=roomy)["xcd_map"] == 0
     finally:
         ops.set_option("xcd_map", -1)
+
+
+def test_plan_xcd_rule_for_untuned_shapes():
+    """Untuned streaming shapes spread a group's members over XCDs for fp32 split
+    4-8 ways and for bf16 split 4 ways with shard rows of at least 1 KiB; every
+    other untuned shape, latency-bound batches, forced launches and LayerNorm or
+    E4M3 keep them on one XCD; the option still forces either way."""
+    roomy = [[0] + [8] * 15 for _ in range(10)]
+    xm = lambda *a, **kw: plan(*a, bpc=roomy, **kw)["xcd_map"]
+    for T in (4096, 16384, 65536):
+        for H in (1024, 3072, 8192):
+            assert xm("f32", T, H, H, 4) == 0 and xm("f32", T, H, H, 8) == 0, (T, H)
+            assert xm("f32", T, H, H, 2) == 1, (T, H)
+            assert xm("bf16", T, H, H, 2) == 1 and xm("bf16", T, H, H, 8) == 1, (T, H)
+            # bf16 four ways: shard rows of H / 4 * 2 bytes
+            assert xm("bf16", T, H, H, 4) == (0 if H // 4 * 2 >= 1024 else 1), (T, H)
+            for dt in ("ln_bf16", "e4m3_bf16", "e4m3_e4m3"):
+                assert xm(dt, T, H, H, 4) == 1 and xm(dt, T, H, H, 8) == 1, (dt, T, H)
+    # a narrow K shard keeps bf16 on one XCD (K rows of 256 columns = 512 bytes)
+    assert xm("bf16", 16384, 4096, 1024, 4) == 1
+    assert xm("bf16", 16384, 4096, 4096, 4) == 0
+    # latency-bound (decode-sized) batches: one XCD
+    assert xm("f32", 64, 4096, 4096, 4) == 1 and xm("bf16", 64, 4096, 4096, 4) == 1
+    try:
+        ops.set_option("rows", 2)  # a forced launch follows the option alone
+        assert xm("f32", 16384, 3072, 3072, 4) == 1
+    finally:
+        ops.set_option("rows", 0)
+    try:
+        ops.set_option("xcd_map", 1)
+        assert xm("f32", 16384, 3072, 3072, 4) == 1
+        ops.set_option("xcd_map", 0)
+        assert xm("bf16", 16384, 3072, 3072, 2) == 0
+    finally:
+        ops.set_option("xcd_map", -1)

@@ -388,19 +388,22 @@ int qknorm_set_option(int key, int64_t value);
 int64_t qknorm_get_option(int key);
 
 /* Bandwidth ceiling for measurements: copies q -> out_q and k -> out_k
- * (bytes_q, bytes_k bytes) with the fused kernel's access widths. Pointers
- * must be 16-byte aligned; an output overlapping any input or the other
- * output is QKN_EOVERLAP. */
+ * (bytes_q, bytes_k bytes) with a one-shot grid of one-wave workgroups, each
+ * thread moving one 16-byte vector (the fastest simple pattern measured on
+ * this part). Pointers must be 16-byte aligned; an output overlapping any
+ * input or the other output is QKN_EOVERLAP; a tensor above 2^31 - 2^16
+ * bytes is QKN_EINVAL. */
 int qknorm_bench_copy(const void* q, const void* k, void* out_q, void* out_k,
                       int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
 
 /* Bandwidth ceiling for byte mixes that write twice what they read (E4M3
  * inputs with bf16 outputs): every byte of q (bytes_q of them) becomes one
  * 16-bit word of out_q, the byte zero-extended (out_q holds 2 * bytes_q
- * bytes), and likewise k -> out_k. Pointers must be 16-byte aligned; an
- * output overlapping any input or the other output is QKN_EOVERLAP. A
- * tensor of 0 bytes may be passed as a null pointer (also for
- * qknorm_bench_copy). */
+ * bytes), and likewise k -> out_k; one-wave workgroups, each thread loading
+ * 8 bytes and storing 16. Pointers must be 16-byte aligned; an output
+ * overlapping any input or the other output is QKN_EOVERLAP; an output above
+ * 2^31 - 2^16 bytes is QKN_EINVAL. A tensor of 0 bytes may be passed as a
+ * null pointer (also for qknorm_bench_copy). */
 int qknorm_bench_widen(const void* q, const void* k, void* out_q, void* out_k,
                        int64_t bytes_q, int64_t bytes_k, hipStream_t stream);
 

@@ -1,7 +1,7 @@
 // Measurement kernel: the copy skeleton of a fused launch. Kept apart from the
 // fused kernels' source, which it shares nothing with but the helpers it includes.
 #pragma once
-#include "qknorm_kernels.hpp"
+#include "qknorm_ceilings.hpp"
 
 namespace qkn {
 
@@ -152,8 +152,10 @@ skeleton_kernel(SkeletonParams p)
         store_tile(tile_of(k), cur);
         __syncthreads();
         if (more) {
-            // the stores just issued may stay in flight; the loads before them must be done
-            wait_vmcnt<WIDEN ? 2 * VPT : VPT>();
+            // the loads before the stores just issued must be done; as in the
+            // fused kernel, VPT stores may stay in flight (WIDEN: the first VPT
+            // of its 2*VPT stores complete too)
+            wait_vmcnt<VPT>();
 #pragma unroll
             for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
         }

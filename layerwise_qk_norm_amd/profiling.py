@@ -122,7 +122,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_txt: str, cmd_fetch: s
                       title: str = "fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)",
                       plan=None):
     fetch, write = _per_kernel(fetch_csv), _per_kernel(write_csv)
-    copy_name = next(n for n in fetch if "copy2_kernel" in n)
+    copy_name = next(n for n in fetch if "copy_ceiling_kernel" in n)
     fused_name = next(n for n in fetch if kernel in n)
     kib_copy_f = statistics.mean(fetch[copy_name])
     kib_copy_w = statistics.mean(write[copy_name])
@@ -173,7 +173,7 @@ def summarize_sq(csvs, out_txt: str, cmds, kernel: str, title: str):
     for path in csvs:
         per = _counters(path)
         fname = next(n for n in per if kernel in n)
-        cname = next(n for n in per if "copy2_kernel" in n)
+        cname = next(n for n in per if "copy_ceiling_kernel" in n)
         for c, v in per[fname].items():
             fused[c] = statistics.mean(v)
         for c, v in per[cname].items():

@@ -164,6 +164,12 @@ def test_split_entry_points_reject_bad_arguments():
     assert L.qknorm_bench_copy(FAKE[0], FAKE[1], FAKE[2], FAKE[2] + 48, 64, 64, None) == \
         ops.QKN_EOVERLAP
     assert L.qknorm_bench_copy(FAKE[0], FAKE[1], FAKE[0], FAKE[3], 64, 64, None) == ops.QKN_EOVERLAP
+    # one launch each: tensors (widening: outputs) up to 2^31 - 2^16 bytes
+    far = [i << 40 for i in range(1, 5)]
+    big = (1 << 31) - (1 << 16)
+    assert L.qknorm_bench_copy(far[0], far[1], far[2], far[3], big + 16, 16, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_copy(far[0], far[1], far[2], far[3], 16, big + 16, None) == ops.QKN_EINVAL
+    assert L.qknorm_bench_widen(far[0], far[1], far[2], far[3], big // 2 + 8, 8, None) == ops.QKN_EINVAL
 
 
 def test_bench_skeleton_rejects_bad_arguments():

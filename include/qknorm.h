@@ -348,6 +348,11 @@ typedef struct qknorm_plan {
     int xcd_map;        /* 1: members of a group share blockIdx % 8 */
     int iters;          /* tiles per group (ceil(n_tiles / n_groups)) */
     int st;             /* 1: single-tensor tiles; 0: mixed Q+K tiles */
+    int pace_gbs;       /* pacing rate in GB/s (0: none; see QKN_OPT_PACE for the
+                           kernels that have one): no workgroup passes its k-th
+                           barrier before k periods after its start, one period being
+                           the time the whole grid's tile bytes of one iteration take
+                           at that rate (launches of more than two iterations) */
 } qknorm_plan;
 int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
                       int cu_count, const int* blocks_per_cu, int aligned,
@@ -377,6 +382,12 @@ enum {
                                    2 = single-tensor tiles wherever allowed */
     QKN_OPT_WPC = 12,           /* 0 = planner's choice, else workgroups per CU the
                                    planner's search must use (launch timing) */
+    QKN_OPT_PACE = 14,          /* -1 = planner's choice (the tuned launches measured
+                                   faster paced), 0 = no pacing, else a pacing rate in
+                                   GB/s (qknorm_plan.pace_gbs) for launches whose kernel
+                                   has a paced build: bf16 variant 8 on mixed tiles,
+                                   E4M3 -> bf16 variants 0 (single-tensor tiles) and 7
+                                   (mixed), E4M3 -> E4M3 variant 7 (single-tensor) */
     QKN_OPT_STATIC_SLOTS = 13,  /* test hook: 0 = the no-allocation call may use all of
                                    its static slots, else at most this many (so that
                                    QKN_ESCRATCH can be exercised) */

@@ -207,6 +207,21 @@ FusedFn fused_fn_layout(int fmt, int v, bool st)
     default: return fused_fn_st<F32, 1>(v);
     }
 }
+// Paced builds (PACE = true) of the kernels the tuned table
+// paces: bf16 variant 8 on mixed tiles (GQA), E4M3 -> bf16 variant 0 on
+// single-tensor tiles and 7 on mixed tiles, E4M3 -> E4M3 variant 7 on
+// single-tensor tiles; nullptr for every other kernel, which runs unpaced.
+FusedFn paced_fn(int fmt, int v, bool st)
+{
+    if (fmt == QKN_FMT_BF16 && v == 8 && !st) return qkn::fused_qknorm_kernel<Bf16, 3, true, 2, 768, 0, false, true>;
+    if (fmt == QKN_FMT_E4M3_BF16 && v == 0 && st)
+        return qkn::fused_qknorm_kernel<E4m3Bf16, 1, true, 1, kE4m3MaxThreads[0], 0, true, true>;
+    if (fmt == QKN_FMT_E4M3_BF16 && v == 7 && !st)
+        return qkn::fused_qknorm_kernel<E4m3Bf16, 2, true, 2, kE4m3MaxThreads[7], 0, false, true>;
+    if (fmt == QKN_FMT_E4M3_E4M3 && v == 7 && st)
+        return qkn::fused_qknorm_kernel<E4m3E4m3, 2, true, 2, kE4m3MaxThreads[7], 0, true, true>;
+    return nullptr;
+}
 // Measurement ceilings: threads per workgroup of the one-shot copy and
 // widening kernels (each thread moves one vector; one wave per workgroup
 // measured fastest for both: 100.8 against 103.4 us with four waves for the
@@ -283,6 +298,7 @@ struct Options {
     int64_t split_vectors = 0;
     int64_t tile_layout = 0;
     int64_t wpc = 0;
+    int64_t pace_gbs = -1;
 };
 Options g_opt;
 
@@ -717,6 +733,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     struct Tuned {
         int dtype, wq, wk, n, v, w, rows, wpc, st;
         int xcd = 1;
+        int pace = 0;  // pacing rate in GB/s measured faster than none (0: none)
     };
     static const Tuned kTuned[] = {
         // single-tensor tiles first where they measured faster; the mixed-tile
@@ -730,18 +747,18 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 2, 1, 0},
         {QKN_FMT_BF16, 1280, 1280, 4, 9, 5, 4, 1, 0},
         {QKN_FMT_BF16, 640, 640, 8, 9, 3, 4, 2, 0},
-        {QKN_FMT_BF16, 1280, 256, 4, 8, 2, 2, 4, 0, 0},
-        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 0, 15, 3, 1, 1},
-        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 3, 2, 3, 0, 0},
+        {QKN_FMT_BF16, 1280, 256, 4, 8, 2, 2, 4, 0, 0, 6700},
+        {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 0, 15, 3, 1, 1, 1, 6600},
+        {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 3, 2, 3, 0, 0, 6600},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 5, 8, 1, 1},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1, 0},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 1, 10, 4, 1, 0, 0},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},
-        {QKN_FMT_E4M3_BF16, 640, 640, 8, 7, 2, 3, 4, 0, 0},
+        {QKN_FMT_E4M3_BF16, 640, 640, 8, 7, 2, 3, 4, 0, 0, 6600},
         {QKN_FMT_E4M3_BF16, 1280, 256, 4, 7, 3, 4, 3, 0, 0},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 6, 15, 3, 1, 1},
-        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 8, 1, 1},
+        {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 8, 1, 1, 1, 6600},
         {QKN_FMT_E4M3_E4M3, 5120, 5120, 1, 1, 15, 3, 1, 0},
         {QKN_FMT_E4M3_E4M3, 2560, 2560, 2, 7, 10, 4, 1, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 1280, 4, 7, 3, 2, 3, 0},
@@ -759,6 +776,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
                         g_opt.tile_layout == 2;
     bool tuned = false;
     bool tuned_xcd = true;
+    int tuned_pace = 0;
     if (!forced && T >= 4096) {
         for (const Tuned& t : kTuned) {
             if (t.dtype == dtype && t.wq == Wq && t.wk == Wk && t.n == N &&
@@ -767,6 +785,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
             if (best.v >= 0) {  // the first entry that fits the device
                 tuned = true;
                 tuned_xcd = t.xcd != 0;
+                tuned_pace = t.pace;
                 break;
             }
         }
@@ -868,7 +887,26 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     out->xcd_map = xcd;
     out->iters = (int)((n_tiles + groups - 1) / groups);
     out->st = best.st ? 1 : 0;
+    // pacing: the tuned launch's measured rate unless the option sets one (0: off),
+    // for kernels with a paced build
+    out->pace_gbs = !paced_fn(dtype, best.v, best.st) ? 0
+                    : g_opt.pace_gbs >= 0           ? (int)g_opt.pace_gbs
+                    : tuned                         ? tuned_pace
+                                                    : 0;
     return QKN_OK;
+}
+
+// Pacing period of a fused launch in 1/256 wall-clock ticks per iteration: the
+// time the whole grid's bytes of one iteration (one tile's loads and stores per
+// workgroup) take at the plan's pacing rate; 0 when the plan has none or runs
+// two iterations or fewer.
+uint32_t pace_period(const qknorm_plan& pl, int wv_q, int wv_k, const Fmt& f, int wall_khz)
+{
+    if (pl.pace_gbs <= 0 || pl.iters <= 2) return 0;
+    const double tile_in = (double)pl.rows * (pl.st ? (double)wv_q : (double)(wv_q + wv_k)) * 16.0;
+    const double per_iter = (double)pl.grid * tile_in * (1.0 + (double)f.out / (double)f.in);
+    const double ticks = per_iter / ((double)pl.pace_gbs * 1e9) * (double)wall_khz * 1e3;
+    return (uint32_t)std::min(ticks * 256.0, 4.0e9);
 }
 
 // ---------------------------------------------------------------- split launches
@@ -1342,9 +1380,10 @@ int layerwise_fwd(int dtype, const void* q, const void* k, const void* gq, const
     p.spin_ticks = ticks < 1.0 ? 1 : (uint64_t)ticks;
     p.test_flags = g_opt.test_skip_publish ? 1u : 0u;
     p.nq = pl.st ? (T + pl.rows - 1) / pl.rows : 0;
+    p.pace = pace_period(pl, p.Wv[0], p.Wv[1], f, di->wall_khz);
     *tag_base += (uint32_t)pl.iters;
 
-    FusedFn fn = fused_fn_layout(dtype, pl.variant, pl.st != 0);
+    FusedFn fn = p.pace ? paced_fn(dtype, pl.variant, pl.st != 0) : fused_fn_layout(dtype, pl.variant, pl.st != 0);
     if (!fn) return QKN_EINVAL;
     const size_t lds = gamma_lds_bytes(dtype, pl.variant, pl.data_waves, pl.st != 0);
     if (g_opt.cooperative) {
@@ -1752,6 +1791,9 @@ int qknorm_set_option(int key, int64_t value)
     case QKN_OPT_WPC:
         if (value < 0 || value > 64) return QKN_EINVAL;
         g_opt.wpc = value; return QKN_OK;
+    case QKN_OPT_PACE:
+        if (value < -1 || value > 100000) return QKN_EINVAL;
+        g_opt.pace_gbs = value; return QKN_OK;
     case QKN_OPT_STATIC_SLOTS:
         if (value < 0 || (uint64_t)value > kStaticSlots) return QKN_EINVAL;
         g_static_slot_limit = (size_t)value; return QKN_OK;
@@ -1774,6 +1816,7 @@ int64_t qknorm_get_option(int key)
     case QKN_OPT_SPLIT_VECTORS: return g_opt.split_vectors;
     case QKN_OPT_TILE_LAYOUT: return g_opt.tile_layout;
     case QKN_OPT_WPC: return g_opt.wpc;
+    case QKN_OPT_PACE: return g_opt.pace_gbs;
     case QKN_OPT_STATIC_SLOTS: return (int64_t)g_static_slot_limit;
     default: return INT64_MIN;
     }
@@ -1875,6 +1918,7 @@ int qknorm_bench_skeleton(int dtype, const void* q, const void* k, void* out_q, 
     p.n_groups = pl.n_groups;
     p.xcd_map = pl.xcd_map;
     p.in_bytes = f.in;
+    p.pace = pace_period(pl, p.Wv[0], p.Wv[1], f, di->wall_khz);
     hipLaunchKernelGGL(fn, dim3(pl.grid), dim3(pl.threads), 0, stream, p);
     QKN_HIP(hipGetLastError());
     return QKN_OK;

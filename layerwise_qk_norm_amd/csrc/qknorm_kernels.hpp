@@ -108,7 +108,8 @@ __device__ __forceinline__ void unpack(E4m3E4m3, const u32x4& v, float* f) { unp
 
 // fp32 -> E4M3: round to nearest even by the hardware converter, after
 // saturating magnitudes above 448 (infinities included) to +-448. The converter
-// itself turns magnitudes of 480 and more into NaN, so the clamp is needed. It
+// itself rounds magnitudes above 464 to 480, which it encodes as NaN (as it does
+// infinities), so the clamp is needed. It
 // uses the NaN-propagating maximum and minimum of IEEE 754-2019 (one
 // v_maximum3_f32 and one v_minimum3_f32 on gfx950, no lane mask), so NaN stays
 // NaN and -0 stays -0.
@@ -266,6 +267,7 @@ struct FusedParams {
     uint64_t spin_ticks;   // wall-clock ticks a comm wave may wait for one tile
     uint32_t test_flags;   // bit 0: never publish (forces the timeout path)
     int64_t nq;            // single-tensor tiles: tiles 0..nq-1 hold Q rows, nq..n_tiles-1 K rows
+    uint32_t pace;         // pacing period in 1/256 wall-clock ticks per iteration (0: none)
 };
 
 // Workgroup = 1 comm wave (wave 0) + p.nwd data waves. Every workgroup owns
@@ -303,7 +305,11 @@ struct FusedParams {
 // partners without waiting, and the exchange overlaps the loads of the next
 // tiles and the products x*gamma. u is held for LAG tiles; the slot ring is
 // 2*LAG deep; red and rinv_s are double-buffered by tile parity.
-template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT, int NORM = 0, bool ST = false>
+//
+// PACE: the comm wave holds barrier k until k pacing periods (p.pace) after its
+// workgroup's start; no other step changes. Only the kernels of the launches
+// measured faster paced are built with it.
+template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT, int NORM = 0, bool ST = false, bool PACE = false>
 __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
@@ -365,6 +371,7 @@ fused_qknorm_kernel(FusedParams p)
         bool abandon = false;
         constexpr int RING = 2 * LAG;  // slot ring depth
         float own0 = 0.f, own1 = 0.f;  // own partials of the last tiles (even, odd)
+        const uint64_t t_entry = PACE ? wall_clock64() : 0;
         for (int k = 0; k < K + LAG; ++k) {
             if (k >= LAG) {
                 // ---- Phase B comm path for tile k-LAG ---------------------------
@@ -414,6 +421,13 @@ fused_qknorm_kernel(FusedParams p)
                         mu_s[j & 1][lane] = mu;
                     }
                 }
+            }
+            if constexpr (PACE) {
+                // pacing: barrier k opens no earlier than k periods after this
+                // workgroup's start, so no group runs ahead of the pace (the wait
+                // ends: the last due time is K + LAG - 1 periods after the start)
+                const uint64_t due = t_entry + (((uint64_t)k * p.pace) >> 8);
+                while (wall_clock64() < due) __builtin_amdgcn_s_sleep(1);
             }
             __syncthreads();  // red[k&1] written; rinv_s[(k-LAG)&1] ready
             if (k < K && mine) {

@@ -9,8 +9,8 @@ namespace qkn {
 
 // Copy skeleton of a fused launch: the fused kernel's grid, workgroups (one
 // wave that only passes the barriers plus `nwd` data waves), group and shard
-// mapping, slot layout, tile stride loop, one barrier per iteration and
-// one-tile prefetch, with no arithmetic and no exchange: each tile's bytes of
+// mapping, slot layout, tile stride loop, one barrier per iteration, pacing
+// and one-tile prefetch, with no arithmetic and no exchange: each tile's bytes of
 // x are stored unchanged to y (WIDEN: each byte zero-extended to a 16-bit
 // word, the byte mix of E4M3 inputs with bf16 outputs). It measures what the
 // persistent streaming structure itself can move.
@@ -24,6 +24,7 @@ struct SkeletonParams {
     int32_t Wv[2];     // shard widths in 16-byte vectors of x
     int32_t rows, nwd, n_shards, n_groups, xcd_map;
     int32_t in_bytes;  // element size of x
+    uint32_t pace;     // the fused launch's pacing period (1/256 wall-clock ticks; 0: none)
 };
 
 template <int VPT, bool ST, bool WIDEN>
@@ -50,7 +51,15 @@ skeleton_kernel(SkeletonParams p)
     const int K = p.n_tiles > group ? (int)((p.n_tiles - 1 - group) / p.n_groups + 1) : 0;
     if (K == 0) return;
     if (wave == 0) {
-        for (int k = 0; k <= K; ++k) __syncthreads();
+        // passes the barriers, paced as the fused kernel's comm wave paces them
+        const uint64_t t_entry = p.pace ? wall_clock64() : 0;
+        for (int k = 0; k <= K; ++k) {
+            if (p.pace) {
+                const uint64_t due = t_entry + (((uint64_t)k * p.pace) >> 8);
+                while (wall_clock64() < due) __builtin_amdgcn_s_sleep(1);
+            }
+            __syncthreads();
+        }
         return;
     }
     const int dwave = wave - 1;

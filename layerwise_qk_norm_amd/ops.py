@@ -29,7 +29,7 @@ MAX_DATA_WAVES = 15
 MAX_SHARDS = 64
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,
        "max_groups": 6, "force_split": 7, "test_skip_publish": 8, "data_waves": 9,
-       "split_vectors": 10, "tile_layout": 11, "wpc": 12, "static_slots": 13}
+       "split_vectors": 10, "tile_layout": 11, "wpc": 12, "static_slots": 13, "pace": 14}
 
 
 class QKNormError(RuntimeError):
@@ -47,7 +47,7 @@ class Plan(ctypes.Structure):
                 ("data_waves", ctypes.c_int), ("slots", ctypes.c_int),
                 ("rows", ctypes.c_int), ("n_tiles", ctypes.c_int64), ("n_groups", ctypes.c_int),
                 ("grid", ctypes.c_int), ("xcd_map", ctypes.c_int), ("iters", ctypes.c_int),
-                ("st", ctypes.c_int)]
+                ("st", ctypes.c_int), ("pace_gbs", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -226,7 +226,7 @@ def main():
     q.add_argument("out_txt")
     q.add_argument("csvs", nargs="+")
     q.add_argument("--cmd", action="append", required=True)
-    q.add_argument("--kernel", default="fused_qknorm_kernel<qkn::Bf16, 4, true, 2, 512, 0, true>")
+    q.add_argument("--kernel", default="fused_qknorm_kernel<qkn::Bf16, 4, true, 2, 512, 0, true, false>")
     q.add_argument("--title", default="fused prefill kernel (T=16384, Q and K width 5120, bf16, N=2)")
     a = ap.parse_args()
     if a.what == "sq":

@@ -520,6 +520,49 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
         ops.set_option("xcd_map", -1)
 
 
+def test_plan_pace_follows_the_tuned_launch():
+    """Tuned launches measured faster paced carry their pacing rate in the plan
+    (bf16 GQA 6700 GB/s; E4M3 -> bf16 split 1, 4 and 8 ways and E4M3 -> E4M3 split
+    2 ways 6600 GB/s); every other launch, forced launches included, has none
+    unless the option sets a rate and its kernel has a paced build; 0 turns pacing
+    off."""
+    roomy = [[0] + [8] * 15 for _ in range(10)]
+    pace = lambda *a: plan(*a, bpc=roomy)["pace_gbs"]
+    assert ops.get_option("pace") == -1
+    assert pace("bf16", 8192, 5120, 1024, 4) == 6700
+    for N in (1, 4, 8):
+        assert pace("e4m3_bf16", 16384, 5120, 5120, N) == 6600, N
+    assert pace("e4m3_e4m3", 16384, 5120, 5120, 2) == 6600
+    for dt, N in (("bf16", 1), ("bf16", 2), ("bf16", 4), ("bf16", 8), ("e4m3_bf16", 2), ("e4m3_e4m3", 1),
+                  ("e4m3_e4m3", 4), ("e4m3_e4m3", 8), ("ln_bf16", 2)):
+        assert pace(dt, 16384, 5120, 5120, N) == 0, (dt, N)
+    assert pace("bf16", 16384, 3072, 3072, 4) == 0 and pace("f32", 16384, 8192, 8192, 8) == 0
+    assert pace("bf16", 64, 4096, 4096, 4) == 0
+    try:
+        # a forced launch is not the tuned one, even on the tuned launch's kernel
+        for n, v in (("force_variant", 8), ("data_waves", 2), ("rows", 2), ("tile_layout", 1)):
+            ops.set_option(n, v)
+        assert plan("bf16", 8192, 5120, 1024, 4, bpc=roomy)["variant"] == 8
+        assert pace("bf16", 8192, 5120, 1024, 4) == 0
+        ops.set_option("pace", 7000)
+        assert pace("bf16", 8192, 5120, 1024, 4) == 7000
+    finally:
+        for n, v in (("force_variant", -1), ("data_waves", 0), ("rows", 0), ("tile_layout", 0)):
+            ops.set_option(n, v)
+    try:
+        ops.set_option("pace", 0)
+        assert pace("bf16", 8192, 5120, 1024, 4) == 0
+        ops.set_option("pace", 5000)
+        assert pace("bf16", 8192, 5120, 1024, 4) == 5000
+        assert pace("e4m3_e4m3", 16384, 5120, 5120, 2) == 5000
+        # kernels without a paced build run unpaced whatever the option says
+        assert pace("bf16", 16384, 3072, 3072, 2) == 0 and pace("bf16", 16384, 5120, 5120, 2) == 0
+        for bad in (-2, 100001):
+            assert ops.lib().qknorm_set_option(ops.OPT["pace"], bad) == ops.QKN_EINVAL
+    finally:
+        ops.set_option("pace", -1)
+
+
 def test_plan_xcd_rule_for_untuned_shapes():
     """Untuned streaming shapes spread a group's members over XCDs for fp32 split
     4-8 ways and for bf16 split 4 ways with shard rows of at least 1 KiB; every

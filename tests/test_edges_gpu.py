@@ -537,6 +537,61 @@ def test_bench_skeleton_moves_every_byte(fmt, T, Hq, Hk, N, layout):
             assert torch.equal(y.contiguous().view(torch.uint8), xb), (fmt, T, Hq, Hk, N, layout)
 
 
+@pytest.mark.parametrize("fmt,T,Hq,Hk,N,rate", [
+    ("bf16", 8192, 5120, 1024, 4, -1),      # the tuned GQA launch, paced by default
+    ("bf16", 4096, 5120, 1024, 4, 4000),    # a rate below the launch's own: barriers held
+    ("e4m3_bf16", 4096, 5120, 5120, 4, -1),
+    ("e4m3_bf16", 4099, 5120, 5120, 1, 4000),
+    ("e4m3_bf16", 8192, 5120, 5120, 8, -1),
+    ("e4m3_e4m3", 4096, 5120, 5120, 2, -1),
+])
+def test_pacing_changes_no_output(fmt, T, Hq, Hk, N, rate):
+    """Pacing only holds barriers: a paced launch's outputs are bitwise those of the
+    unpaced one, no exchange times out, and the paced launch skeleton still stores
+    every byte."""
+    g = torch.Generator(device=DEV).manual_seed(T + Hq + N)
+    e4 = fmt.startswith("e4m3")
+    tin = torch.float8_e4m3fn if e4 else (torch.float32 if fmt == "f32" else torch.bfloat16)
+    tout = torch.float8_e4m3fn if fmt == "e4m3_e4m3" else (torch.bfloat16 if e4 else tin)
+    tg = torch.bfloat16 if e4 else tin
+    q = (torch.randn(T, Hq, generator=g, device=DEV) * 2).to(tin)
+    k = (torch.randn(T, Hk, generator=g, device=DEV) * 2).to(tin)
+    gq = (torch.rand(Hq, generator=g, device=DEV) + 0.5).to(tg)
+    gk = (torch.rand(Hk, generator=g, device=DEV) + 0.5).to(tg)
+
+    def run():
+        oq = torch.empty(T, Hq, dtype=tout, device=DEV)
+        ok = torch.empty(T, Hk, dtype=tout, device=DEV)
+        if fmt.startswith("ln"):
+            ops.layernorm_fwd(q, k, gq, gk, N, 1e-6, beta_q=gq, beta_k=gk, out_q=oq, out_k=ok)
+        else:
+            ops.layerwise_fwd(q, k, gq, gk, N, 1e-6, out_q=oq, out_k=ok)
+        torch.cuda.synchronize()
+        assert ops.check_fault() == ops.QKN_OK
+        return oq.view(torch.uint8), ok.view(torch.uint8)
+
+    ops.set_option("pace", 0)
+    assert ops.current_plan(fmt, T, Hq, Hk, N)["pace_gbs"] == 0
+    ref = run()
+    ops.set_option("pace", rate)
+    p = ops.current_plan(fmt, T, Hq, Hk, N)
+    assert p["pace_gbs"] > 0 and p["iters"] > 2, p
+    for _ in range(3):
+        got = run()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), (fmt, T, Hq, Hk, N)
+    # the skeleton of the paced launch moves every byte
+    sq, sk = torch.empty_like(q), torch.empty_like(k)
+    if fmt == "e4m3_bf16":
+        sq, sk = torch.empty(T, Hq, dtype=torch.bfloat16, device=DEV), torch.empty(T, Hk, dtype=torch.bfloat16, device=DEV)
+    ops.bench_skeleton(q, k, sq, sk, N, fmt)
+    torch.cuda.synchronize()
+    for x, y in ((q, sq), (k, sk)):
+        if fmt == "e4m3_bf16":
+            assert torch.equal(y.view(torch.int16).to(torch.int32) & 0xffff, x.view(torch.uint8).to(torch.int32))
+        else:
+            assert torch.equal(y.view(torch.uint8), x.view(torch.uint8))
+
+
 def test_bench_skeleton_refuses_split_shapes():
     # shard widths that are not whole vectors run the split kernels: no fused plan to mirror
     q = torch.zeros((8, 100), dtype=torch.bfloat16, device=DEV)

@@ -334,7 +334,7 @@ int qknorm_release_workspace(void);
  * Here the single-tensor kernels are taken to occupy the device like the mixed
  * ones (the real path queries both).
  * `dtype` is a format (QKN_FMT_*). */
-#define QKN_NUM_VARIANTS 10
+#define QKN_NUM_VARIANTS 11
 #define QKN_MAX_DATA_WAVES 15
 typedef struct qknorm_plan {
     int variant;        /* fused kernel variant, or -1: shape uses the split kernels */

@@ -17,6 +17,7 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "qknorm_kernels.hpp"
@@ -80,6 +81,10 @@ constexpr Variant kVariants[QKN_NUM_VARIANTS] = {
     {2, true, 2, 1024},
     {3, true, 2, 768},
     {4, true, 2, 512},
+    // bf16 only: four data waves and the comm wave, one wave per SIMD, so no
+    // SIMD runs two data waves' arithmetic (reached through the tuned table or
+    // QKN_OPT_FORCE_VARIANT, not the scored search)
+    {5, true, 2, 320},
 };
 
 using FusedFn = void (*)(FusedParams);
@@ -101,6 +106,9 @@ FusedFn fused_fn(int v)
     case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024>;
     case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768>;
     case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512>;
+    case 10:
+        if constexpr (std::is_same<DT, Bf16>::value) return qkn::fused_qknorm_kernel<DT, 5, true, 2, 320>;
+        return nullptr;
     default: return nullptr;
     }
 }
@@ -122,7 +130,7 @@ FusedFn fused_fn<F32>(int v)
     }
 }
 // E4M3 launch bounds: variants 2 and 7 need more registers than 1024 threads allow
-constexpr int kE4m3MaxThreads[QKN_NUM_VARIANTS] = {1024, 1024, 768, 0, 0, 0, 1024, 768, 0, 0};
+constexpr int kE4m3MaxThreads[QKN_NUM_VARIANTS] = {1024, 1024, 768, 0, 0, 0, 1024, 768, 0, 0, 0};
 template <class DT>
 FusedFn fused_fn_e4m3(int v)
 {
@@ -179,6 +187,10 @@ FusedFn fused_fn_st(int v)
     case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024, NORM, true>;
     case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768, NORM, true>;
     case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512, NORM, true>;
+    case 10:
+        if constexpr (std::is_same<DT, Bf16>::value && NORM == 0)
+            return qkn::fused_qknorm_kernel<DT, 5, true, 2, 320, NORM, true>;
+        return nullptr;
     default: return nullptr;
     }
 }
@@ -213,13 +225,15 @@ FusedFn fused_fn_layout(int fmt, int v, bool st)
 // single-tensor tiles; nullptr for every other kernel, which runs unpaced.
 FusedFn paced_fn(int fmt, int v, bool st)
 {
-    if (fmt == QKN_FMT_BF16 && v == 8 && !st) return qkn::fused_qknorm_kernel<Bf16, 3, true, 2, 768, 0, false, true>;
+    if (fmt == QKN_FMT_BF16 && v == 9 && st) return qkn::fused_qknorm_kernel<Bf16, 4, true, 2, 512, 0, true, 2>;
+    if (fmt == QKN_FMT_BF16 && v == 10 && st) return qkn::fused_qknorm_kernel<Bf16, 5, true, 2, 320, 0, true, 2>;
+    if (fmt == QKN_FMT_BF16 && v == 8 && !st) return qkn::fused_qknorm_kernel<Bf16, 3, true, 2, 768, 0, false, 1>;
     if (fmt == QKN_FMT_E4M3_BF16 && v == 0 && st)
-        return qkn::fused_qknorm_kernel<E4m3Bf16, 1, true, 1, kE4m3MaxThreads[0], 0, true, true>;
+        return qkn::fused_qknorm_kernel<E4m3Bf16, 1, true, 1, kE4m3MaxThreads[0], 0, true, 1>;
     if (fmt == QKN_FMT_E4M3_BF16 && v == 7 && !st)
-        return qkn::fused_qknorm_kernel<E4m3Bf16, 2, true, 2, kE4m3MaxThreads[7], 0, false, true>;
+        return qkn::fused_qknorm_kernel<E4m3Bf16, 2, true, 2, kE4m3MaxThreads[7], 0, false, 1>;
     if (fmt == QKN_FMT_E4M3_E4M3 && v == 7 && st)
-        return qkn::fused_qknorm_kernel<E4m3E4m3, 2, true, 2, kE4m3MaxThreads[7], 0, true, true>;
+        return qkn::fused_qknorm_kernel<E4m3E4m3, 2, true, 2, kE4m3MaxThreads[7], 0, true, 1>;
     return nullptr;
 }
 // Measurement ceilings: threads per workgroup of the one-shot copy and
@@ -239,6 +253,7 @@ SkelFn skeleton_fn_vpt(int vpt)
     case 2: return qkn::skeleton_kernel<2, ST, WIDEN>;
     case 3: return qkn::skeleton_kernel<3, ST, WIDEN>;
     case 4: return WIDEN ? nullptr : qkn::skeleton_kernel<4, ST, false>;
+    case 5: return WIDEN ? nullptr : qkn::skeleton_kernel<5, ST, false>;
     case 6: return WIDEN ? nullptr : qkn::skeleton_kernel<6, ST, false>;
     case 9: return WIDEN ? nullptr : qkn::skeleton_kernel<9, ST, false>;
     default: return nullptr;
@@ -251,6 +266,8 @@ SkelFn skeleton_fn(int vpt, bool st, bool widen)
     return widen ? skeleton_fn_vpt<false, true>(vpt) : skeleton_fn_vpt<false, false>(vpt);
 }
 bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
+// paced builds on the staggered schedule (PACE = 2)
+bool paced_staggered(int fmt, int v, bool st) { return fmt == QKN_FMT_BF16 && st && (v == 9 || v == 10); }
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
 // data waves a workgroup of variant v may have (launch bound / 64, minus the comm wave)
 int max_data_waves(int fmt, int v)
@@ -661,6 +678,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         const Variant& k = kVariants[v];
         if (!variant_usable(dtype, v)) return false;
         if (g_opt.force_variant >= 0) return v == g_opt.force_variant;
+        if (v == 10) return false;
         return N > 1 || k.lag == 1;
     };
     const Fmt fm = fmt_of(dtype);
@@ -739,6 +757,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         // single-tensor tiles first where they measured faster; the mixed-tile
         // entries after them serve when QKN_OPT_TILE_LAYOUT asks for mixed tiles
         {QKN_FMT_BF16, 5120, 5120, 1, 9, 5, 2, 1, 1},
+        {QKN_FMT_BF16, 2560, 2560, 2, 10, 4, 4, 1, 1, 1, 7100},
         {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 4, 1, 1},
         {QKN_FMT_BF16, 1280, 1280, 4, 7, 11, 8, 1, 1, 0},
         {QKN_FMT_BF16, 640, 640, 8, 6, 8, 3, 3, 0, 0},
@@ -1919,6 +1938,7 @@ int qknorm_bench_skeleton(int dtype, const void* q, const void* k, void* out_q, 
     p.xcd_map = pl.xcd_map;
     p.in_bytes = f.in;
     p.pace = pace_period(pl, p.Wv[0], p.Wv[1], f, di->wall_khz);
+    p.stagger = p.pace && paced_staggered(dtype, pl.variant, pl.st != 0) ? 1u : 0u;
     hipLaunchKernelGGL(fn, dim3(pl.grid), dim3(pl.threads), 0, stream, p);
     QKN_HIP(hipGetLastError());
     return QKN_OK;

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace qkn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -238,6 +240,36 @@ __device__ __forceinline__ float wave_sum(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// wave_sum of M values at once, each reduced over the same fixed tree as
+// wave_sum (so each result is bitwise that of wave_sum), with the steps of the
+// M reductions interleaved: the M dependency chains overlap instead of
+// running one after the other.
+template <int M>
+__device__ __forceinline__ void wave_sum_n(float (&v)[M], float (&out)[M])
+{
+#define QKN_DPP(x, ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false))
+#define QKN_DPP_ROWS(x, ctrl, rows) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rows, 0xF, false))
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] += QKN_DPP(v[m], 0xB1);
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] += QKN_DPP(v[m], 0x4E);
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] += QKN_DPP(v[m], 0x141);
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] += QKN_DPP(v[m], 0x140);
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] += QKN_DPP_ROWS(v[m], 0x142, 0xA);
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] += QKN_DPP_ROWS(v[m], 0x143, 0xC);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        out[m] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[m]), 63));
+#undef QKN_DPP_ROWS
+#undef QKN_DPP
+}
+
 // ================================================================ fused kernel
 
 constexpr int kMaxDataWaves = 15;  // data waves per workgroup (plus one comm wave)
@@ -309,10 +341,18 @@ struct FusedParams {
 // PACE: the comm wave holds barrier k until k pacing periods (p.pace) after its
 // workgroup's start; no other step changes. Only the kernels of the launches
 // measured faster paced are built with it.
-template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT, int NORM = 0, bool ST = false, bool PACE = false>
+template <class DT, int VPT, bool PREFETCH, int LAG, int MAXT, int NORM = 0, bool ST = false, int PACE = 0>
 __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
+    // PACE 2 builds run on the staggered schedule, where the data waves' work
+    // per tile is on the critical path of every iteration: Phase A reduces all
+    // of a wave's slots side by side, and the two tile buffers alternate
+    // instead of being copied. The results are bitwise those of the other
+    // builds.
+    constexpr bool LEAN = PACE == 2;
+    static_assert(PACE != 2 || (std::is_same<DT, Bf16>::value && NORM == 0 && LAG == 2 && PREFETCH),
+                  "staggered pacing is built for bf16 RMSNorm with a two-tile lag");
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     constexpr int EV = DT::kVec;
@@ -371,7 +411,7 @@ fused_qknorm_kernel(FusedParams p)
         bool abandon = false;
         constexpr int RING = 2 * LAG;  // slot ring depth
         float own0 = 0.f, own1 = 0.f;  // own partials of the last tiles (even, odd)
-        const uint64_t t_entry = PACE ? wall_clock64() : 0;
+        uint64_t t_entry = PACE ? wall_clock64() : 0;
         for (int k = 0; k < K + LAG; ++k) {
             if (k >= LAG) {
                 // ---- Phase B comm path for tile k-LAG ---------------------------
@@ -425,11 +465,19 @@ fused_qknorm_kernel(FusedParams p)
             if constexpr (PACE) {
                 // pacing: barrier k opens no earlier than k periods after this
                 // workgroup's start, so no group runs ahead of the pace (the wait
-                // ends: the last due time is K + LAG - 1 periods after the start)
-                const uint64_t due = t_entry + (((uint64_t)k * p.pace) >> 8);
-                while (wall_clock64() < due) __builtin_amdgcn_s_sleep(1);
+                // ends: the last due time is K + LAG - 1 periods after the start).
+                // Staggered: k periods after the group passed barrier 0 (its
+                // phase is in its start), and the drain barriers (k >= K, no
+                // loads left) are not held.
+                if (PACE == 1 || (k >= 1 && k < K)) {
+                    const uint64_t due = t_entry + (((uint64_t)k * p.pace) >> 8);
+                    while (wall_clock64() < due) __builtin_amdgcn_s_sleep(1);
+                }
             }
             __syncthreads();  // red[k&1] written; rinv_s[(k-LAG)&1] ready
+            if constexpr (PACE == 2) {
+                if (k == 0) t_entry = wall_clock64();
+            }
             if (k < K && mine) {
                 // ---- publish the partial of tile k (after acquiring tile k-LAG:
                 // a peer reads tile k-2*LAG before it publishes tile k-LAG, so a
@@ -458,6 +506,11 @@ fused_qknorm_kernel(FusedParams p)
     // prefetched tile can be consumed while the previous tile's stores are still
     // in flight.
     const int dwave = wave - 1;
+    // staggered pacing: this group's first loads go out one period plus its
+    // phase (group / n_groups of a period) after entry, gamma staging included
+    const uint64_t t_start = PACE == 2
+                                 ? wall_clock64() + (((uint64_t)p.pace + (uint64_t)group * p.pace / (uint64_t)p.n_groups) >> 8)
+                                 : 0;
     const int ndt = 64 * nwd;  // data threads
     const int dt = tid - 64;
     const int VQ = rows * p.Wv[0];
@@ -582,6 +635,19 @@ fused_qknorm_kernel(FusedParams p)
         }
     }
 
+    // Whether every slot of this wave lies in one segment (the usual case: a
+    // shard row is a multiple of 64 vectors), and the segment of each slot as a
+    // wave-uniform value. Phase A then reduces all slots side by side.
+    int segu[VPT];
+    bool uni = LEAN;
+    if constexpr (LEAN) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            segu[i] = __builtin_amdgcn_readfirstlane(seg[i]);
+            uni = uni && segu[i] == __builtin_amdgcn_readlane(seg[i], 63);
+        }
+    }
+
     // E4M3 outputs: whether this wave saturates before converting (set below,
     // once the first tile's loads are in flight)
     bool sat = true;
@@ -630,6 +696,37 @@ fused_qknorm_kernel(FusedParams p)
     // finished segment (segments the wave does not touch stay 0).
     auto phase_a = [&](const u32x4 (&buf)[VPT], int par) __attribute__((always_inline)) {
         if (lane < NSTAT * nseg) red[par][dwave][lane] = 0.f;
+        if constexpr (LEAN) {
+            if (uni) {
+                // every slot in one segment (RMSNorm): the same sums as below
+                // (each slot's squares in element order, then the wave tree,
+                // then runs of equal segments in slot order), computed for all
+                // slots at once
+                float sq[VPT], w[VPT];
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    float f[EV];
+                    unpack(DT{}, buf[i], f);
+                    sq[i] = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) sq[i] = fmaf(f[e], f[e], sq[i]);
+                }
+                wave_sum_n<VPT>(sq, w);
+                int c = segu[0];
+                float run = 0.f;
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    if (segu[i] != c) {
+                        if (lane == 0) red[par][dwave][c] = run;
+                        run = 0.f;
+                        c = segu[i];
+                    }
+                    run += w[i];
+                }
+                if (lane == 0) red[par][dwave][c] = run;
+                return;
+            }
+        }
         int cur = __builtin_amdgcn_readfirstlane(seg[0]);
         float run = 0.f, run1 = 0.f;
 #pragma unroll
@@ -761,8 +858,22 @@ fused_qknorm_kernel(FusedParams p)
             for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
         }
     };
+    // LEAN: the same iteration with tile k in X and tile k+1 loaded into Y
+    // (the two buffers alternate with the parity of k, so nothing is copied)
+    auto step_xy = [&](int k, float (&u)[VPT][EV], u32x4 (&X)[VPT], u32x4 (&Y)[VPT], bool finish)
+                       __attribute__((always_inline)) {
+        load_tile(tile_of(k + 1), Y);
+        phase_a(X, k & 1);
+        __syncthreads();
+        if (finish) phase_c(u, tile_of(k - LAG), (k - LAG) & 1);
+        phase_b(X, u, tile_of(k));
+        if (finish) wait_vmcnt<VPT>(); else wait_vmcnt<0>();
+    };
 
     // k = 0
+    if constexpr (PACE == 2) {
+        while (wall_clock64() < t_start) __builtin_amdgcn_s_sleep(1);
+    }
     load_tile(tile_of(0), cur);
     // E4M3 outputs saturate at +-448. In every row |x_j| * r <= sqrt(H), since
     // x_j^2 is one term of the row's sum of squares, so |y_j| <= sqrt(H) |gamma_j|
@@ -800,6 +911,36 @@ fused_qknorm_kernel(FusedParams p)
     phase_a(cur, 0);
     __syncthreads();
     phase_b(cur, up0, tile_of(0));
+    if constexpr (LEAN) {
+        // tile 1 stays in nxt: even tiles in cur, odd tiles in nxt
+        wait_vmcnt<0>();
+        if (K > 1) step_xy(1, up1, nxt, cur, false);
+        int k = 2;
+        for (; k + 1 < K; k += 2) {
+            step_xy(k, up0, cur, nxt, true);
+            step_xy(k + 1, up1, nxt, cur, true);
+        }
+        if (k < K) {
+            step_xy(k, up0, cur, nxt, true);
+            ++k;
+        }
+        if (K == 1) {
+            __syncthreads();
+            __syncthreads();
+            phase_c(up0, tile_of(0), 0);
+        } else if (K & 1) {
+            __syncthreads();
+            phase_c(up1, tile_of(K - 2), (K - 2) & 1);
+            __syncthreads();
+            phase_c(up0, tile_of(K - 1), (K - 1) & 1);
+        } else {
+            __syncthreads();
+            phase_c(up0, tile_of(K - 2), (K - 2) & 1);
+            __syncthreads();
+            phase_c(up1, tile_of(K - 1), (K - 1) & 1);
+        }
+        return;
+    }
     if (PREFETCH) {
         wait_vmcnt<0>();
 #pragma unroll

@@ -25,6 +25,7 @@ struct SkeletonParams {
     int32_t rows, nwd, n_shards, n_groups, xcd_map;
     int32_t in_bytes;  // element size of x
     uint32_t pace;     // the fused launch's pacing period (1/256 wall-clock ticks; 0: none)
+    uint32_t stagger;  // 1 = group g's schedule starts g/n_groups periods late
 };
 
 template <int VPT, bool ST, bool WIDEN>
@@ -53,9 +54,10 @@ skeleton_kernel(SkeletonParams p)
     if (wave == 0) {
         // passes the barriers, paced as the fused kernel's comm wave paces them
         const uint64_t t_entry = p.pace ? wall_clock64() : 0;
+        const uint64_t phase = p.stagger ? (uint64_t)group * p.pace / (uint64_t)p.n_groups : 0;
         for (int k = 0; k <= K; ++k) {
             if (p.pace) {
-                const uint64_t due = t_entry + (((uint64_t)k * p.pace) >> 8);
+                const uint64_t due = t_entry + (((uint64_t)k * p.pace + phase) >> 8);
                 while (wall_clock64() < due) __builtin_amdgcn_s_sleep(1);
             }
             __syncthreads();
@@ -152,6 +154,10 @@ skeleton_kernel(SkeletonParams p)
         }
     };
     u32x4 cur[VPT], nxt[VPT];
+    if (p.pace && p.stagger) {
+        const uint64_t due = wall_clock64() + (((uint64_t)group * p.pace / (uint64_t)p.n_groups) >> 8);
+        while (wall_clock64() < due) __builtin_amdgcn_s_sleep(1);
+    }
     load_tile(tile_of(0), cur);
     wait_vmcnt<0>();
     __syncthreads();

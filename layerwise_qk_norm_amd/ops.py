@@ -24,7 +24,7 @@ QKN_BF16, QKN_F32, QKN_E4M3 = 0, 1, 2
 # kernel formats (input x / gamma / output y), the ``dtype`` of the planning calls
 FORMATS = {"bf16": 0, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 3, "ln_bf16": 4, "ln_f32": 5}
 E4M3 = torch.float8_e4m3fn
-NUM_VARIANTS = 10
+NUM_VARIANTS = 11
 MAX_DATA_WAVES = 15
 MAX_SHARDS = 64
 OPT = {"spin_limit_ns": 1, "force_variant": 2, "rows": 3, "xcd_map": 4, "cooperative": 5,

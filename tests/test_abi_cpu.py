@@ -198,19 +198,19 @@ def test_bench_skeleton_rejects_bad_arguments():
 # ------------------------------------------------------------------ planner
 
 CU = 256
-VPT = [1, 2, 3, 4, 6, 9, 1, 2, 3, 4]
+VPT = [1, 2, 3, 4, 6, 9, 1, 2, 3, 4, 5]
 # data waves per variant (launch bound / 64 - 1) and rough register use, per format;
 # 0 = not instantiated for that format
-MAXW = {"bf16": [15, 15, 15, 15, 11, 0, 15, 15, 11, 7],
-        "f32": [15, 15, 15, 15, 11, 15, 15, 15, 11, 7],
-        "e4m3": [15, 15, 11, 0, 0, 0, 15, 11, 0, 0],
-        "ln_bf16": [15, 15, 15, 15, 7, 0, 15, 15, 11, 7],
-        "ln_f32": [15, 15, 15, 15, 7, 0, 15, 15, 11, 7]}
-VGPR = {"bf16": [32, 56, 80, 104, 168, 120, 48, 80, 136, 184],
-        "f32": [32, 56, 80, 104, 168, 120, 48, 80, 104, 128],
-        "e4m3": [56, 104, 144, 1, 1, 1, 96, 168, 1, 1],
-        "ln_bf16": [48, 73, 96, 121, 168, 1, 59, 99, 143, 184],
-        "ln_f32": [32, 58, 71, 95, 124, 1, 40, 72, 98, 139]}
+MAXW = {"bf16": [15, 15, 15, 15, 11, 0, 15, 15, 11, 7, 4],
+        "f32": [15, 15, 15, 15, 11, 15, 15, 15, 11, 7, 0],
+        "e4m3": [15, 15, 11, 0, 0, 0, 15, 11, 0, 0, 0],
+        "ln_bf16": [15, 15, 15, 15, 7, 0, 15, 15, 11, 7, 0],
+        "ln_f32": [15, 15, 15, 15, 7, 0, 15, 15, 11, 7, 0]}
+VGPR = {"bf16": [32, 56, 80, 104, 168, 120, 48, 80, 136, 184, 232],
+        "f32": [32, 56, 80, 104, 168, 120, 48, 80, 104, 128, 1],
+        "e4m3": [56, 104, 144, 1, 1, 1, 96, 168, 1, 1, 1],
+        "ln_bf16": [48, 73, 96, 121, 168, 1, 59, 99, 143, 184, 1],
+        "ln_f32": [32, 58, 71, 95, 124, 1, 40, 72, 98, 139, 1]}
 EV = {"bf16": 8, "f32": 4, "e4m3_bf16": 16, "e4m3_e4m3": 16, "ln_bf16": 8, "ln_f32": 4}
 KGAM = {"bf16": 1, "f32": 1, "e4m3_bf16": 2, "e4m3_e4m3": 2, "ln_bf16": 2, "ln_f32": 2}  # x params
 STATS = {"bf16": 1, "f32": 1, "e4m3_bf16": 1, "e4m3_e4m3": 1, "ln_bf16": 2, "ln_f32": 2}
@@ -350,6 +350,10 @@ def test_plan_prefill_shards_use_single_tensor_tiles():
         check_plan(p, "bf16", 16384, 5120, 5120, N)
         assert p["st"] == 1, (N, p)
     assert plan("bf16", 8192, 5120, 1024, 4)["st"] == 0  # GQA: widths differ
+    # the two-way prefill split: four data waves of five vectors (one wave per
+    # SIMD), four-row tiles, members on one XCD, on the staggered schedule
+    p = plan("bf16", 16384, 5120, 5120, 2)
+    assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["xcd_map"], p["pace_gbs"]) == (10, 4, 4, 1, 1, 7100), p
     # E4M3 entries, timed with rotating buffer sets (inputs beyond the Infinity Cache)
     p = plan("e4m3_e4m3", 16384, 5120, 5120, 2)
     assert (p["variant"], p["data_waves"], p["rows"], p["st"]) == (7, 10, 8, 1), p
@@ -500,10 +504,10 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
     group's members on one XCD for the bf16 prefill split two ways, spread over
     XCDs for GQA and the eight-way splits; 0 and 1 force it either way. (A device
     roomy enough for every tuned launch.)"""
-    roomy = [[0] + [8] * 15 for _ in range(10)]
+    roomy = [[0] + [8] * 15 for _ in range(ops.NUM_VARIANTS)]
     assert ops.get_option("xcd_map") == -1
     p = plan("bf16", 16384, 5120, 5120, 2, bpc=roomy)
-    assert p["xcd_map"] == 1 and (p["variant"], p["rows"], p["st"]) == (9, 4, 1), p
+    assert p["xcd_map"] == 1 and (p["variant"], p["rows"], p["st"]) == (10, 4, 1), p
     g = plan("bf16", 8192, 5120, 1024, 4, bpc=roomy)
     assert g["xcd_map"] == 0 and (g["variant"], g["data_waves"], g["rows"], g["n_groups"]) == (8, 2, 2, 256), g
     for dt in ("bf16", "e4m3_bf16", "e4m3_e4m3", "ln_bf16"):
@@ -522,18 +526,19 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
 
 def test_plan_pace_follows_the_tuned_launch():
     """Tuned launches measured faster paced carry their pacing rate in the plan
-    (bf16 GQA 6700 GB/s; E4M3 -> bf16 split 1, 4 and 8 ways and E4M3 -> E4M3 split
-    2 ways 6600 GB/s); every other launch, forced launches included, has none
-    unless the option sets a rate and its kernel has a paced build; 0 turns pacing
-    off."""
-    roomy = [[0] + [8] * 15 for _ in range(10)]
+    (bf16 split 2 ways on the staggered schedule 7100 GB/s; bf16 GQA 6700 GB/s;
+    E4M3 -> bf16 split 1, 4 and 8 ways and E4M3 -> E4M3 split 2 ways 6600 GB/s);
+    every other launch, forced launches included, has none unless the option
+    sets a rate and its kernel has a paced build; 0 turns pacing off."""
+    roomy = [[0] + [8] * 15 for _ in range(ops.NUM_VARIANTS)]
     pace = lambda *a: plan(*a, bpc=roomy)["pace_gbs"]
     assert ops.get_option("pace") == -1
     assert pace("bf16", 8192, 5120, 1024, 4) == 6700
+    assert pace("bf16", 16384, 5120, 5120, 2) == 7100
     for N in (1, 4, 8):
         assert pace("e4m3_bf16", 16384, 5120, 5120, N) == 6600, N
     assert pace("e4m3_e4m3", 16384, 5120, 5120, 2) == 6600
-    for dt, N in (("bf16", 1), ("bf16", 2), ("bf16", 4), ("bf16", 8), ("e4m3_bf16", 2), ("e4m3_e4m3", 1),
+    for dt, N in (("bf16", 1), ("bf16", 4), ("bf16", 8), ("e4m3_bf16", 2), ("e4m3_e4m3", 1),
                   ("e4m3_e4m3", 4), ("e4m3_e4m3", 8), ("ln_bf16", 2)):
         assert pace(dt, 16384, 5120, 5120, N) == 0, (dt, N)
     assert pace("bf16", 16384, 3072, 3072, 4) == 0 and pace("f32", 16384, 8192, 8192, 8) == 0
@@ -556,7 +561,8 @@ def test_plan_pace_follows_the_tuned_launch():
         assert pace("bf16", 8192, 5120, 1024, 4) == 5000
         assert pace("e4m3_e4m3", 16384, 5120, 5120, 2) == 5000
         # kernels without a paced build run unpaced whatever the option says
-        assert pace("bf16", 16384, 3072, 3072, 2) == 0 and pace("bf16", 16384, 5120, 5120, 2) == 0
+        assert pace("bf16", 16384, 3072, 3072, 2) == 0 and pace("bf16", 16384, 5120, 5120, 4) == 0
+        assert pace("bf16", 16384, 5120, 5120, 2) == 5000
         for bad in (-2, 100001):
             assert ops.lib().qknorm_set_option(ops.OPT["pace"], bad) == ops.QKN_EINVAL
     finally:
@@ -568,7 +574,7 @@ def test_plan_xcd_rule_for_untuned_shapes():
     4-8 ways and for bf16 split 4 ways with shard rows of at least 1 KiB; every
     other untuned shape, latency-bound batches, forced launches and LayerNorm or
     E4M3 keep them on one XCD; the option still forces either way."""
-    roomy = [[0] + [8] * 15 for _ in range(10)]
+    roomy = [[0] + [8] * 15 for _ in range(ops.NUM_VARIANTS)]
     xm = lambda *a, **kw: plan(*a, bpc=roomy, **kw)["xcd_map"]
     for T in (4096, 16384, 65536):
         for H in (1024, 3072, 8192):

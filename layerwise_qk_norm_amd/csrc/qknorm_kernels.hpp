@@ -351,8 +351,8 @@ fused_qknorm_kernel(FusedParams p)
     // instead of being copied. The results are bitwise those of the other
     // builds.
     constexpr bool LEAN = PACE == 2;
-    static_assert(PACE != 2 || (std::is_same<DT, Bf16>::value && NORM == 0 && LAG == 2 && PREFETCH),
-                  "staggered pacing is built for bf16 RMSNorm with a two-tile lag");
+    static_assert(PACE != 2 || (std::is_same<DT, Bf16>::value && NORM == 0 && LAG == 2 && PREFETCH && ST),
+                  "staggered pacing is built for bf16 RMSNorm on single-tensor tiles with a two-tile lag");
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     constexpr int EV = DT::kVec;
@@ -506,10 +506,15 @@ fused_qknorm_kernel(FusedParams p)
     // prefetched tile can be consumed while the previous tile's stores are still
     // in flight.
     const int dwave = wave - 1;
-    // staggered pacing: this group's first loads go out one period plus its
-    // phase (group / n_groups of a period) after entry, gamma staging included
+    // staggered pacing: this group's first loads go out a lead plus its phase
+    // (group / n_groups of a period) after entry. The lead covers gamma staging
+    // (about 0.6-0.75 us); a group still staging when its start comes goes out
+    // of tile order, which measured costly: leads of 1/2, 3/8 and 1/4 of a
+    // 1.48 us period took the two-way prefill 103.3, 103.9 and 106.8 us, a full
+    // period 104.2 us. 5/8 of a period keeps a margin above the staging time.
+    constexpr uint64_t kLead = 160;  // 1/256 of a period
     const uint64_t t_start = PACE == 2
-                                 ? wall_clock64() + (((uint64_t)p.pace + (uint64_t)group * p.pace / (uint64_t)p.n_groups) >> 8)
+                                 ? wall_clock64() + ((kLead * p.pace / 256 + (uint64_t)group * p.pace / (uint64_t)p.n_groups) >> 8)
                                  : 0;
     const int ndt = 64 * nwd;  // data threads
     const int dt = tid - 64;
@@ -531,6 +536,9 @@ fused_qknorm_kernel(FusedParams p)
     // vectors 32..63, each as whole lines (lanes 0-31 write first halves,
     // lanes 32-63 second halves).
     constexpr bool kPair = KO == 2;
+    // LEAN: gamma words of every slot (Q's, then K's), loaded together and
+    // written to LDS after one wait
+    u32x4 gstage[LEAN ? 2 * VPT : 1];
     uint32_t voff[VPT];  // input byte offset from the tile's first row, or kOOB
     uint32_t ooff[VPT];  // output byte offset (equal to voff when ES == OS)
     uint32_t poff[kPair ? VPT : 1][2];  // kPair: the lane's offsets for its two stores
@@ -591,7 +599,11 @@ fused_qknorm_kernel(FusedParams p)
         // (Two spellings of the same staging: the streaming loop's speed depends
         // on register assignment, which this code shifts, and each kernel keeps
         // the spelling it was measured fastest with.)
-        if constexpr (!(ST && (NORM || EV == 16))) {
+        if constexpr (LEAN) {
+            // (bf16 RMSNorm, single-tensor tiles: one gamma word per slot and tensor)
+            gstage[i] = valid ? ld_cached(static_cast<const gam_t*>(p.gamma[0]) + col) : u32x4{0, 0, 0, 0};
+            gstage[VPT + i] = valid ? ld_cached(static_cast<const gam_t*>(p.gamma[1]) + col) : u32x4{0, 0, 0, 0};
+        } else if constexpr (!(ST && (NORM || EV == 16))) {
 #pragma unroll
             for (int g = 0; g < KG; ++g)
                 gam_lds[(i * ndt + dt) * KG + g] =
@@ -645,6 +657,14 @@ fused_qknorm_kernel(FusedParams p)
         for (int i = 0; i < VPT; ++i) {
             segu[i] = __builtin_amdgcn_readfirstlane(seg[i]);
             uni = uni && segu[i] == __builtin_amdgcn_readlane(seg[i], 63);
+        }
+    }
+
+    if constexpr (LEAN) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            gam_lds[i * ndt + dt] = gstage[i];
+            gam_lds[VPT * ndt + i * ndt + dt] = gstage[VPT + i];
         }
     }
 

@@ -320,7 +320,10 @@ int qknorm_release_workspace(void);
  * real path queries the occupancy API). Variants 0-5 hold 1, 2, 3, 4, 6, 9
  * 16-byte vectors per data thread (5: fp32 only) and scale a tile one
  * iteration after reducing it; variants 6-9 hold 1, 2, 3, 4 and scale it two
- * iterations later, which decouples the shards of a group further. The e4m3
+ * iterations later, which decouples the shards of a group further; variant 10
+ * (bf16 on single-tensor tiles only, at most four data waves: one per SIMD
+ * with the exchange wave) holds 5 with the two-iteration lag and is planned
+ * only by the tuned table or QKN_OPT_FORCE_VARIANT. The e4m3
  * formats have variants 0, 1, 2, 6 and 7 (a 16-byte vector is 16 columns);
  * the LayerNorm formats have all but variant 5.
  * A tile is `rows` tokens of Q and of K (mixed layout), or, with Hq == Hk,
@@ -352,7 +355,12 @@ typedef struct qknorm_plan {
                            kernels that have one): no workgroup passes its k-th
                            barrier before k periods after its start, one period being
                            the time the whole grid's tile bytes of one iteration take
-                           at that rate (launches of more than two iterations) */
+                           at that rate (launches of more than two iterations). The
+                           staggered builds (bf16 variants 9 and 10 on single-tensor
+                           tiles) start group g's first loads 5/8 of a period plus
+                           g / n_groups of a period after entry and count barrier
+                           k's period from barrier 0, so tiles are loaded in tile
+                           order; their drain barriers are not held */
 } qknorm_plan;
 int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
                       int cu_count, const int* blocks_per_cu, int aligned,
@@ -385,9 +393,11 @@ enum {
     QKN_OPT_PACE = 14,          /* -1 = planner's choice (the tuned launches measured
                                    faster paced), 0 = no pacing, else a pacing rate in
                                    GB/s (qknorm_plan.pace_gbs) for launches whose kernel
-                                   has a paced build: bf16 variant 8 on mixed tiles,
-                                   E4M3 -> bf16 variants 0 (single-tensor tiles) and 7
-                                   (mixed), E4M3 -> E4M3 variant 7 (single-tensor) */
+                                   has a paced build: bf16 variant 8 on mixed tiles and
+                                   variants 9 and 10 on single-tensor tiles (staggered:
+                                   see qknorm_plan.pace_gbs), E4M3 -> bf16 variants 0
+                                   (single-tensor tiles) and 7 (mixed), E4M3 -> E4M3
+                                   variant 7 (single-tensor) */
     QKN_OPT_STATIC_SLOTS = 13,  /* test hook: 0 = the no-allocation call may use all of
                                    its static slots, else at most this many (so that
                                    QKN_ESCRATCH can be exercised) */

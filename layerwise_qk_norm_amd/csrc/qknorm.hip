@@ -81,9 +81,9 @@ constexpr Variant kVariants[QKN_NUM_VARIANTS] = {
     {2, true, 2, 1024},
     {3, true, 2, 768},
     {4, true, 2, 512},
-    // bf16 only: four data waves and the comm wave, one wave per SIMD, so no
-    // SIMD runs two data waves' arithmetic (reached through the tuned table or
-    // QKN_OPT_FORCE_VARIANT, not the scored search)
+    // bf16 single-tensor tiles only: four data waves and the comm wave, one
+    // wave per SIMD, so no SIMD runs two data waves' arithmetic (reached
+    // through the tuned table or QKN_OPT_FORCE_VARIANT, not the scored search)
     {5, true, 2, 320},
 };
 
@@ -106,10 +106,7 @@ FusedFn fused_fn(int v)
     case 7: return qkn::fused_qknorm_kernel<DT, 2, true, 2, 1024>;
     case 8: return qkn::fused_qknorm_kernel<DT, 3, true, 2, 768>;
     case 9: return qkn::fused_qknorm_kernel<DT, 4, true, 2, 512>;
-    case 10:
-        if constexpr (std::is_same<DT, Bf16>::value) return qkn::fused_qknorm_kernel<DT, 5, true, 2, 320>;
-        return nullptr;
-    default: return nullptr;
+    default: return nullptr;  // variant 10: single-tensor tiles only
     }
 }
 template <>

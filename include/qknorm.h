@@ -306,7 +306,8 @@ int qknorm_max_coresident_workgroups(int dtype, int64_t Hq, int64_t Hk, int n_sh
  * + w] = workgroups of fused variant v with w data waves that one compute
  * unit can hold (0 = not launchable), an array of QKN_NUM_VARIANTS x
  * (QKN_MAX_DATA_WAVES + 1) ints; *cu_count = compute units. Feeds
- * qknorm_plan_fused with the numbers the library itself plans with. */
+ * qknorm_plan_fused with the numbers the library itself plans with. A variant
+ * built for single-tensor tiles only (10) reports that kernel's occupancy. */
 int qknorm_device_occupancy(int dtype, int* blocks_per_cu, int* cu_count);
 
 /* Frees every workspace the library allocated (all devices and streams).
@@ -357,10 +358,12 @@ typedef struct qknorm_plan {
                            the time the whole grid's tile bytes of one iteration take
                            at that rate (launches of more than two iterations). The
                            staggered builds (bf16 variants 9 and 10 on single-tensor
-                           tiles) start group g's first loads 5/8 of a period plus
-                           g / n_groups of a period after entry and count barrier
-                           k's period from barrier 0, so tiles are loaded in tile
-                           order; their drain barriers are not held */
+                           tiles, LayerNorm bf16 variant 7 on mixed tiles) start
+                           group g's first loads a lead (5/8 of a period for the
+                           bf16 builds, one period for LayerNorm) plus g / n_groups
+                           of a period after entry and count barrier k's period from
+                           barrier 0, so tiles are loaded in tile order; their drain
+                           barriers are not held */
 } qknorm_plan;
 int qknorm_plan_fused(int dtype, int64_t T, int64_t Hq, int64_t Hk, int n_shards,
                       int cu_count, const int* blocks_per_cu, int aligned,
@@ -397,7 +400,8 @@ enum {
                                    variants 9 and 10 on single-tensor tiles (staggered:
                                    see qknorm_plan.pace_gbs), E4M3 -> bf16 variants 0
                                    (single-tensor tiles) and 7 (mixed), E4M3 -> E4M3
-                                   variant 7 (single-tensor) */
+                                   variant 7 (single-tensor), LayerNorm bf16 variant 7
+                                   on mixed tiles (staggered) */
     QKN_OPT_STATIC_SLOTS = 13,  /* test hook: 0 = the no-allocation call may use all of
                                    its static slots, else at most this many (so that
                                    QKN_ESCRATCH can be exercised) */

@@ -216,14 +216,17 @@ FusedFn fused_fn_layout(int fmt, int v, bool st)
     default: return fused_fn_st<F32, 1>(v);
     }
 }
-// Paced builds (PACE = true) of the kernels the tuned table
-// paces: bf16 variant 8 on mixed tiles (GQA), E4M3 -> bf16 variant 0 on
-// single-tensor tiles and 7 on mixed tiles, E4M3 -> E4M3 variant 7 on
-// single-tensor tiles; nullptr for every other kernel, which runs unpaced.
+// Paced builds of the kernels the tuned table paces. On one schedule for every
+// group (PACE = 1): bf16 variant 8 on mixed tiles (GQA), E4M3 -> bf16 variant 0
+// on single-tensor tiles and 7 on mixed tiles, E4M3 -> E4M3 variant 7 on
+// single-tensor tiles. Staggered (PACE = 2): bf16 variants 9 and 10 on
+// single-tensor tiles (the prefill split one and two ways) and LayerNorm bf16
+// variant 7 on mixed tiles. nullptr for every other kernel, which runs unpaced.
 FusedFn paced_fn(int fmt, int v, bool st)
 {
     if (fmt == QKN_FMT_BF16 && v == 9 && st) return qkn::fused_qknorm_kernel<Bf16, 4, true, 2, 512, 0, true, 2>;
     if (fmt == QKN_FMT_BF16 && v == 10 && st) return qkn::fused_qknorm_kernel<Bf16, 5, true, 2, 320, 0, true, 2>;
+    if (fmt == QKN_FMT_LN_BF16 && v == 7 && !st) return qkn::fused_qknorm_kernel<Bf16, 2, true, 2, 1024, 1, false, 2>;
     if (fmt == QKN_FMT_BF16 && v == 8 && !st) return qkn::fused_qknorm_kernel<Bf16, 3, true, 2, 768, 0, false, 1>;
     if (fmt == QKN_FMT_E4M3_BF16 && v == 0 && st)
         return qkn::fused_qknorm_kernel<E4m3Bf16, 1, true, 1, kE4m3MaxThreads[0], 0, true, 1>;
@@ -264,7 +267,10 @@ SkelFn skeleton_fn(int vpt, bool st, bool widen)
 }
 bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
 // paced builds on the staggered schedule (PACE = 2)
-bool paced_staggered(int fmt, int v, bool st) { return fmt == QKN_FMT_BF16 && st && (v == 9 || v == 10); }
+bool paced_staggered(int fmt, int v, bool st)
+{
+    return (fmt == QKN_FMT_BF16 && st && (v == 9 || v == 10)) || (fmt == QKN_FMT_LN_BF16 && !st && v == 7);
+}
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
 // data waves a workgroup of variant v may have (launch bound / 64, minus the comm wave)
 int max_data_waves(int fmt, int v)
@@ -708,6 +714,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     auto consider = [&](int v, int w, int r, int wpc, bool st) {
         const Variant& k = kVariants[v];
         if (st && (!st_ok || r > rows_cap_st || !fused_fn_layout(dtype, v, true))) return;
+        if (!st && !fused_fn_layout(dtype, v, false)) return;  // (variant 10: single-tensor tiles only)
         const int64_t tv = tile_vectors(r, st);
         if (w < 1 || w > max_data_waves(dtype, v) || (int64_t)64 * w * k.vpt < tv) return;
         const int b = (st ? bpc_st : bpc)[v * (QKN_MAX_DATA_WAVES + 1) + w];
@@ -781,7 +788,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4, 0, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 256, 4, 7, 3, 4, 3, 0},
         {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1, 0},
-        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1, 0},
+        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1, 0, 1, 6700},
         {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 10, 4, 1, 0},
         {QKN_FMT_LN_BF16, 640, 640, 8, 6, 5, 4, 4, 1, 0},
         {QKN_FMT_LN_BF16, 640, 640, 8, 7, 3, 2, 4, 0},
@@ -1744,9 +1751,12 @@ int qknorm_device_occupancy(int dtype, int* blocks_per_cu, int* cu_count)
     if (rc) return rc;
     DevInfo* di = nullptr;
     if ((rc = device_info(dev, dtype, &di))) return rc;
-    for (int v = 0; v < QKN_NUM_VARIANTS; ++v)
+    // a variant built for single-tensor tiles only reports that kernel's occupancy
+    for (int v = 0; v < QKN_NUM_VARIANTS; ++v) {
+        const bool st_only = !fused_fn_layout(dtype, v, false) && fused_fn_layout(dtype, v, true);
         for (int w = 0; w <= QKN_MAX_DATA_WAVES; ++w)
-            blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1) + w] = di->occ[dtype][v][w];
+            blocks_per_cu[v * (QKN_MAX_DATA_WAVES + 1) + w] = st_only ? di->occ_st[dtype][v][w] : di->occ[dtype][v][w];
+    }
     *cu_count = di->cu;
     return QKN_OK;
 }

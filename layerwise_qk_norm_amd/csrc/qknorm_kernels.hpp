@@ -346,13 +346,12 @@ __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
     // PACE 2 builds run on the staggered schedule, where the data waves' work
-    // per tile is on the critical path of every iteration: Phase A reduces all
-    // of a wave's slots side by side, and the two tile buffers alternate
-    // instead of being copied. The results are bitwise those of the other
-    // builds.
-    constexpr bool LEAN = PACE == 2;
-    static_assert(PACE != 2 || (std::is_same<DT, Bf16>::value && NORM == 0 && LAG == 2 && PREFETCH && ST),
-                  "staggered pacing is built for bf16 RMSNorm on single-tensor tiles with a two-tile lag");
+    // per tile is on the critical path of every iteration. For bf16 RMSNorm on
+    // single-tensor tiles with a two-tile lag they also reduce all of a wave's
+    // Phase A slots side by side, alternate the two tile buffers instead of
+    // copying them and stage gamma with one wait (LEAN). The results are
+    // bitwise those of the other builds.
+    constexpr bool LEAN = PACE == 2 && std::is_same<DT, Bf16>::value && NORM == 0 && LAG == 2 && PREFETCH && ST;
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     constexpr int EV = DT::kVec;
@@ -512,7 +511,7 @@ fused_qknorm_kernel(FusedParams p)
     // of tile order, which measured costly: leads of 1/2, 3/8 and 1/4 of a
     // 1.48 us period took the two-way prefill 103.3, 103.9 and 106.8 us, a full
     // period 104.2 us. 5/8 of a period keeps a margin above the staging time.
-    constexpr uint64_t kLead = 160;  // 1/256 of a period
+    constexpr uint64_t kLead = LEAN ? 160 : 256;  // 1/256 of a period (serial staging: a whole one)
     const uint64_t t_start = PACE == 2
                                  ? wall_clock64() + ((kLead * p.pace / 256 + (uint64_t)group * p.pace / (uint64_t)p.n_groups) >> 8)
                                  : 0;

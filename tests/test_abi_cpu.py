@@ -526,8 +526,9 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
 
 def test_plan_pace_follows_the_tuned_launch():
     """Tuned launches measured faster paced carry their pacing rate in the plan
-    (bf16 split 2 ways on the staggered schedule 7100 GB/s; bf16 GQA 6700 GB/s;
-    E4M3 -> bf16 split 1, 4 and 8 ways and E4M3 -> E4M3 split 2 ways 6600 GB/s);
+    (bf16 split 2 ways on the staggered schedule 7100 GB/s, LayerNorm bf16 split 2
+    ways staggered 6700 GB/s; bf16 GQA 6700 GB/s; E4M3 -> bf16 split 1, 4 and 8 ways
+    and E4M3 -> E4M3 split 2 ways 6600 GB/s);
     every other launch, forced launches included, has none unless the option
     sets a rate and its kernel has a paced build; 0 turns pacing off."""
     roomy = [[0] + [8] * 15 for _ in range(ops.NUM_VARIANTS)]
@@ -535,11 +536,12 @@ def test_plan_pace_follows_the_tuned_launch():
     assert ops.get_option("pace") == -1
     assert pace("bf16", 8192, 5120, 1024, 4) == 6700
     assert pace("bf16", 16384, 5120, 5120, 2) == 7100
+    assert pace("ln_bf16", 16384, 5120, 5120, 2) == 6700
     for N in (1, 4, 8):
         assert pace("e4m3_bf16", 16384, 5120, 5120, N) == 6600, N
     assert pace("e4m3_e4m3", 16384, 5120, 5120, 2) == 6600
     for dt, N in (("bf16", 1), ("bf16", 4), ("bf16", 8), ("e4m3_bf16", 2), ("e4m3_e4m3", 1),
-                  ("e4m3_e4m3", 4), ("e4m3_e4m3", 8), ("ln_bf16", 2)):
+                  ("e4m3_e4m3", 4), ("e4m3_e4m3", 8), ("ln_bf16", 4)):
         assert pace(dt, 16384, 5120, 5120, N) == 0, (dt, N)
     assert pace("bf16", 16384, 3072, 3072, 4) == 0 and pace("f32", 16384, 8192, 8192, 8) == 0
     assert pace("bf16", 64, 4096, 4096, 4) == 0

@@ -357,8 +357,8 @@ typedef struct qknorm_plan {
                            barrier before k periods after its start, one period being
                            the time the whole grid's tile bytes of one iteration take
                            at that rate (launches of more than two iterations). The
-                           staggered builds (bf16 variants 9 and 10 on single-tensor
-                           tiles, LayerNorm bf16 variant 7 on mixed tiles) start
+                           staggered builds (bf16 variant 10 on single-tensor tiles,
+                           LayerNorm bf16 variant 7 on mixed tiles) start
                            group g's first loads a lead (5/8 of a period for the
                            bf16 builds, one period for LayerNorm) plus g / n_groups
                            of a period after entry and count barrier k's period from
@@ -397,7 +397,7 @@ enum {
                                    faster paced), 0 = no pacing, else a pacing rate in
                                    GB/s (qknorm_plan.pace_gbs) for launches whose kernel
                                    has a paced build: bf16 variant 8 on mixed tiles and
-                                   variants 9 and 10 on single-tensor tiles (staggered:
+                                   variant 10 on single-tensor tiles (staggered:
                                    see qknorm_plan.pace_gbs), E4M3 -> bf16 variants 0
                                    (single-tensor tiles) and 7 (mixed), E4M3 -> E4M3
                                    variant 7 (single-tensor), LayerNorm bf16 variant 7

@@ -219,12 +219,11 @@ FusedFn fused_fn_layout(int fmt, int v, bool st)
 // Paced builds of the kernels the tuned table paces. On one schedule for every
 // group (PACE = 1): bf16 variant 8 on mixed tiles (GQA), E4M3 -> bf16 variant 0
 // on single-tensor tiles and 7 on mixed tiles, E4M3 -> E4M3 variant 7 on
-// single-tensor tiles. Staggered (PACE = 2): bf16 variants 9 and 10 on
-// single-tensor tiles (the prefill split one and two ways) and LayerNorm bf16
-// variant 7 on mixed tiles. nullptr for every other kernel, which runs unpaced.
+// single-tensor tiles. Staggered (PACE = 2): bf16 variant 10 on single-tensor
+// tiles (the prefill split one and two ways) and LayerNorm bf16 variant 7 on
+// mixed tiles. nullptr for every other kernel, which runs unpaced.
 FusedFn paced_fn(int fmt, int v, bool st)
 {
-    if (fmt == QKN_FMT_BF16 && v == 9 && st) return qkn::fused_qknorm_kernel<Bf16, 4, true, 2, 512, 0, true, 2>;
     if (fmt == QKN_FMT_BF16 && v == 10 && st) return qkn::fused_qknorm_kernel<Bf16, 5, true, 2, 320, 0, true, 2>;
     if (fmt == QKN_FMT_LN_BF16 && v == 7 && !st) return qkn::fused_qknorm_kernel<Bf16, 2, true, 2, 1024, 1, false, 2>;
     if (fmt == QKN_FMT_BF16 && v == 8 && !st) return qkn::fused_qknorm_kernel<Bf16, 3, true, 2, 768, 0, false, 1>;
@@ -265,11 +264,12 @@ SkelFn skeleton_fn(int vpt, bool st, bool widen)
     if (st) return widen ? skeleton_fn_vpt<true, true>(vpt) : skeleton_fn_vpt<true, false>(vpt);
     return widen ? skeleton_fn_vpt<false, true>(vpt) : skeleton_fn_vpt<false, false>(vpt);
 }
-bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr; }
+// built for this format in some tile layout (variant 10: single-tensor tiles only)
+bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr || fused_fn_layout(fmt, v, true) != nullptr; }
 // paced builds on the staggered schedule (PACE = 2)
 bool paced_staggered(int fmt, int v, bool st)
 {
-    return (fmt == QKN_FMT_BF16 && st && (v == 9 || v == 10)) || (fmt == QKN_FMT_LN_BF16 && !st && v == 7);
+    return (fmt == QKN_FMT_BF16 && st && v == 10) || (fmt == QKN_FMT_LN_BF16 && !st && v == 7);
 }
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
 // data waves a workgroup of variant v may have (launch bound / 64, minus the comm wave)
@@ -760,6 +760,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
     static const Tuned kTuned[] = {
         // single-tensor tiles first where they measured faster; the mixed-tile
         // entries after them serve when QKN_OPT_TILE_LAYOUT asks for mixed tiles
+        {QKN_FMT_BF16, 5120, 5120, 1, 10, 4, 2, 1, 1, 1, 7100},
         {QKN_FMT_BF16, 5120, 5120, 1, 9, 5, 2, 1, 1},
         {QKN_FMT_BF16, 2560, 2560, 2, 10, 4, 4, 1, 1, 1, 7100},
         {QKN_FMT_BF16, 2560, 2560, 2, 9, 5, 4, 1, 1},

@@ -354,6 +354,8 @@ def test_plan_prefill_shards_use_single_tensor_tiles():
     # SIMD), four-row tiles, members on one XCD, on the staggered schedule
     p = plan("bf16", 16384, 5120, 5120, 2)
     assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["xcd_map"], p["pace_gbs"]) == (10, 4, 4, 1, 1, 7100), p
+    p = plan("bf16", 16384, 5120, 5120, 1)  # unsplit: the same tile as 2-row tiles
+    assert (p["variant"], p["data_waves"], p["rows"], p["st"], p["pace_gbs"]) == (10, 4, 2, 1, 7100), p
     # E4M3 entries, timed with rotating buffer sets (inputs beyond the Infinity Cache)
     p = plan("e4m3_e4m3", 16384, 5120, 5120, 2)
     assert (p["variant"], p["data_waves"], p["rows"], p["st"]) == (7, 10, 8, 1), p
@@ -526,7 +528,7 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
 
 def test_plan_pace_follows_the_tuned_launch():
     """Tuned launches measured faster paced carry their pacing rate in the plan
-    (bf16 split 2 ways on the staggered schedule 7100 GB/s, LayerNorm bf16 split 2
+    (bf16 split 1 and 2 ways on the staggered schedule 7100 GB/s, LayerNorm bf16 split 2
     ways staggered 6700 GB/s; bf16 GQA 6700 GB/s; E4M3 -> bf16 split 1, 4 and 8 ways
     and E4M3 -> E4M3 split 2 ways 6600 GB/s);
     every other launch, forced launches included, has none unless the option
@@ -536,11 +538,12 @@ def test_plan_pace_follows_the_tuned_launch():
     assert ops.get_option("pace") == -1
     assert pace("bf16", 8192, 5120, 1024, 4) == 6700
     assert pace("bf16", 16384, 5120, 5120, 2) == 7100
+    assert pace("bf16", 16384, 5120, 5120, 1) == 7100
     assert pace("ln_bf16", 16384, 5120, 5120, 2) == 6700
     for N in (1, 4, 8):
         assert pace("e4m3_bf16", 16384, 5120, 5120, N) == 6600, N
     assert pace("e4m3_e4m3", 16384, 5120, 5120, 2) == 6600
-    for dt, N in (("bf16", 1), ("bf16", 4), ("bf16", 8), ("e4m3_bf16", 2), ("e4m3_e4m3", 1),
+    for dt, N in (("bf16", 4), ("bf16", 8), ("e4m3_bf16", 2), ("e4m3_e4m3", 1),
                   ("e4m3_e4m3", 4), ("e4m3_e4m3", 8), ("ln_bf16", 4)):
         assert pace(dt, 16384, 5120, 5120, N) == 0, (dt, N)
     assert pace("bf16", 16384, 3072, 3072, 4) == 0 and pace("f32", 16384, 8192, 8192, 8) == 0
@@ -604,3 +607,21 @@ def test_plan_xcd_rule_for_untuned_shapes():
         assert xm("bf16", 16384, 3072, 3072, 2) == 0
     finally:
         ops.set_option("xcd_map", -1)
+
+
+def test_plan_forced_single_tensor_only_variant():
+    """Variant 10 exists for single-tensor tiles only: forcing it plans it on such
+    tiles, and never on mixed tiles (the forced search then finds no launch)."""
+    try:
+        for n, v in (("force_variant", 10), ("data_waves", 4), ("rows", 4), ("tile_layout", 2)):
+            ops.set_option(n, v)
+        p = plan("bf16", 16384, 5120, 5120, 2)
+        assert (p["variant"], p["data_waves"], p["rows"], p["st"]) == (10, 4, 4, 1), p
+        ops.set_option("rows", 2)
+        p = plan("bf16", 16384, 5120, 5120, 1)
+        assert (p["variant"], p["rows"], p["st"]) == (10, 2, 1), p
+        ops.set_option("tile_layout", 1)
+        assert plan("bf16", 16384, 5120, 5120, 2)["variant"] != 10
+    finally:
+        for n, v in (("force_variant", -1), ("data_waves", 0), ("rows", 0), ("tile_layout", 0)):
+            ops.set_option(n, v)

@@ -541,7 +541,8 @@ def test_bench_skeleton_moves_every_byte(fmt, T, Hq, Hk, N, layout):
     ("bf16", 8192, 5120, 1024, 4, -1),      # the tuned GQA launch, paced by default
     ("bf16", 16384, 5120, 5120, 2, -1),     # the tuned prefill launch, staggered by default
     ("bf16", 4099, 5120, 5120, 2, 4000),    # staggered, groups of 17 and 16 tiles, barriers held
-    ("bf16", 4096, 5120, 5120, 1, 7000),    # the staggered build of the one-shard launch
+    ("bf16", 4096, 5120, 5120, 1, -1),      # the tuned one-shard launch, staggered by default
+    ("bf16", 4099, 5120, 5120, 1, 6000),    # the same, ragged, at a set rate
     ("ln_bf16", 16384, 5120, 5120, 2, -1),  # the tuned LayerNorm launch, staggered by default
     ("ln_bf16", 4099, 5120, 5120, 2, 4000), # staggered LayerNorm, ragged, barriers held
     ("bf16", 4096, 5120, 1024, 4, 4000),    # a rate below the launch's own: barriers held

@@ -220,13 +220,16 @@ FusedFn fused_fn_layout(int fmt, int v, bool st)
 // group (PACE = 1): bf16 variant 8 on mixed tiles (GQA), E4M3 -> bf16 variant 0
 // on single-tensor tiles and 7 on mixed tiles, E4M3 -> E4M3 variant 7 on
 // single-tensor tiles. Staggered (PACE = 2): bf16 variant 10 on single-tensor
-// tiles (the prefill split one and two ways) and LayerNorm bf16 variant 7 on
-// mixed tiles. nullptr for every other kernel, which runs unpaced.
+// tiles (the prefill split one and two ways), E4M3 -> bf16 variant 7 on
+// single-tensor tiles (split two ways) and LayerNorm bf16 variant 7 on mixed
+// tiles. nullptr for every other kernel, which runs unpaced.
 FusedFn paced_fn(int fmt, int v, bool st)
 {
     if (fmt == QKN_FMT_BF16 && v == 10 && st) return qkn::fused_qknorm_kernel<Bf16, 5, true, 2, 320, 0, true, 2>;
     if (fmt == QKN_FMT_LN_BF16 && v == 7 && !st) return qkn::fused_qknorm_kernel<Bf16, 2, true, 2, 1024, 1, false, 2>;
     if (fmt == QKN_FMT_BF16 && v == 8 && !st) return qkn::fused_qknorm_kernel<Bf16, 3, true, 2, 768, 0, false, 1>;
+    if (fmt == QKN_FMT_E4M3_BF16 && v == 7 && st)
+        return qkn::fused_qknorm_kernel<E4m3Bf16, 2, true, 2, kE4m3MaxThreads[7], 0, true, 2>;
     if (fmt == QKN_FMT_E4M3_BF16 && v == 0 && st)
         return qkn::fused_qknorm_kernel<E4m3Bf16, 1, true, 1, kE4m3MaxThreads[0], 0, true, 1>;
     if (fmt == QKN_FMT_E4M3_BF16 && v == 7 && !st)
@@ -269,7 +272,8 @@ bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr || 
 // paced builds on the staggered schedule (PACE = 2)
 bool paced_staggered(int fmt, int v, bool st)
 {
-    return (fmt == QKN_FMT_BF16 && st && v == 10) || (fmt == QKN_FMT_LN_BF16 && !st && v == 7);
+    return (fmt == QKN_FMT_BF16 && st && v == 10) || (fmt == QKN_FMT_LN_BF16 && !st && v == 7) ||
+           (fmt == QKN_FMT_E4M3_BF16 && st && v == 7);
 }
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
 // data waves a workgroup of variant v may have (launch bound / 64, minus the comm wave)
@@ -776,6 +780,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 3, 2, 3, 0, 0, 6600},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 7, 5, 8, 1, 1},
         {QKN_FMT_E4M3_BF16, 5120, 5120, 1, 2, 7, 2, 1, 0},
+        {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 10, 8, 1, 1, 1, 6800},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 1, 10, 4, 1, 0, 0},
         {QKN_FMT_E4M3_BF16, 2560, 2560, 2, 7, 8, 3, 1, 0},
         {QKN_FMT_E4M3_BF16, 1280, 1280, 4, 6, 8, 3, 1, 0},

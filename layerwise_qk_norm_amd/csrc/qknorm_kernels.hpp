@@ -346,12 +346,13 @@ __global__ void __launch_bounds__(MAXT)
 fused_qknorm_kernel(FusedParams p)
 {
     // PACE 2 builds run on the staggered schedule, where the data waves' work
-    // per tile is on the critical path of every iteration. For bf16 RMSNorm on
-    // single-tensor tiles with a two-tile lag they also reduce all of a wave's
-    // Phase A slots side by side, alternate the two tile buffers instead of
-    // copying them and stage gamma with one wait (LEAN). The results are
-    // bitwise those of the other builds.
-    constexpr bool LEAN = PACE == 2 && std::is_same<DT, Bf16>::value && NORM == 0 && LAG == 2 && PREFETCH && ST;
+    // per tile is on the critical path of every iteration. For RMSNorm with bf16
+    // outputs (bf16 or E4M3 inputs) on single-tensor tiles with a two-tile lag
+    // they also reduce all of a wave's Phase A slots side by side, alternate the
+    // two tile buffers instead of copying them and stage gamma with one wait
+    // (LEAN). The results are bitwise those of the other builds.
+    constexpr bool LEAN = PACE == 2 && (std::is_same<DT, Bf16>::value || std::is_same<DT, E4m3Bf16>::value) &&
+                          NORM == 0 && LAG == 2 && PREFETCH && ST;
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     constexpr int EV = DT::kVec;
@@ -511,7 +512,11 @@ fused_qknorm_kernel(FusedParams p)
     // of tile order, which measured costly: leads of 1/2, 3/8 and 1/4 of a
     // 1.48 us period took the two-way prefill 103.3, 103.9 and 106.8 us, a full
     // period 104.2 us. 5/8 of a period keeps a margin above the staging time.
-    constexpr uint64_t kLead = LEAN ? 160 : 256;  // 1/256 of a period (serial staging: a whole one)
+    // E4M3 -> bf16 tiles hold twice the tokens per byte of input, so its period
+    // (8-row tiles at 6800 GB/s: 2.3 us) is longer than the staging; leads of
+    // 3/16, 3/8 and 5/8 of it took its two-way prefill 83.9, 83.6 and 84.4 us.
+    constexpr uint64_t kLead = LEAN ? (std::is_same<DT, E4m3Bf16>::value ? 96 : 160)
+                                    : 256;  // 1/256 of a period (serial staging: a whole one)
     const uint64_t t_start = PACE == 2
                                  ? wall_clock64() + ((kLead * p.pace / 256 + (uint64_t)group * p.pace / (uint64_t)p.n_groups) >> 8)
                                  : 0;
@@ -537,7 +542,7 @@ fused_qknorm_kernel(FusedParams p)
     constexpr bool kPair = KO == 2;
     // LEAN: gamma words of every slot (Q's, then K's), loaded together and
     // written to LDS after one wait
-    u32x4 gstage[LEAN ? 2 * VPT : 1];
+    u32x4 gstage[LEAN ? 2 * VPT * KG : 1];
     uint32_t voff[VPT];  // input byte offset from the tile's first row, or kOOB
     uint32_t ooff[VPT];  // output byte offset (equal to voff when ES == OS)
     uint32_t poff[kPair ? VPT : 1][2];  // kPair: the lane's offsets for its two stores
@@ -599,9 +604,14 @@ fused_qknorm_kernel(FusedParams p)
         // on register assignment, which this code shifts, and each kernel keeps
         // the spelling it was measured fastest with.)
         if constexpr (LEAN) {
-            // (bf16 RMSNorm, single-tensor tiles: one gamma word per slot and tensor)
-            gstage[i] = valid ? ld_cached(static_cast<const gam_t*>(p.gamma[0]) + col) : u32x4{0, 0, 0, 0};
-            gstage[VPT + i] = valid ? ld_cached(static_cast<const gam_t*>(p.gamma[1]) + col) : u32x4{0, 0, 0, 0};
+            // (RMSNorm, single-tensor tiles: KG gamma words per slot and tensor)
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                const int c = col + g * (16 / (int)sizeof(gam_t));
+                gstage[i * KG + g] = valid ? ld_cached(static_cast<const gam_t*>(p.gamma[0]) + c) : u32x4{0, 0, 0, 0};
+                gstage[(VPT + i) * KG + g] =
+                    valid ? ld_cached(static_cast<const gam_t*>(p.gamma[1]) + c) : u32x4{0, 0, 0, 0};
+            }
         } else if constexpr (!(ST && (NORM || EV == 16))) {
 #pragma unroll
             for (int g = 0; g < KG; ++g)
@@ -662,8 +672,11 @@ fused_qknorm_kernel(FusedParams p)
     if constexpr (LEAN) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            gam_lds[i * ndt + dt] = gstage[i];
-            gam_lds[VPT * ndt + i * ndt + dt] = gstage[VPT + i];
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                gam_lds[(i * ndt + dt) * KG + g] = gstage[i * KG + g];
+                gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] = gstage[(VPT + i) * KG + g];
+            }
         }
     }
 

@@ -516,7 +516,7 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
         assert plan(dt, 16384, 5120, 5120, 8, bpc=roomy)["xcd_map"] == 0, dt
     assert plan("e4m3_e4m3", 8192, 5120, 1024, 4, bpc=roomy)["xcd_map"] == 1
     e = plan("e4m3_bf16", 16384, 5120, 5120, 2, bpc=roomy)
-    assert e["xcd_map"] == 0 and (e["variant"], e["data_waves"], e["rows"]) == (1, 10, 4), e
+    assert e["xcd_map"] == 1 and (e["variant"], e["data_waves"], e["rows"], e["st"]) == (7, 10, 8, 1), e
     try:
         ops.set_option("xcd_map", 1)
         assert plan("bf16", 8192, 5120, 1024, 4, bpc=roomy)["xcd_map"] == 1
@@ -529,8 +529,8 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
 def test_plan_pace_follows_the_tuned_launch():
     """Tuned launches measured faster paced carry their pacing rate in the plan
     (bf16 split 1 and 2 ways on the staggered schedule 7100 GB/s, LayerNorm bf16 split 2
-    ways staggered 6700 GB/s; bf16 GQA 6700 GB/s; E4M3 -> bf16 split 1, 4 and 8 ways
-    and E4M3 -> E4M3 split 2 ways 6600 GB/s);
+    ways staggered 6700 GB/s; bf16 GQA 6700 GB/s; E4M3 -> bf16 split 2 ways staggered
+    6800 GB/s; E4M3 -> bf16 split 1, 4 and 8 ways and E4M3 -> E4M3 split 2 ways 6600 GB/s);
     every other launch, forced launches included, has none unless the option
     sets a rate and its kernel has a paced build; 0 turns pacing off."""
     roomy = [[0] + [8] * 15 for _ in range(ops.NUM_VARIANTS)]
@@ -542,8 +542,9 @@ def test_plan_pace_follows_the_tuned_launch():
     assert pace("ln_bf16", 16384, 5120, 5120, 2) == 6700
     for N in (1, 4, 8):
         assert pace("e4m3_bf16", 16384, 5120, 5120, N) == 6600, N
+    assert pace("e4m3_bf16", 16384, 5120, 5120, 2) == 6800
     assert pace("e4m3_e4m3", 16384, 5120, 5120, 2) == 6600
-    for dt, N in (("bf16", 4), ("bf16", 8), ("e4m3_bf16", 2), ("e4m3_e4m3", 1),
+    for dt, N in (("bf16", 4), ("bf16", 8), ("e4m3_e4m3", 1),
                   ("e4m3_e4m3", 4), ("e4m3_e4m3", 8), ("ln_bf16", 4)):
         assert pace(dt, 16384, 5120, 5120, N) == 0, (dt, N)
     assert pace("bf16", 16384, 3072, 3072, 4) == 0 and pace("f32", 16384, 8192, 8192, 8) == 0

@@ -546,6 +546,8 @@ def test_bench_skeleton_moves_every_byte(fmt, T, Hq, Hk, N, layout):
     ("ln_bf16", 16384, 5120, 5120, 2, -1),  # the tuned LayerNorm launch, staggered by default
     ("ln_bf16", 4099, 5120, 5120, 2, 4000), # staggered LayerNorm, ragged, barriers held
     ("bf16", 4096, 5120, 1024, 4, 4000),    # a rate below the launch's own: barriers held
+    ("e4m3_bf16", 16384, 5120, 5120, 2, -1),  # the tuned E4M3 -> bf16 launch, staggered
+    ("e4m3_bf16", 4099, 5120, 5120, 2, 4000), # the same, ragged, barriers held
     ("e4m3_bf16", 4096, 5120, 5120, 4, -1),
     ("e4m3_bf16", 4099, 5120, 5120, 1, 4000),
     ("e4m3_bf16", 8192, 5120, 5120, 8, -1),

@@ -357,11 +357,11 @@ typedef struct qknorm_plan {
                            barrier before k periods after its start, one period being
                            the time the whole grid's tile bytes of one iteration take
                            at that rate (launches of more than two iterations). The
-                           staggered builds (bf16 variant 10 and E4M3 -> bf16
-                           variant 7 on single-tensor tiles, LayerNorm bf16 variant 7
-                           on mixed tiles) start group g's first loads a lead (5/8
-                           of a period for bf16, 3/8 for E4M3 -> bf16, one period
-                           for LayerNorm) plus g / n_groups
+                           staggered builds (bf16 variant 10, E4M3 -> bf16 variant 7
+                           and LayerNorm bf16 variant 7 on single-tensor tiles,
+                           LayerNorm bf16 variant 7 on mixed tiles) start group g's
+                           first loads a lead (5/8 of a period, 3/8 for E4M3 ->
+                           bf16, one period for mixed-tile LayerNorm) plus g / n_groups
                            of a period after entry and count barrier k's period from
                            barrier 0, so tiles are loaded in tile order; their drain
                            barriers are not held */
@@ -403,7 +403,7 @@ enum {
                                    (single-tensor tiles) and 7 (mixed; single-tensor
                                    tiles: staggered), E4M3 -> E4M3
                                    variant 7 (single-tensor), LayerNorm bf16 variant 7
-                                   on mixed tiles (staggered) */
+                                   (both layouts, staggered) */
     QKN_OPT_STATIC_SLOTS = 13,  /* test hook: 0 = the no-allocation call may use all of
                                    its static slots, else at most this many (so that
                                    QKN_ESCRATCH can be exercised) */

@@ -221,11 +221,13 @@ FusedFn fused_fn_layout(int fmt, int v, bool st)
 // on single-tensor tiles and 7 on mixed tiles, E4M3 -> E4M3 variant 7 on
 // single-tensor tiles. Staggered (PACE = 2): bf16 variant 10 on single-tensor
 // tiles (the prefill split one and two ways), E4M3 -> bf16 variant 7 on
-// single-tensor tiles (split two ways) and LayerNorm bf16 variant 7 on mixed
-// tiles. nullptr for every other kernel, which runs unpaced.
+// single-tensor tiles (split two ways) and LayerNorm bf16 variant 7 on
+// single-tensor tiles (split two ways) and on mixed tiles. nullptr for every
+// other kernel, which runs unpaced.
 FusedFn paced_fn(int fmt, int v, bool st)
 {
     if (fmt == QKN_FMT_BF16 && v == 10 && st) return qkn::fused_qknorm_kernel<Bf16, 5, true, 2, 320, 0, true, 2>;
+    if (fmt == QKN_FMT_LN_BF16 && v == 7 && st) return qkn::fused_qknorm_kernel<Bf16, 2, true, 2, 1024, 1, true, 2>;
     if (fmt == QKN_FMT_LN_BF16 && v == 7 && !st) return qkn::fused_qknorm_kernel<Bf16, 2, true, 2, 1024, 1, false, 2>;
     if (fmt == QKN_FMT_BF16 && v == 8 && !st) return qkn::fused_qknorm_kernel<Bf16, 3, true, 2, 768, 0, false, 1>;
     if (fmt == QKN_FMT_E4M3_BF16 && v == 7 && st)
@@ -272,7 +274,7 @@ bool variant_usable(int fmt, int v) { return fused_fn_for(fmt, v) != nullptr || 
 // paced builds on the staggered schedule (PACE = 2)
 bool paced_staggered(int fmt, int v, bool st)
 {
-    return (fmt == QKN_FMT_BF16 && st && v == 10) || (fmt == QKN_FMT_LN_BF16 && !st && v == 7) ||
+    return (fmt == QKN_FMT_BF16 && st && v == 10) || (fmt == QKN_FMT_LN_BF16 && v == 7) ||
            (fmt == QKN_FMT_E4M3_BF16 && st && v == 7);
 }
 bool is_e4m3(int fmt) { return fmt == QKN_FMT_E4M3_BF16 || fmt == QKN_FMT_E4M3_E4M3; }
@@ -794,6 +796,7 @@ int plan(int dtype, int64_t T, int64_t Hq, int64_t Hk, int N, int cu, const int*
         {QKN_FMT_E4M3_E4M3, 640, 640, 8, 7, 2, 3, 4, 0, 0},
         {QKN_FMT_E4M3_E4M3, 1280, 256, 4, 7, 3, 4, 3, 0},
         {QKN_FMT_LN_BF16, 5120, 5120, 1, 1, 10, 1, 1, 0},
+        {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 4, 1, 1, 1, 6900},
         {QKN_FMT_LN_BF16, 2560, 2560, 2, 7, 10, 2, 1, 0, 1, 6700},
         {QKN_FMT_LN_BF16, 1280, 1280, 4, 7, 10, 4, 1, 0},
         {QKN_FMT_LN_BF16, 640, 640, 8, 6, 5, 4, 4, 1, 0},

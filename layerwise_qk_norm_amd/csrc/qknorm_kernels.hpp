@@ -347,12 +347,15 @@ fused_qknorm_kernel(FusedParams p)
 {
     // PACE 2 builds run on the staggered schedule, where the data waves' work
     // per tile is on the critical path of every iteration. For RMSNorm with bf16
-    // outputs (bf16 or E4M3 inputs) on single-tensor tiles with a two-tile lag
-    // they also reduce all of a wave's Phase A slots side by side, alternate the
-    // two tile buffers instead of copying them and stage gamma with one wait
-    // (LEAN). The results are bitwise those of the other builds.
-    constexpr bool LEAN = PACE == 2 && (std::is_same<DT, Bf16>::value || std::is_same<DT, E4m3Bf16>::value) &&
-                          NORM == 0 && LAG == 2 && PREFETCH && ST;
+    // outputs (bf16 or E4M3 inputs) and bf16 LayerNorm, on single-tensor tiles
+    // with a two-tile lag, they also reduce all of a wave's Phase A slots side by
+    // side, alternate the two tile buffers instead of copying them and stage
+    // gamma (and beta) with one wait (LEAN). The results are bitwise those of
+    // the other builds.
+    constexpr bool LEAN =
+        PACE == 2 && LAG == 2 && PREFETCH && ST &&
+        ((NORM == 0 && (std::is_same<DT, Bf16>::value || std::is_same<DT, E4m3Bf16>::value)) ||
+         (NORM == 1 && std::is_same<DT, Bf16>::value));
     using in_t = typename DT::in_t;
     using gam_t = typename DT::gam_t;
     constexpr int EV = DT::kVec;
@@ -540,9 +543,11 @@ fused_qknorm_kernel(FusedParams p)
     // vectors 32..63, each as whole lines (lanes 0-31 write first halves,
     // lanes 32-63 second halves).
     constexpr bool kPair = KO == 2;
-    // LEAN: gamma words of every slot (Q's, then K's), loaded together and
+    // LEAN: the gamma (and beta) words of every slot, image by image in LDS
+    // order (Q's gamma, [Q's beta,] K's gamma, [K's beta]), loaded together and
     // written to LDS after one wait
-    u32x4 gstage[LEAN ? 2 * VPT * KG : 1];
+    constexpr int NIMG = 2 * (NORM ? 2 : 1);
+    u32x4 gstage[LEAN ? NIMG * VPT * KG : 1];
     uint32_t voff[VPT];  // input byte offset from the tile's first row, or kOOB
     uint32_t ooff[VPT];  // output byte offset (equal to voff when ES == OS)
     uint32_t poff[kPair ? VPT : 1][2];  // kPair: the lane's offsets for its two stores
@@ -604,13 +609,26 @@ fused_qknorm_kernel(FusedParams p)
         // on register assignment, which this code shifts, and each kernel keeps
         // the spelling it was measured fastest with.)
         if constexpr (LEAN) {
-            // (RMSNorm, single-tensor tiles: KG gamma words per slot and tensor)
+            // (single-tensor tiles: KG words per slot, tensor and parameter)
+            if constexpr (NORM == 0) {
 #pragma unroll
-            for (int g = 0; g < KG; ++g) {
-                const int c = col + g * (16 / (int)sizeof(gam_t));
-                gstage[i * KG + g] = valid ? ld_cached(static_cast<const gam_t*>(p.gamma[0]) + c) : u32x4{0, 0, 0, 0};
-                gstage[(VPT + i) * KG + g] =
-                    valid ? ld_cached(static_cast<const gam_t*>(p.gamma[1]) + c) : u32x4{0, 0, 0, 0};
+                for (int g = 0; g < KG; ++g) {
+                    const int c = col + g * (16 / (int)sizeof(gam_t));
+                    gstage[i * KG + g] = valid ? ld_cached(static_cast<const gam_t*>(p.gamma[0]) + c) : u32x4{0, 0, 0, 0};
+                    gstage[(VPT + i) * KG + g] =
+                        valid ? ld_cached(static_cast<const gam_t*>(p.gamma[1]) + c) : u32x4{0, 0, 0, 0};
+                }
+            } else {
+                // images gamma_q, beta_q, gamma_k, beta_k; a null beta staged as zeros
+#pragma unroll
+                for (int im = 0; im < NIMG; ++im) {
+                    const gam_t* src = static_cast<const gam_t*>((im & 1) ? p.beta[im >> 1] : p.gamma[im >> 1]);
+#pragma unroll
+                    for (int g = 0; g < KG; ++g) {
+                        const int c = col + g * (16 / (int)sizeof(gam_t));
+                        gstage[(im * VPT + i) * KG + g] = (valid && src) ? ld_cached(src + c) : u32x4{0, 0, 0, 0};
+                    }
+                }
             }
         } else if constexpr (!(ST && (NORM || EV == 16))) {
 #pragma unroll
@@ -672,10 +690,19 @@ fused_qknorm_kernel(FusedParams p)
     if constexpr (LEAN) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
+            if constexpr (NORM == 0) {
 #pragma unroll
-            for (int g = 0; g < KG; ++g) {
-                gam_lds[(i * ndt + dt) * KG + g] = gstage[i * KG + g];
-                gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] = gstage[(VPT + i) * KG + g];
+                for (int g = 0; g < KG; ++g) {
+                    gam_lds[(i * ndt + dt) * KG + g] = gstage[i * KG + g];
+                    gam_lds[(VPT * ndt + i * ndt + dt) * KG + g] = gstage[(VPT + i) * KG + g];
+                }
+            } else {
+#pragma unroll
+                for (int im = 0; im < NIMG; ++im) {
+#pragma unroll
+                    for (int g = 0; g < KG; ++g)
+                        gam_lds[(im * VPT * ndt + i * ndt + dt) * KG + g] = gstage[(im * VPT + i) * KG + g];
+                }
             }
         }
     }
@@ -734,6 +761,7 @@ fused_qknorm_kernel(FusedParams p)
                 // (each slot's squares in element order, then the wave tree,
                 // then runs of equal segments in slot order), computed for all
                 // slots at once
+                if constexpr (NORM == 0) {
                 float sq[VPT], w[VPT];
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
@@ -756,6 +784,43 @@ fused_qknorm_kernel(FusedParams p)
                     run += w[i];
                 }
                 if (lane == 0) red[par][dwave][c] = run;
+                } else {
+                // LayerNorm: the squares and the values of every slot, each in
+                // element order, reduced side by side
+                float sq[2 * VPT], w[2 * VPT];  // squares, then values
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    float f[EV];
+                    unpack(DT{}, buf[i], f);
+                    sq[i] = 0.f;
+                    sq[VPT + i] = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) sq[i] = fmaf(f[e], f[e], sq[i]);
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) sq[VPT + i] += f[e];
+                }
+                wave_sum_n<2 * VPT>(sq, w);
+                int c = segu[0];
+                float run = 0.f, run1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    if (segu[i] != c) {
+                        if (lane == 0) {
+                            red[par][dwave][c] = run;
+                            red[par][dwave][nseg + c] = run1;
+                        }
+                        run = 0.f;
+                        run1 = 0.f;
+                        c = segu[i];
+                    }
+                    run += w[i];
+                    run1 += w[VPT + i];
+                }
+                if (lane == 0) {
+                    red[par][dwave][c] = run;
+                    red[par][dwave][nseg + c] = run1;
+                }
+                }
                 return;
             }
         }

@@ -529,7 +529,8 @@ def test_plan_xcd_mapping_follows_the_tuned_launch():
 def test_plan_pace_follows_the_tuned_launch():
     """Tuned launches measured faster paced carry their pacing rate in the plan
     (bf16 split 1 and 2 ways on the staggered schedule 7100 GB/s, LayerNorm bf16 split 2
-    ways staggered 6700 GB/s; bf16 GQA 6700 GB/s; E4M3 -> bf16 split 2 ways staggered
+    ways staggered 6900 GB/s on single-tensor tiles, 6700 on mixed ones; bf16 GQA
+    6700 GB/s; E4M3 -> bf16 split 2 ways staggered
     6800 GB/s; E4M3 -> bf16 split 1, 4 and 8 ways and E4M3 -> E4M3 split 2 ways 6600 GB/s);
     every other launch, forced launches included, has none unless the option
     sets a rate and its kernel has a paced build; 0 turns pacing off."""
@@ -539,7 +540,16 @@ def test_plan_pace_follows_the_tuned_launch():
     assert pace("bf16", 8192, 5120, 1024, 4) == 6700
     assert pace("bf16", 16384, 5120, 5120, 2) == 7100
     assert pace("bf16", 16384, 5120, 5120, 1) == 7100
-    assert pace("ln_bf16", 16384, 5120, 5120, 2) == 6700
+    assert pace("ln_bf16", 16384, 5120, 5120, 2) == 6900
+    ln = plan("ln_bf16", 16384, 5120, 5120, 2, bpc=roomy)
+    assert (ln["variant"], ln["data_waves"], ln["rows"], ln["st"]) == (7, 10, 4, 1), ln
+    try:
+        # mixed tiles asked for: the mixed-tile staggered entry
+        ops.set_option("tile_layout", 1)
+        ln = plan("ln_bf16", 16384, 5120, 5120, 2, bpc=roomy)
+        assert (ln["variant"], ln["rows"], ln["st"], ln["pace_gbs"]) == (7, 2, 0, 6700), ln
+    finally:
+        ops.set_option("tile_layout", 0)
     for N in (1, 4, 8):
         assert pace("e4m3_bf16", 16384, 5120, 5120, N) == 6600, N
     assert pace("e4m3_bf16", 16384, 5120, 5120, 2) == 6800

@@ -544,7 +544,7 @@ def test_bench_skeleton_moves_every_byte(fmt, T, Hq, Hk, N, layout):
     ("bf16", 4096, 5120, 5120, 1, -1),      # the tuned one-shard launch, staggered by default
     ("bf16", 4099, 5120, 5120, 1, 6000),    # the same, ragged, at a set rate
     ("ln_bf16", 16384, 5120, 5120, 2, -1),  # the tuned LayerNorm launch, staggered by default
-    ("ln_bf16", 4099, 5120, 5120, 2, 4000), # staggered LayerNorm, ragged, barriers held
+    ("ln_bf16", 4099, 5120, 5120, 2, 4000), # staggered LayerNorm (lean), ragged, barriers held
     ("bf16", 4096, 5120, 1024, 4, 4000),    # a rate below the launch's own: barriers held
     ("e4m3_bf16", 16384, 5120, 5120, 2, -1),  # the tuned E4M3 -> bf16 launch, staggered
     ("e4m3_bf16", 4099, 5120, 5120, 2, 4000), # the same, ragged, barriers held

@@ -360,8 +360,8 @@ typedef struct qknorm_plan {
                            staggered builds (bf16 variant 10, E4M3 -> bf16 variant 7
                            and LayerNorm bf16 variant 7 on single-tensor tiles,
                            LayerNorm bf16 variant 7 on mixed tiles) start group g's
-                           first loads a lead (5/8 of a period, 3/8 for E4M3 ->
-                           bf16, one period for mixed-tile LayerNorm) plus g / n_groups
+                           first loads a lead (5/8 of a period for bf16 RMSNorm,
+                           3/8 for E4M3 -> bf16, one period for LayerNorm) plus g / n_groups
                            of a period after entry and count barrier k's period from
                            barrier 0, so tiles are loaded in tile order; their drain
                            barriers are not held */

@@ -518,7 +518,10 @@ fused_qknorm_kernel(FusedParams p)
     // E4M3 -> bf16 tiles hold twice the tokens per byte of input, so its period
     // (8-row tiles at 6800 GB/s: 2.3 us) is longer than the staging; leads of
     // 3/16, 3/8 and 5/8 of it took its two-way prefill 83.9, 83.6 and 84.4 us.
-    constexpr uint64_t kLead = LEAN ? (std::is_same<DT, E4m3Bf16>::value ? 96 : 160)
+    // LayerNorm stages four words per slot (gamma and beta of both tensors) and
+    // varies most from run to run: a whole period gave the steadiest medians
+    // (111.7 us at 6900 and 7000 GB/s; 3/8: 111.7 and 114.7; 5/8: 114.2 and 117.1).
+    constexpr uint64_t kLead = LEAN ? (std::is_same<DT, E4m3Bf16>::value ? 96 : NORM ? 256 : 160)
                                     : 256;  // 1/256 of a period (serial staging: a whole one)
     const uint64_t t_start = PACE == 2
                                  ? wall_clock64() + ((kLead * p.pace / 256 + (uint64_t)group * p.pace / (uint64_t)p.n_groups) >> 8)

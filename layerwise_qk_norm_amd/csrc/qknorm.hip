@@ -1135,13 +1135,13 @@ template <class DT>
 void launch_headwise_as(int vh, dim3 g, hipStream_t s, const qkn::HeadwiseParams& p)
 {
     switch (vh) {
-    case 1: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 1>), g, dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 2>), g, dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 4>), g, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 8>), g, dim3(256), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 16>), g, dim3(256), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 32>), g, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 64>), g, dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 1>), g, dim3(qkn::kHeadwiseThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 2>), g, dim3(qkn::kHeadwiseThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 4>), g, dim3(qkn::kHeadwiseThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 8>), g, dim3(qkn::kHeadwiseThreads), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 16>), g, dim3(qkn::kHeadwiseThreads), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 32>), g, dim3(qkn::kHeadwiseThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((qkn::headwise_kernel<DT, 64>), g, dim3(qkn::kHeadwiseThreads), 0, s, p); break;
     }
 }
 
@@ -1185,8 +1185,9 @@ int headwise_fwd(int fmt, const void* q, const void* k, const void* gq, const vo
     if (vec) {
         p.nv[0] = T * Hq * f.in / 16;
         p.nv[1] = T * Hk * f.in / 16;
-        p.blocks_q = (p.nv[0] + 255) / 256;
-        const int64_t blocks = p.blocks_q + (p.nv[1] + 255) / 256;
+        constexpr int64_t W = qkn::kHeadwiseThreads;
+        p.blocks_q = (p.nv[0] + W - 1) / W;
+        const int64_t blocks = p.blocks_q + (p.nv[1] + W - 1) / W;
         if (blocks > 0x7fffffff) return QKN_EINVAL;
         if (f.in == 2) launch_headwise_as<Bf16>((int)vh, dim3((unsigned)blocks), stream, p);
         else launch_headwise_as<F32>((int)vh, dim3((unsigned)blocks), stream, p);

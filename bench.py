@@ -59,7 +59,6 @@ TRAFFIC_SUMMARY_HW = os.path.join(PROFILES, "headwise_prefill_T16384_traffic.txt
 TRAFFIC_SUMMARY_GQA = os.path.join(PROFILES, "fused_gqa_T8192_traffic.txt")
 # the headwise kernel is one-shot (no planner): its launch is named by its shape
 HEADWISE_PLAN = {"kernel": "headwise", "vectors_per_head": 16, "threads": 256}
-PMC_PLANS = os.path.join(ROOT, "gpurun_out", "pmc_plans.json")
 
 
 def log(*a):
@@ -494,7 +493,7 @@ def prepare_all(torch, pmc: bool):
     return prep, d
 
 
-def run_pmc(torch, prep):
+def run_pmc(torch, prep, plans_path=""):
     """Five launches of each kernel whose counters are collected, plus the copy of
     known size (the prefill workload's Q and K)."""
     from layerwise_qk_norm_amd import ops
@@ -526,8 +525,9 @@ def run_pmc(torch, prep):
         wk = prep[key][0]
         plans[key] = ops.current_plan(wk.fmt, wk.T, wk.Hq, wk.Hk, wk.n_shards)
     plans["ln_prefill"] = ops.current_plan(wl.fmt, wl.T, wl.Hq, wl.Hk, wl.n_shards)
-    os.makedirs(os.path.dirname(PMC_PLANS), exist_ok=True)
-    json.dump(plans, open(PMC_PLANS, "w"), indent=1, sort_keys=True)
+    if plans_path:
+        os.makedirs(os.path.dirname(os.path.abspath(plans_path)), exist_ok=True)
+        json.dump(plans, open(plans_path, "w"), indent=1, sort_keys=True)
     log("pmc mode done: 5 launches each of the fused bf16 prefill kernel and of the copy of "
         f"{w.T * (w.Hq + w.Hk) * w.elem_bytes} bytes read, then 5 each of fused E4M3->bf16 and "
         "E4M3->E4M3 prefill, GQA, LayerNorm prefill and headwise prefill")
@@ -540,6 +540,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc", action="store_true", help="counter-collection mode")
+    ap.add_argument("--pmc-plans", default="", help="counter-collection mode: write each leg's "
+                    "launch plan to this JSON file (the traffic summaries key on it)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -560,7 +562,7 @@ def main():
     prep, d = prepare_all(torch, args.pmc)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     if args.pmc:
-        run_pmc(torch, prep)
+        run_pmc(torch, prep, args.pmc_plans)
         return
 
     w, gq, gk, bufs = prep["prefill"]

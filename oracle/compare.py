@@ -13,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 
 # Tolerances on the final outputs, by output dtype (relative error against the
-# unrounded oracle). E4M3 outputs are judged by code instead: see e4m3_accepts.
+# unrounded oracle). E4M3 outputs are checked by code instead: see e4m3_accepts.
 TOL = {"bf16": 8e-3, "f32": 1e-5}
 # Relative perturbation of the exact value within which either E4M3 neighbour is
 # accepted: fp32 arithmetic may move a value lying that close to a rounding

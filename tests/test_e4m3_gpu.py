@@ -184,7 +184,7 @@ def test_sweep_full_size(w):
             # every element of every row against a plain fp64 reference on the device
             device_rms_check(x, g, y, w.eps, compare.TOL["bf16"], w.name)
         else:
-            # E4M3 outputs are judged by code, on the rows above. An E4M3 output lies
+            # E4M3 outputs are checked by code, on the rows above. An E4M3 output lies
             # within a factor (1 +- 2^-4) of the exact value (normal range), so a mean
             # of squares moves by at most (1 + 2^-4)^2 - 1 = 0.129 (reached by
             # heavy-tailed rows that a few large values dominate); subnormal outputs
